@@ -1,0 +1,132 @@
+"""Seeded synthetic inputs for the 8-bit rollout hot path.
+
+This module only draws inputs.  It holds none of the method's arithmetic (no
+amax, no scale, no e4m3/int8 code, no GEMM): both the CPU oracle's tests and
+the GPU path's tests and benchmark take their inputs from here, so the two
+sides are compared on identical bits.
+
+Recipe (the pages fix none of it; they speak of 7B/32B-class policies whose
+weights change every step, of small-batch long-tail decode and of prefill
+batches of up to 16,384 tokens):
+
+* generator: numpy PCG64 ``default_rng([seed, stream])``, one stream per
+  tensor, ``standard_normal`` drawn in float32;
+* weights ``Wt`` ~ N(0, 0.02) (sigma = 0.02), stored ``[N, K]`` row-major
+  (output channels x input features, K contiguous);
+* activations ``A`` ~ N(0, 1), ``[M, K]``; for the decode and prefill shapes
+  ``round(0.01 K)`` columns, chosen without replacement by a separate stream,
+  are multiplied by 20 (outlier channels) before rounding;
+* every value is rounded float32 -> bfloat16 with round-to-nearest-even and
+  returned as raw ``uint16`` bit patterns.
+
+The layer shapes stand in for the real Qwen2.5-7B / 32B-class models and RL
+datasets that the pages measure on; none of those is needed here.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Stream ids: one independent PCG64 stream per tensor of a workload.
+_STREAMS = {
+    "A": 1, "W": 2, "A_down": 3, "W_down": 4, "A_cols": 5, "A_down_cols": 6,
+    "q": 11, "k": 12, "v": 13, "o": 14, "gate": 15, "up": 16, "down": 17,
+    "special": 21,
+}
+
+# Layer shapes as Wt [N, K] of one 32B-class decoder layer (hidden 5120,
+# 8 KV heads of 128, FFN 27648).
+STACK_32B = (
+    ("q", 5120, 5120),
+    ("k", 1024, 5120),
+    ("v", 1024, 5120),
+    ("o", 5120, 5120),
+    ("gate", 27648, 5120),
+    ("up", 27648, 5120),
+    ("down", 5120, 27648),
+)
+
+DECODE_SWEEP_M = (1, 2, 4, 8, 32, 128)
+
+# Named workloads.  "gemms" lists (M, N, K, outliers) GEMM problems.
+CONFIGS = {
+    "tiny": dict(gemms=[(16, 256, 256, False)]),
+    "decode7b_upgate": dict(gemms=[(64, 37888, 3584, True)]),
+    "decode32b_sweep": dict(gemms=[(m, 27648, 5120, True) for m in DECODE_SWEEP_M]),
+    "prefill32b": dict(gemms=[(8192, 27648, 5120, True), (8192, 5120, 27648, True)]),
+    "stack32b_requant": dict(layers=STACK_32B, gemm_m=64),
+}
+
+
+def _rng(seed: int, stream: str) -> np.random.Generator:
+    return np.random.default_rng([int(seed), _STREAMS[stream]])
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to bfloat16 (nearest, ties to even)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    b = b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+    return (b >> np.uint32(16)).astype(np.uint16)
+
+
+def outlier_columns(K: int, seed: int, stream: str = "A_cols") -> np.ndarray:
+    """The round(0.01 K) activation columns that carry x20 outliers."""
+    n = int(round(0.01 * K))
+    if n == 0:
+        return np.zeros(0, dtype=np.int64)
+    return np.sort(_rng(seed, stream).choice(K, size=n, replace=False))
+
+
+def bf16_normal(shape, sigma: float, seed: int, stream: str,
+                outlier_cols: np.ndarray | None = None) -> np.ndarray:
+    """N(0, sigma^2) draws rounded to bf16 bits; optional x20 columns."""
+    x = _rng(seed, stream).standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    if outlier_cols is not None and len(outlier_cols):
+        x[..., outlier_cols] *= np.float32(20.0)
+    return f32_to_bf16_bits(x)
+
+
+def weight(N: int, K: int, seed: int = 0, stream: str = "W") -> np.ndarray:
+    """Wt [N, K] bf16 bits, N(0, 0.02)."""
+    return bf16_normal((N, K), 0.02, seed, stream)
+
+
+def activation(M: int, K: int, seed: int = 0, outliers: bool = True,
+               stream: str = "A") -> np.ndarray:
+    """A [M, K] bf16 bits, N(0, 1), optionally with x20 outlier columns."""
+    cols = outlier_columns(K, seed, stream + "_cols") if outliers else None
+    return bf16_normal((M, K), 1.0, seed, stream, cols)
+
+
+def gemm_problem(M: int, N: int, K: int, outliers: bool, seed: int = 0,
+                 down: bool = False) -> dict:
+    """The bf16 inputs of one linear layer: A [M, K] and Wt [N, K]."""
+    a_stream, w_stream = ("A_down", "W_down") if down else ("A", "W")
+    return dict(A=activation(M, K, seed, outliers, a_stream),
+                Wt=weight(N, K, seed, w_stream), M=M, N=N, K=K)
+
+
+def decode_sweep(seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """32B decode sweep: one W draw and the M = 128 activation draw; the
+    problem at batch M uses the first M rows of that draw."""
+    Mmax = max(DECODE_SWEEP_M)
+    A = activation(Mmax, 5120, seed, True, "A")
+    Wt = weight(27648, 5120, seed, "W")
+    return A, Wt
+
+
+def stack_layer(name: str, seed: int = 0) -> np.ndarray:
+    """One weight of the 32B-class layer stack, Wt [N, K] bf16 bits."""
+    for lname, N, K in STACK_32B:
+        if lname == name:
+            return weight(N, K, seed, name)
+    raise KeyError(name)
+
+
+def special_values_bf16() -> np.ndarray:
+    """Every finite bf16 bit pattern (65,536 minus the 512 inf/NaN codes)."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    exp = (allbits >> np.uint16(7)) & np.uint16(0xFF)
+    return allbits[exp != 0xFF]
