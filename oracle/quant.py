@@ -61,24 +61,40 @@ def fp8_block_scale(x_block: np.ndarray) -> np.float32:
         return np.float32(amax / FP8_DIV)
 
 
+def _block_amax(x: np.ndarray, rb: int, cb: int) -> np.ndarray:
+    """max |x| over each rb x cb block (partial edge blocks: their valid
+    elements; zero padding cannot raise a maximum of magnitudes)."""
+    R, C = x.shape
+    nr, nc = -(-R // rb), -(-C // cb)
+    pad = np.zeros((nr * rb, nc * cb), dtype=np.float32)
+    pad[:R, :C] = np.abs(x)
+    return pad.reshape(nr, rb, nc, cb).max(axis=(1, 3))
+
+
+def _divide_and_encode(x: np.ndarray, s_full: np.ndarray, encode) -> np.ndarray:
+    """encode(fl32(x / s)) elementwise, with x itself where s == 0; done in
+    row chunks to bound the temporaries."""
+    out = np.empty(x.shape, dtype=np.uint8 if encode is e4m3.encode else np.int8)
+    step = max(1, (1 << 22) // max(1, x.shape[1]))
+    for r in range(0, x.shape[0], step):
+        xs, ss = x[r:r + step], s_full[r:r + step]
+        with np.errstate(divide="ignore", invalid="ignore", under="ignore"):
+            v = np.where(ss == 0, xs, xs / np.where(ss == 0, np.float32(1), ss))
+        out[r:r + step] = encode(v.astype(np.float32))
+    return out
+
+
 def fp8_weight_block_quant(w_bits) -> tuple[np.ndarray, np.ndarray]:
     """Wt bf16 [N, K] -> (codes uint8 [N, K], scales float32 [ceil(N/128),
     ceil(K/128)])."""
     x = bf16_to_f32(w_bits)
     _check_finite(x)
     N, K = x.shape
-    nb, kb = -(-N // BLOCK), -(-K // BLOCK)
-    scales = np.empty((nb, kb), dtype=np.float32)
-    codes = np.empty((N, K), dtype=np.uint8)
-    for i in range(nb):
-        rows = slice(i * BLOCK, min(N, (i + 1) * BLOCK))
-        for j in range(kb):
-            cols = slice(j * BLOCK, min(K, (j + 1) * BLOCK))
-            blk = x[rows, cols]
-            s = fp8_block_scale(blk)
-            scales[i, j] = s
-            codes[rows, cols] = e4m3.encode(_quotient(blk, s))
-    return codes, scales
+    amax = _block_amax(x, BLOCK, BLOCK)
+    with np.errstate(under="ignore"):
+        scales = (amax / FP8_DIV).astype(np.float32)
+    s_full = np.repeat(np.repeat(scales, BLOCK, axis=0)[:N], BLOCK, axis=1)[:, :K]
+    return _divide_and_encode(x, s_full, e4m3.encode), scales
 
 
 def fp8_weight_blocks(w_bits, block_ids) -> list[tuple[np.ndarray, np.float32]]:
@@ -99,17 +115,11 @@ def fp8_act_token_quant(a_bits) -> tuple[np.ndarray, np.ndarray]:
     x = bf16_to_f32(a_bits)
     _check_finite(x)
     M, K = x.shape
-    kb = -(-K // BLOCK)
-    scales = np.empty((M, kb), dtype=np.float32)
-    codes = np.empty((M, K), dtype=np.uint8)
-    for m in range(M):
-        for j in range(kb):
-            cols = slice(j * BLOCK, min(K, (j + 1) * BLOCK))
-            grp = x[m, cols]
-            s = fp8_block_scale(grp)
-            scales[m, j] = s
-            codes[m, cols] = e4m3.encode(_quotient(grp, s))
-    return codes, scales
+    amax = _block_amax(x, 1, BLOCK)
+    with np.errstate(under="ignore"):
+        scales = (amax / FP8_DIV).astype(np.float32)
+    s_full = np.repeat(scales, BLOCK, axis=1)[:, :K]
+    return _divide_and_encode(x, s_full, e4m3.encode), scales
 
 
 def int8_encode(v: np.ndarray) -> np.ndarray:
@@ -118,15 +128,11 @@ def int8_encode(v: np.ndarray) -> np.ndarray:
 
 
 def _int8_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
-    R = x.shape[0]
-    scales = np.empty(R, dtype=np.float32)
-    codes = np.empty(x.shape, dtype=np.int8)
-    for r in range(R):
-        amax = np.float32(np.max(np.abs(x[r])))
-        with np.errstate(under="ignore"):
-            s = np.float32(amax / INT8_DIV)
-        scales[r] = s
-        codes[r] = 0 if s == 0 else int8_encode(_quotient(x[r], s))
+    amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    with np.errstate(under="ignore"):
+        scales = (amax.astype(np.float32) / INT8_DIV).astype(np.float32)
+    codes = _divide_and_encode(x, np.repeat(scales[:, None], x.shape[1], axis=1), int8_encode)
+    codes[scales == 0] = 0
     return codes, scales
 
 
