@@ -1,0 +1,389 @@
+"""Benchmark of the 8-bit rollout hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole path over one batch of the workload:
+FP8 block re-quantization of the weight, FP8 per-token-group quantization
+of the activations, the W8A8 block-scaled GEMM, and the INT8 per-channel
+variant of all three.  The default workload is the 7B-class decode FFN
+up/gate layer (A [64, 3584], Wt [37888, 3584]).  Inputs are synthetic
+(seeded, see precision_rl_rollout_amd.workloads), resident in HBM before
+the timed region; two input sets alternate so that no step finds its bf16
+weight in the 256 MB last-level cache.
+
+Prints one JSON line.  ``value`` is algorithmic bytes of the step / step
+time (GB/s); ``roofline`` gives the dominant kernel's algorithmic GB/s
+(from HIP events on the launch stream) against the 8 TB/s HBM peak;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same step.
+
+Other workloads (``--workload``): ``decode32b_sweep`` (GEMMs at M = 1..128,
+N 27648, K 5120, cold weights), ``prefill32b`` (M 8192 up/gate and down
+GEMMs, TFLOP/s), ``stack32b_requant`` (FP8 and INT8 re-quantization of a
+32B-class layer's seven weights).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W8A8 block GEMM TFLOP/s (% FP8 peak); decode-shape HBM GB/s (% peak)"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+INT8_PEAK_TOPS = 5000.0
+
+
+# ---------------------------------------------------------------- work counts
+def quant_bytes(rows, K, units):
+    """bf16 read + code written + one fp32 scale per block / group / row."""
+    return 3 * rows * K + 4 * units
+
+
+def gemm_bytes(M, N, K, a_scales, w_scales):
+    """FP8/INT8 weight + activation codes, their scales, bf16 output."""
+    return N * K + M * K + 4 * (a_scales + w_scales) + 2 * M * N
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+# ---------------------------------------------------------------- helpers
+def _sources_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "precision_rl_rollout_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "fp8_weight_block_quant": ["quant_fp8.hip", "prr_device.h"],
+    "fp8_act_token_quant": ["quant_fp8.hip", "prr_device.h"],
+    "int8_weight_channel_quant": ["quant_int8.hip", "prr_device.h"],
+    "int8_act_token_quant": ["quant_int8.hip", "prr_device.h"],
+    "w8a8_block_gemm": ["gemm.hip", "prr_device.h"],
+    "w8a8_int8_channel_gemm": ["gemm.hip", "prr_device.h"],
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if
+    it was taken on the kernel's current sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    rec = table.get(f"{kernel}@{workload}")
+    if not rec or rec.get("sources") != _sources_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """Per-call HIP event pairs on torch's current stream (the stream the
+    binding launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+        return out
+
+    def avg_us(self):
+        return {k: 1e3 * float(np.mean([s.elapsed_time(e) for s, e in v]))
+                for k, v in self.pairs.items()}
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        n = 1
+    return int(n)
+
+
+# ---------------------------------------------------------------- workloads
+def run_decode7b(args, torch, B, W):
+    M, N, K = 64, 37888, 3584
+    sets = []
+    for seed in (0, 1):
+        p = W.gemm_problem(M, N, K, True, seed=seed)
+        sets.append(dict(A=torch.from_numpy(p["A"].view(np.int16)).cuda(),
+                         Wt=torch.from_numpy(p["Wt"].view(np.int16)).cuda()))
+    dev = torch.device("cuda:0")
+    outs = []
+    for _ in sets:
+        outs.append(dict(
+            wq8=torch.empty((N, K), dtype=torch.uint8, device=dev),
+            sw8=torch.empty((cdiv(N, 128), K // 128), dtype=torch.float32, device=dev),
+            aq8=torch.empty((M, K), dtype=torch.uint8, device=dev),
+            sa8=torch.empty((M, K // 128), dtype=torch.float32, device=dev),
+            c8=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+            wqi=torch.empty((N, K), dtype=torch.int8, device=dev),
+            swi=torch.empty((N,), dtype=torch.float32, device=dev),
+            aqi=torch.empty((M, K), dtype=torch.int8, device=dev),
+            sai=torch.empty((M,), dtype=torch.float32, device=dev),
+            ci=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+
+    work = {
+        "fp8_weight_block_quant": quant_bytes(N, K, cdiv(N, 128) * (K // 128)),
+        "fp8_act_token_quant": quant_bytes(M, K, M * (K // 128)),
+        "w8a8_block_gemm": gemm_bytes(M, N, K, M * (K // 128), cdiv(N, 128) * (K // 128)),
+        "int8_weight_channel_quant": quant_bytes(N, K, N),
+        "int8_act_token_quant": quant_bytes(M, K, M),
+        "w8a8_int8_channel_gemm": gemm_bytes(M, N, K, M, N),
+    }
+    step_bytes = sum(work.values())
+
+    def step(i, timer=None):
+        s, o = sets[i % 2], outs[i % 2]
+        t = timer.run if timer else (lambda _n, f: f())
+        t("fp8_weight_block_quant", lambda: B.fp8_weight_block_quant(s["Wt"], out=o["wq8"], scale=o["sw8"]))
+        t("fp8_act_token_quant", lambda: B.fp8_act_token_quant(s["A"], out=o["aq8"], scale=o["sa8"]))
+        t("w8a8_block_gemm", lambda: B.w8a8_block_gemm(o["aq8"], o["sa8"], o["wq8"], o["sw8"], out=o["c8"]))
+        t("int8_weight_channel_quant", lambda: B.int8_weight_channel_quant(s["Wt"], out=o["wqi"], scale=o["swi"]))
+        t("int8_act_token_quant", lambda: B.int8_act_token_quant(s["A"], out=o["aqi"], scale=o["sai"]))
+        t("w8a8_int8_channel_gemm", lambda: B.w8a8_int8_channel_gemm(o["aqi"], o["sai"], o["wqi"], o["swi"], out=o["ci"]))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, timer)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    us = timer.avg_us()
+
+    kernels = {k: {"us": round(us[k], 2), "algorithmic_bytes": work[k],
+                   "GB/s": round(work[k] / us[k] / 1e3, 1)} for k in work}
+    dom = max(us, key=us.get)
+    achieved = work[dom] / us[dom] / 1e3
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom, "decode7b_upgate")}
+    line = {
+        "metric": METRIC, "value": round(step_bytes / dt / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3+int8", "data": "synthetic",
+        "config": {"workload": "decode7b_upgate", "M": M, "N": N, "K": K,
+                   "step": "fp8 W block quant + fp8 A group quant + fp8 W8A8 GEMM + int8 W "
+                           "channel quant + int8 A token quant + int8 W8A8 GEMM",
+                   "step_algorithmic_bytes": step_bytes},
+        "roofline": roofline, "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode7b(W, step_bytes)
+    return line
+
+
+def cpu_baseline_decode7b(W, step_bytes):
+    """The oracle, as it stands, on a bounded sample of the same step: the
+    full activation and the first `rows` weight rows (one N slice), all six
+    operations; scaled to the step's unit (algorithmic GB/s)."""
+    from oracle import gemm, quant
+    M, N, K = 64, 37888, 3584
+    rows = 2048
+    p = W.gemm_problem(M, N, K, True, seed=0)
+    A, Wt = p["A"], p["Wt"][:rows]
+    t0 = time.perf_counter()
+    wq, sw = quant.fp8_weight_block_quant(Wt)
+    aq, sa = quant.fp8_act_token_quant(A)
+    gemm.round_bf16(gemm.w8a8_block_gemm(aq, sa, wq, sw))
+    wqi, swi = quant.int8_weight_channel_quant(Wt)
+    aqi, sai = quant.int8_act_token_quant(A)
+    gemm.round_bf16(gemm.int8_channel_gemm(aqi, sai, wqi, swi))
+    dt = time.perf_counter() - t0
+    sample_bytes = (quant_bytes(rows, K, (rows // 128) * (K // 128)) + quant_bytes(M, K, M * (K // 128))
+                    + gemm_bytes(M, rows, K, M * (K // 128), (rows // 128) * (K // 128))
+                    + quant_bytes(rows, K, rows) + quant_bytes(M, K, M)
+                    + gemm_bytes(M, rows, K, M, rows))
+    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"all six operations with the full A [64, 3584] and Wt rows 0..{rows - 1} "
+                      f"of 37888 (N = {rows}); numpy elementwise (1 thread) + fp64 BLAS"}
+
+
+def _cold_copies(torch, make, nbytes, budget=600 << 20):
+    """Enough copies of a tensor set that cycling through them cannot be
+    served by the 256 MB last-level cache."""
+    n = max(2, -(-budget // max(1, nbytes)))
+    return [make(i) for i in range(min(n, 64))]
+
+
+def run_decode32b(args, torch, B, W):
+    A, Wt = W.decode_sweep(seed=0)
+    wdev = torch.from_numpy(Wt.view(np.int16)).cuda()
+    w8 = B.fp8_weight_block_quant(wdev)
+    wi = B.int8_weight_channel_quant(wdev)
+    N, K = Wt.shape
+    copies8 = _cold_copies(torch, lambda i: (w8[0].clone(), w8[1].clone()), N * K)
+    copiesi = _cold_copies(torch, lambda i: (wi[0].clone(), wi[1].clone()), N * K)
+    del wdev
+    res = {}
+    for M in W.DECODE_SWEEP_M:
+        a = torch.from_numpy(A[:M].copy().view(np.int16)).cuda()
+        aq8, sa8 = B.fp8_act_token_quant(a)
+        aqi, sai = B.int8_act_token_quant(a)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+        for name, cp, fn, aq, sa, nws, nas in (
+                ("w8a8_block_gemm", copies8, B.w8a8_block_gemm, aq8, sa8, (N // 128) * (K // 128), M * (K // 128)),
+                ("w8a8_int8_channel_gemm", copiesi, B.w8a8_int8_channel_gemm, aqi, sai, N, M)):
+            for i in range(args.warmup):
+                fn(aq, sa, cp[i % len(cp)][0], cp[i % len(cp)][1], out=c)
+            timer = Timer(torch)
+            for i in range(args.steps):
+                wq, sw = cp[i % len(cp)]
+                timer.run(name, lambda: fn(aq, sa, wq, sw, out=c))
+            torch.cuda.synchronize()
+            us = timer.avg_us()[name]
+            by = gemm_bytes(M, N, K, nas, nws)
+            res[f"{name}/M{M}"] = {"us": round(us, 2), "GB/s": round(by / us / 1e3, 1),
+                                   "TFLOP/s": round(2 * M * N * K / us / 1e6, 2),
+                                   "hbm_frac": round(by / us / 1e3 / HBM_PEAK_GBS, 4)}
+    worst = min(v["GB/s"] for k, v in res.items() if k.startswith("w8a8_block_gemm"))
+    return {"metric": METRIC, "value": worst, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None,
+            "dtype": "fp8e4m3+int8", "data": "synthetic",
+            "config": {"workload": "decode32b_sweep", "N": N, "K": K,
+                       "value_is": "lowest fp8 GEMM GB/s over M"},
+            "kernels": res}
+
+
+def run_prefill32b(args, torch, B, W):
+    res = {}
+    for which, (N, K) in (("upgate", (27648, 5120)), ("down", (5120, 27648))):
+        p = W.gemm_problem(8192, N, K, True, seed=0, down=which == "down")
+        a = torch.from_numpy(p["A"].view(np.int16)).cuda()
+        w = torch.from_numpy(p["Wt"].view(np.int16)).cuda()
+        aq8, sa8 = B.fp8_act_token_quant(a)
+        wq8, sw8 = B.fp8_weight_block_quant(w)
+        aqi, sai = B.int8_act_token_quant(a)
+        wqi, swi = B.int8_weight_channel_quant(w)
+        c = torch.empty((8192, N), dtype=torch.bfloat16, device="cuda:0")
+        flops = 2 * 8192 * N * K
+        for name, fn, args_ in (("w8a8_block_gemm", B.w8a8_block_gemm, (aq8, sa8, wq8, sw8)),
+                                ("w8a8_int8_channel_gemm", B.w8a8_int8_channel_gemm, (aqi, sai, wqi, swi)),
+                                ("fp8_act_token_quant", None, None)):
+            timer = Timer(torch)
+            if fn is None:
+                for i in range(args.warmup):
+                    B.fp8_act_token_quant(a, out=aq8, scale=sa8)
+                for i in range(args.steps):
+                    timer.run(name, lambda: B.fp8_act_token_quant(a, out=aq8, scale=sa8))
+                torch.cuda.synchronize()
+                us = timer.avg_us()[name]
+                by = quant_bytes(8192, K, 8192 * (K // 128))
+                res[f"{name}/{which}"] = {"us": round(us, 2), "GB/s": round(by / us / 1e3, 1)}
+                continue
+            for i in range(args.warmup):
+                fn(*args_, out=c)
+            for i in range(args.steps):
+                timer.run(name, lambda: fn(*args_, out=c))
+            torch.cuda.synchronize()
+            us = timer.avg_us()[name]
+            tf = flops / us / 1e6
+            res[f"{name}/{which}"] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
+                                      "peak_frac": round(tf / FP8_PEAK_TFLOPS, 4)}
+        del a, w, c
+    up = res["w8a8_block_gemm/upgate"]
+    return {"metric": METRIC, "value": up["TFLOP/s"], "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "vs_baseline": None, "dtype": "fp8e4m3+int8", "data": "synthetic",
+            "config": {"workload": "prefill32b", "M": 8192,
+                       "value_is": "fp8 up/gate GEMM M8192 N27648 K5120"},
+            "roofline": {"bound": "mfma", "kernel": "w8a8_block_gemm", "achieved": up["TFLOP/s"],
+                         "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": up["peak_frac"],
+                         "traffic": measured_traffic("w8a8_block_gemm", "prefill32b")},
+            "kernels": res}
+
+
+def run_stack32b(args, torch, B, W):
+    layers = []
+    for name, N, K in W.STACK_32B:
+        w = torch.from_numpy(W.stack_layer(name, 0).view(np.int16)).cuda()
+        layers.append((name, N, K, w, B.fp8_weight_block_quant(w), B.int8_weight_channel_quant(w)))
+    def step(timer=None):
+        for name, N, K, w, o8, oi in layers:
+            f8 = lambda: B.fp8_weight_block_quant(w, out=o8[0], scale=o8[1])
+            fi = lambda: B.int8_weight_channel_quant(w, out=oi[0], scale=oi[1])
+            if timer:
+                timer.run("fp8_weight_block_quant", f8)
+                timer.run("int8_weight_channel_quant", fi)
+            else:
+                f8(); fi()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    us = timer.avg_us()
+    elems = sum(N * K for _, N, K, *_ in layers)
+    b8 = sum(quant_bytes(N, K, cdiv(N, 128) * cdiv(K, 128)) for _, N, K, *_ in layers)
+    bi = sum(quant_bytes(N, K, N) for _, N, K, *_ in layers)
+    per8 = us["fp8_weight_block_quant"] * len(layers)
+    peri = us["int8_weight_channel_quant"] * len(layers)
+    return {"metric": METRIC, "value": round((b8 + bi) / dt / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 3),
+            "higher_is_better": True, "vs_baseline": None, "dtype": "fp8e4m3+int8",
+            "data": "synthetic",
+            "config": {"workload": "stack32b_requant", "elements": elems},
+            "kernels": {"fp8_weight_block_quant(stack)": {"us": round(per8, 1), "GB/s": round(b8 / per8 / 1e3, 1)},
+                        "int8_weight_channel_quant(stack)": {"us": round(peri, 1), "GB/s": round(bi / peri / 1e3, 1)}}}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode7b_upgate",
+                    choices=["decode7b_upgate", "decode32b_sweep", "prefill32b", "stack32b_requant"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this path is a single-GPU kernel library "
+              "(a data-parallel deployment runs one independent copy per GPU); run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    from precision_rl_rollout_amd import binding as B
+    from precision_rl_rollout_amd import workloads as W
+    B.load()
+    run = {"decode7b_upgate": run_decode7b, "decode32b_sweep": run_decode32b,
+           "prefill32b": run_prefill32b, "stack32b_requant": run_stack32b}[args.workload]
+    line = run(args, torch, B, W)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

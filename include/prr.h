@@ -1,0 +1,180 @@
+/*
+ * prr.h -- C ABI of libprr.so: MI355X (gfx950) kernels for 8-bit rollout.
+ *
+ * The calls implement the per-step re-quantization of freshly updated bf16
+ * policy weights and activations into FP8 e4m3 with block scales, the W8A8
+ * block-scaled linear layer with bf16 output, and an INT8 per-channel
+ * variant of both.  Sources:
+ *   - "FP8-RL: A Practical and Stable Low-Precision Stack for LLM
+ *     Reinforcement Learning", abstract: policy weights change every step
+ *     and must be quantized again every step; item (i): FP8 W8A8
+ *     linear-layer rollout with blockwise FP8 quantization.
+ *   - FlashRL article ("FlashRL: 8Bit Rollouts, Full Power RL"), sections
+ *     on rollout quantization and online quantization with parameter
+ *     updates: INT8 and FP8 rollout.
+ * Block sizes (128 x 128 weight blocks, 1 x 128 activation groups), the
+ * e4m3 format with scale amax / 448, and the INT8 per-channel granularity
+ * are fixed by this library; the pages do not state them.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Data:
+ *   - bf16 tensors are raw uint16_t bit patterns; FP8 tensors are OCP e4m3
+ *     codes (uint8_t: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ *     largest finite 448, 0x7F/0xFF NaN -- never produced); INT8 codes are
+ *     int8_t in [-127, 127]; scales are IEEE binary32.
+ *   - Every matrix is dense row-major.  Weights are stored as Wt [N, K]
+ *     (output channel x input feature, K contiguous) -- the transpose of the
+ *     logical W [K, N] of C = A W.  128 x 128 blocks are square, so the
+ *     blocking of Wt is the blocking of W.
+ *   - Quantized values follow one definition, bit for bit:
+ *       FP8:  s = fl32(amax / 448), q = E4M3_saturating_RNE(fl32(x / s));
+ *       INT8: s = fl32(amax / 127), q = clamp(RNE(fl32(x / s)), -127, 127);
+ *     fl32 is an IEEE binary32 operation, correctly rounded, subnormals
+ *     kept.  An all-zero block/row has s = 0: FP8 codes are the inputs'
+ *     signed zeros (0x00 / 0x80), INT8 codes are 0.  Partial edge blocks
+ *     take amax over their valid elements.
+ *   - Inputs must be finite; non-finite inputs give unspecified (but
+ *     memory-safe) results.
+ * Pointers and memory:
+ *   - Every pointer is a device pointer on the current HIP device, 16-byte
+ *     aligned (PRR_ERR_MISALIGNED otherwise).  The caller allocates and owns
+ *     every buffer; the library allocates nothing, frees nothing and keeps
+ *     no pointer after the call returns.  Inputs and outputs must not
+ *     overlap.
+ *   - A call whose output is empty (a zero dimension) returns PRR_OK and
+ *     touches no memory; its pointers may then be NULL.
+ * Execution:
+ *   - Every call only enqueues work on `stream` (NULL = the null stream)
+ *     and returns without synchronizing.  Buffers must stay valid until
+ *     that work has completed.  Faults inside a kernel surface at the
+ *     caller's next synchronization with the stream.
+ *   - Calls are stateless, thread-safe and deterministic (no atomics; the
+ *     same inputs give the same bits).
+ * Errors (returned synchronously, after argument checks and the launch):
+ *   - PRR_ERR_INVALID_ARG: a negative dimension, a dimension above
+ *     2^31 - 1, or a NULL pointer for a non-empty operand;
+ *   - PRR_ERR_UNSUPPORTED_SHAPE: a GEMM with K % 128 != 0, or an INT8 GEMM
+ *     with K > 133143 (127^2 K could overflow its int32 accumulator);
+ *   - PRR_ERR_MISALIGNED: a pointer that is not 16-byte aligned;
+ *   - PRR_ERR_NO_DEVICE: no HIP device is visible;
+ *   - PRR_ERR_UNSUPPORTED_DEVICE: the current device is not gfx950;
+ *   - PRR_ERR_HIP: the HIP runtime reported an error at launch.
+ */
+#ifndef PRR_H
+#define PRR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PRR_ABI_VERSION 1
+
+typedef enum prr_status {
+  PRR_OK = 0,
+  PRR_ERR_INVALID_ARG = 1,
+  PRR_ERR_UNSUPPORTED_SHAPE = 2,
+  PRR_ERR_MISALIGNED = 3,
+  PRR_ERR_NO_DEVICE = 4,
+  PRR_ERR_UNSUPPORTED_DEVICE = 5,
+  PRR_ERR_HIP = 6
+} prr_status;
+
+/*
+ * fp8_weight_block_quant -- FP8 e4m3 re-quantization of one bf16 weight in
+ * 128 x 128 blocks (FP8-RL, abstract: repeated per-step quantization of the
+ * changing policy weights; item (i): blockwise FP8).
+ *   w_bf16  in   [N, K] bf16 bits, row-major (Wt layout).
+ *   N, K         rows (output channels) and columns (input features), >= 0.
+ *   w_fp8   out  [N, K] e4m3 codes, row-major.
+ *   w_scale out  [ceil(N/128), ceil(K/128)] fp32, row-major: block (i, j)
+ *                covers rows 128i.. and columns 128j.. of w_bf16.
+ */
+prr_status fp8_weight_block_quant(const uint16_t* w_bf16, int64_t N, int64_t K,
+                                  uint8_t* w_fp8, float* w_scale,
+                                  hipStream_t stream);
+
+/*
+ * fp8_act_token_quant -- FP8 e4m3 quantization of bf16 activations in
+ * per-token groups of 128 consecutive input features (FP8-RL, abstract,
+ * item (i): the "A8" of W8A8).
+ *   a_bf16  in   [M, K] bf16 bits, row-major (token x feature).
+ *   a_fp8   out  [M, K] e4m3 codes.
+ *   a_scale out  [M, ceil(K/128)] fp32: group j of row m covers columns
+ *                128j .. 128j+127 of that row.
+ */
+prr_status fp8_act_token_quant(const uint16_t* a_bf16, int64_t M, int64_t K,
+                               uint8_t* a_fp8, float* a_scale,
+                               hipStream_t stream);
+
+/*
+ * w8a8_block_gemm -- the FP8 W8A8 linear layer with block scales and bf16
+ * output (FP8-RL, abstract, item (i)):
+ *   C[m, n] = bf16( sum_kb a_scale[m, kb] * w_scale[n / 128, kb]
+ *                   * sum_{k in kb} D(a_fp8[m, k]) * D(w_fp8[n, k]) )
+ * with D the exact e4m3 value, fp32 accumulation and one RNE rounding to
+ * bf16.  The result agrees with the fp64 evaluation of the same sum,
+ * rounded once to bf16, within a relative Frobenius error of 1e-3.
+ *   a_fp8 [M, K], a_scale [M, K/128]   as written by fp8_act_token_quant.
+ *   w_fp8 [N, K], w_scale [ceil(N/128), K/128] as written by
+ *                                      fp8_weight_block_quant.
+ *   M, N >= 0; K >= 0 with K % 128 == 0 (K == 0 writes +0.0).
+ *   c_bf16 out [M, N] bf16 bits, row-major.
+ */
+prr_status w8a8_block_gemm(const uint8_t* a_fp8, const float* a_scale,
+                           const uint8_t* w_fp8, const float* w_scale,
+                           int64_t M, int64_t N, int64_t K, uint16_t* c_bf16,
+                           hipStream_t stream);
+
+/*
+ * int8_weight_channel_quant -- INT8 re-quantization of one bf16 weight with
+ * one scale per output channel (FlashRL article: INT8 rollout with
+ * per-step quantization of the updated weights; granularity fixed here).
+ *   w_bf16  in   [N, K] bf16 bits (Wt layout).
+ *   w_i8    out  [N, K] int8 codes.
+ *   w_scale out  [N] fp32: row n's scale, over all K of that row.
+ */
+prr_status int8_weight_channel_quant(const uint16_t* w_bf16, int64_t N,
+                                     int64_t K, int8_t* w_i8, float* w_scale,
+                                     hipStream_t stream);
+
+/*
+ * int8_act_token_quant -- dynamic INT8 quantization of bf16 activations
+ * with one scale per token over the whole K (FlashRL article: INT8
+ * rollout; granularity fixed here).
+ *   a_bf16  in   [M, K] bf16 bits.
+ *   a_i8    out  [M, K] int8 codes.
+ *   a_scale out  [M] fp32.
+ */
+prr_status int8_act_token_quant(const uint16_t* a_bf16, int64_t M, int64_t K,
+                                int8_t* a_i8, float* a_scale,
+                                hipStream_t stream);
+
+/*
+ * w8a8_int8_channel_gemm -- the INT8 W8A8 linear layer (FlashRL article):
+ *   acc[m, n] = sum_k a_i8[m, k] * w_i8[n, k]     (exact, int32)
+ *   C[m, n]   = bf16(acc[m, n] * a_scale[m] * w_scale[n])
+ * evaluated in fp32 and rounded once to bf16; agrees with the fp64
+ * evaluation rounded once to bf16 within a relative Frobenius error of 1e-3.
+ *   a_i8 [M, K], a_scale [M]; w_i8 [N, K], w_scale [N];
+ *   K % 128 == 0 and K <= 133143; c_bf16 out [M, N].
+ */
+prr_status w8a8_int8_channel_gemm(const int8_t* a_i8, const float* a_scale,
+                                  const int8_t* w_i8, const float* w_scale,
+                                  int64_t M, int64_t N, int64_t K,
+                                  uint16_t* c_bf16, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* prr_status_string(prr_status status);
+
+/* PRR_ABI_VERSION of the library that is loaded. */
+int prr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRR_H */

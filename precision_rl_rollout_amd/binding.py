@@ -1,0 +1,190 @@
+"""Thin ctypes binding over libprr.so.
+
+Every function here has the name of the C entry point it calls (see
+``include/prr.h``) and does argument marshalling only: it checks dtypes,
+shapes and devices of torch tensors, allocates the outputs with torch on the
+input's device, passes raw pointers and the current HIP stream, and raises
+``PrrError`` on a non-OK status.  All arithmetic happens in the HIP kernels.
+
+bf16 inputs may be ``torch.bfloat16`` or ``torch.int16`` / ``torch.uint16``
+tensors holding bf16 bit patterns.  FP8 outputs are ``torch.uint8`` codes
+(OCP e4m3; ``.view(torch.float8_e4m3fn)`` reinterprets them), INT8 outputs
+``torch.int8``, scales ``torch.float32``, GEMM outputs ``torch.bfloat16``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libprr.so")
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+_SIGNATURES = {
+    "fp8_weight_block_quant": [_P, _I64, _I64, _P, _P, _P],
+    "fp8_act_token_quant": [_P, _I64, _I64, _P, _P, _P],
+    "w8a8_block_gemm": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P],
+    "int8_weight_channel_quant": [_P, _I64, _I64, _P, _P, _P],
+    "int8_act_token_quant": [_P, _I64, _I64, _P, _P, _P],
+    "w8a8_int8_channel_gemm": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P],
+}
+
+_lib = None
+
+
+class PrrError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} ({status})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libprr.so (once).  Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m precision_rl_rollout_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.prr_status_string.argtypes = [ctypes.c_int]
+        lib.prr_status_string.restype = ctypes.c_char_p
+        lib.prr_abi_version.argtypes = []
+        lib.prr_abi_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().prr_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return load().prr_abi_version()
+
+
+def call(name: str, *args) -> int:
+    """Call a C entry point with raw arguments; returns its status."""
+    return getattr(load(), name)(*args)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _check(name: str, status: int) -> None:
+    if status != 0:
+        raise PrrError(name, status)
+
+
+def _bf16_bits(t: torch.Tensor, what: str) -> torch.Tensor:
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{what}: expected bf16 (or int16 bit patterns), got {t.dtype}")
+    if not t.is_cuda or t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous 2-D CUDA tensor")
+    return t
+
+
+def _operand(t: torch.Tensor, dtype, shape, what: str) -> torch.Tensor:
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_cuda \
+            or not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous CUDA {dtype} tensor of shape "
+                         f"{tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    return t
+
+
+def _out(out, dtype, shape, like: torch.Tensor, what: str) -> torch.Tensor:
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    return _operand(out, dtype, shape, what)
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def fp8_weight_block_quant(w: torch.Tensor, out=None, scale=None):
+    """Wt [N, K] bf16 -> (codes uint8 [N, K], scales fp32 [ceil(N/128), ceil(K/128)])."""
+    w = _bf16_bits(w, "w")
+    N, K = w.shape
+    q = _out(out, torch.uint8, (N, K), w, "out")
+    s = _out(scale, torch.float32, (_cdiv(N, 128), _cdiv(K, 128)), w, "scale")
+    _check("fp8_weight_block_quant",
+           load().fp8_weight_block_quant(_ptr(w), N, K, _ptr(q), _ptr(s), _stream(w)))
+    return q, s
+
+
+def fp8_act_token_quant(a: torch.Tensor, out=None, scale=None):
+    """A [M, K] bf16 -> (codes uint8 [M, K], scales fp32 [M, ceil(K/128)])."""
+    a = _bf16_bits(a, "a")
+    M, K = a.shape
+    q = _out(out, torch.uint8, (M, K), a, "out")
+    s = _out(scale, torch.float32, (M, _cdiv(K, 128)), a, "scale")
+    _check("fp8_act_token_quant",
+           load().fp8_act_token_quant(_ptr(a), M, K, _ptr(q), _ptr(s), _stream(a)))
+    return q, s
+
+
+def w8a8_block_gemm(a_fp8, a_scale, w_fp8, w_scale, out=None):
+    """FP8 codes + block scales -> C [M, N] bf16."""
+    M, K = a_fp8.shape
+    N = w_fp8.shape[0]
+    _operand(a_fp8, torch.uint8, (M, K), "a_fp8")
+    _operand(w_fp8, torch.uint8, (N, K), "w_fp8")
+    _operand(a_scale, torch.float32, (M, _cdiv(K, 128)), "a_scale")
+    _operand(w_scale, torch.float32, (_cdiv(N, 128), _cdiv(K, 128)), "w_scale")
+    c = _out(out, torch.bfloat16, (M, N), a_fp8, "out")
+    _check("w8a8_block_gemm",
+           load().w8a8_block_gemm(_ptr(a_fp8), _ptr(a_scale), _ptr(w_fp8), _ptr(w_scale),
+                                  M, N, K, _ptr(c), _stream(a_fp8)))
+    return c
+
+
+def int8_weight_channel_quant(w: torch.Tensor, out=None, scale=None):
+    """Wt [N, K] bf16 -> (codes int8 [N, K], scales fp32 [N])."""
+    w = _bf16_bits(w, "w")
+    N, K = w.shape
+    q = _out(out, torch.int8, (N, K), w, "out")
+    s = _out(scale, torch.float32, (N,), w, "scale")
+    _check("int8_weight_channel_quant",
+           load().int8_weight_channel_quant(_ptr(w), N, K, _ptr(q), _ptr(s), _stream(w)))
+    return q, s
+
+
+def int8_act_token_quant(a: torch.Tensor, out=None, scale=None):
+    """A [M, K] bf16 -> (codes int8 [M, K], scales fp32 [M])."""
+    a = _bf16_bits(a, "a")
+    M, K = a.shape
+    q = _out(out, torch.int8, (M, K), a, "out")
+    s = _out(scale, torch.float32, (M,), a, "scale")
+    _check("int8_act_token_quant",
+           load().int8_act_token_quant(_ptr(a), M, K, _ptr(q), _ptr(s), _stream(a)))
+    return q, s
+
+
+def w8a8_int8_channel_gemm(a_i8, a_scale, w_i8, w_scale, out=None):
+    """INT8 codes + per-row / per-channel scales -> C [M, N] bf16."""
+    M, K = a_i8.shape
+    N = w_i8.shape[0]
+    _operand(a_i8, torch.int8, (M, K), "a_i8")
+    _operand(w_i8, torch.int8, (N, K), "w_i8")
+    _operand(a_scale, torch.float32, (M,), "a_scale")
+    _operand(w_scale, torch.float32, (N,), "w_scale")
+    c = _out(out, torch.bfloat16, (M, N), a_i8, "out")
+    _check("w8a8_int8_channel_gemm",
+           load().w8a8_int8_channel_gemm(_ptr(a_i8), _ptr(a_scale), _ptr(w_i8), _ptr(w_scale),
+                                         M, N, K, _ptr(c), _stream(a_i8)))
+    return c

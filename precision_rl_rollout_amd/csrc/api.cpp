@@ -1,0 +1,172 @@
+// The C ABI of libprr (declared in include/prr.h): argument checks, device
+// checks, then one launcher call.  No allocation, no synchronization.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "launch.h"
+#include "prr.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7FFFFFFF;        // 2^31 - 1
+constexpr int64_t kMaxInt8GemmK = 133143;      // 127^2 * K < 2^31
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Dimensions: negative or too large -> INVALID_ARG.
+prr_status check_dims(int64_t a, int64_t b, int64_t c = 0) {
+  if (a < 0 || b < 0 || c < 0) return PRR_ERR_INVALID_ARG;
+  if (a > kMaxDim || b > kMaxDim || c > kMaxDim) return PRR_ERR_INVALID_ARG;
+  return PRR_OK;
+}
+
+// Pointers of a non-empty call: NULL -> INVALID_ARG, misaligned -> MISALIGNED.
+prr_status check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p == nullptr) return PRR_ERR_INVALID_ARG;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return PRR_ERR_MISALIGNED;
+  return PRR_OK;
+}
+
+// The current device must exist and be a gfx950.  The answer is cached per
+// device ordinal (a HIP device's architecture does not change in a process).
+prr_status check_device() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return PRR_ERR_NO_DEVICE;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PRR_ERR_NO_DEVICE;
+  static int cache[64];   // 0 unknown, 1 gfx950, 2 other
+  if (dev < 64 && cache[dev] != 0) return cache[dev] == 1 ? PRR_OK : PRR_ERR_UNSUPPORTED_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PRR_ERR_HIP;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) cache[dev] = ok ? 1 : 2;
+  return ok ? PRR_OK : PRR_ERR_UNSUPPORTED_DEVICE;
+}
+
+prr_status from_hip(hipError_t e) { return e == hipSuccess ? PRR_OK : PRR_ERR_HIP; }
+
+#define PRR_TRY(expr)                    \
+  do {                                   \
+    const prr_status st_ = (expr);       \
+    if (st_ != PRR_OK) return st_;       \
+  } while (0)
+
+prr_status quant_common(const void* in, int64_t R, int64_t K, const void* out,
+                        const void* scale, int64_t blocks) {
+  PRR_TRY(check_dims(R, K));
+  if (R == 0 || K == 0) return PRR_OK;
+  PRR_TRY(check_ptrs({in, out, scale}));
+  if (blocks > kMaxGrid) return PRR_ERR_UNSUPPORTED_SHAPE;
+  return check_device();
+}
+
+}  // namespace
+
+extern "C" {
+
+prr_status fp8_weight_block_quant(const uint16_t* w_bf16, int64_t N, int64_t K, uint8_t* w_fp8,
+                                  float* w_scale, hipStream_t stream) {
+  if (N < 0 || K < 0) return PRR_ERR_INVALID_ARG;
+  const int64_t blocks = ((N + 127) / 128) * ((K + 127) / 128);
+  if (N == 0 || K == 0) return check_dims(N, K);
+  PRR_TRY(quant_common(w_bf16, N, K, w_fp8, w_scale, blocks));
+  return from_hip(prr::launch_fp8_weight_block_quant(w_bf16, N, K, w_fp8, w_scale, stream));
+}
+
+prr_status fp8_act_token_quant(const uint16_t* a_bf16, int64_t M, int64_t K, uint8_t* a_fp8,
+                               float* a_scale, hipStream_t stream) {
+  if (M < 0 || K < 0) return PRR_ERR_INVALID_ARG;
+  if (M == 0 || K == 0) return check_dims(M, K);
+  const int64_t wgs = (M * ((K + 127) / 128) + 15) / 16;
+  PRR_TRY(quant_common(a_bf16, M, K, a_fp8, a_scale, wgs));
+  return from_hip(prr::launch_fp8_act_token_quant(a_bf16, M, K, a_fp8, a_scale, stream));
+}
+
+prr_status int8_weight_channel_quant(const uint16_t* w_bf16, int64_t N, int64_t K, int8_t* w_i8,
+                                     float* w_scale, hipStream_t stream) {
+  if (N < 0 || K < 0) return PRR_ERR_INVALID_ARG;
+  if (N == 0 || K == 0) {
+    // K == 0 with N > 0: every row is empty, amax = 0, scale = 0.
+    PRR_TRY(check_dims(N, K));
+    if (N == 0) return PRR_OK;
+    PRR_TRY(check_ptrs({w_scale}));
+    PRR_TRY(check_device());
+    // The row kernel with K == 0 writes scale 0 and reads no element.
+    return from_hip(prr::launch_int8_weight_channel_quant(w_bf16, N, 0, w_i8, w_scale, stream));
+  }
+  PRR_TRY(quant_common(w_bf16, N, K, w_i8, w_scale, N));
+  return from_hip(prr::launch_int8_weight_channel_quant(w_bf16, N, K, w_i8, w_scale, stream));
+}
+
+prr_status int8_act_token_quant(const uint16_t* a_bf16, int64_t M, int64_t K, int8_t* a_i8,
+                                float* a_scale, hipStream_t stream) {
+  if (M < 0 || K < 0) return PRR_ERR_INVALID_ARG;
+  if (M == 0 || K == 0) {
+    PRR_TRY(check_dims(M, K));
+    if (M == 0) return PRR_OK;
+    PRR_TRY(check_ptrs({a_scale}));
+    PRR_TRY(check_device());
+    return from_hip(prr::launch_int8_act_token_quant(a_bf16, M, 0, a_i8, a_scale, stream));
+  }
+  PRR_TRY(quant_common(a_bf16, M, K, a_i8, a_scale, M));
+  return from_hip(prr::launch_int8_act_token_quant(a_bf16, M, K, a_i8, a_scale, stream));
+}
+
+static prr_status gemm_common(const void* a, const void* sa, const void* w, const void* sw,
+                              int64_t M, int64_t N, int64_t K, const void* c, bool int8) {
+  PRR_TRY(check_dims(M, N, K));
+  if (K % 128 != 0) return PRR_ERR_UNSUPPORTED_SHAPE;
+  if (int8 && K > kMaxInt8GemmK) return PRR_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0 || N == 0) return PRR_OK;
+  if (K == 0) {
+    PRR_TRY(check_ptrs({c}));
+    if ((M * N + 255) / 256 > kMaxGrid) return PRR_ERR_UNSUPPORTED_SHAPE;
+  } else {
+    PRR_TRY(check_ptrs({a, sa, w, sw, c}));
+    if ((N + 15) / 16 > kMaxGrid || ((N + 127) / 128) * ((M + 127) / 128) > kMaxGrid)
+      return PRR_ERR_UNSUPPORTED_SHAPE;
+  }
+  return check_device();
+}
+
+prr_status w8a8_block_gemm(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                           const float* w_scale, int64_t M, int64_t N, int64_t K,
+                           uint16_t* c_bf16, hipStream_t stream) {
+  PRR_TRY(gemm_common(a_fp8, a_scale, w_fp8, w_scale, M, N, K, c_bf16, false));
+  if (M == 0 || N == 0) return PRR_OK;
+  return from_hip(
+      prr::launch_w8a8_block_gemm(a_fp8, a_scale, w_fp8, w_scale, M, N, K, c_bf16, stream));
+}
+
+prr_status w8a8_int8_channel_gemm(const int8_t* a_i8, const float* a_scale, const int8_t* w_i8,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                  uint16_t* c_bf16, hipStream_t stream) {
+  PRR_TRY(gemm_common(a_i8, a_scale, w_i8, w_scale, M, N, K, c_bf16, true));
+  if (M == 0 || N == 0) return PRR_OK;
+  return from_hip(
+      prr::launch_w8a8_int8_channel_gemm(a_i8, a_scale, w_i8, w_scale, M, N, K, c_bf16, stream));
+}
+
+const char* prr_status_string(prr_status status) {
+  switch (status) {
+    case PRR_OK: return "PRR_OK";
+    case PRR_ERR_INVALID_ARG: return "PRR_ERR_INVALID_ARG";
+    case PRR_ERR_UNSUPPORTED_SHAPE: return "PRR_ERR_UNSUPPORTED_SHAPE";
+    case PRR_ERR_MISALIGNED: return "PRR_ERR_MISALIGNED";
+    case PRR_ERR_NO_DEVICE: return "PRR_ERR_NO_DEVICE";
+    case PRR_ERR_UNSUPPORTED_DEVICE: return "PRR_ERR_UNSUPPORTED_DEVICE";
+    case PRR_ERR_HIP: return "PRR_ERR_HIP";
+  }
+  return "PRR_ERR_UNKNOWN";
+}
+
+int prr_abi_version(void) { return PRR_ABI_VERSION; }
+
+}  // extern "C"

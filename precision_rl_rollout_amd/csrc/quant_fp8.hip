@@ -1,0 +1,154 @@
+// FP8 e4m3 re-quantization kernels: 128 x 128 weight blocks and 1 x 128
+// per-token activation groups, one fp32 scale amax / 448 per block or group
+// (FP8-RL, abstract: weights change every step and are quantized again;
+// item (i): blockwise FP8 W8A8).
+//
+// Both kernels read each bf16 element once from HBM, keep it in registers
+// while the block's amax is reduced, and write one code byte per element
+// plus one scale per block: 3 bytes of traffic per element.
+#include "launch.h"
+#include "prr_device.h"
+
+namespace prr {
+
+// ---------------------------------------------------------------------------
+// Weight blocks.  One 256-thread workgroup per 128 x 128 block.  Each group
+// of 16 lanes covers one 128-element row segment (16 lanes x 8 bf16 = 256
+// bytes, a fully coalesced row); the workgroup walks 16 rows per step, 8
+// steps, so every lane holds 64 bf16 in 8 x 16-byte registers.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fp8_weight_block_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ q,
+    float* __restrict__ scale, int nbk) {
+  const int bi = blockIdx.x / nbk;
+  const int bj = blockIdx.x - bi * nbk;
+  const int tid = threadIdx.x;
+  const int seg = tid >> 4;       // row within a step, 0..15
+  const int l16 = tid & 15;       // 8-element chunk within the row segment
+  const int64_t row0 = (int64_t)bi * kBlock;
+  const int64_t col = (int64_t)bj * kBlock + l16 * 8;
+  // Workgroup-uniform: a complete block with 16-byte aligned rows takes the
+  // vector path; edge blocks of ragged shapes take the bounds-checked one.
+  const bool full = (row0 + kBlock <= N) && ((int64_t)(bj + 1) * kBlock <= K) && (K % 8 == 0);
+
+  uint4 v[8];
+  uint32_t m = 0;
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = row0 + i * 16 + seg;
+      v[i] = *reinterpret_cast<const uint4*>(w + r * K + col);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = row0 + i * 16 + seg;
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        h[e] = (r < N && col + e < K) ? (uint32_t)w[r * K + col + e] : 0u;
+      v[i] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                        h[6] | (h[7] << 16));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    m = absmax_bf16x2(m, v[i].x);
+    m = absmax_bf16x2(m, v[i].y);
+    m = absmax_bf16x2(m, v[i].z);
+    m = absmax_bf16x2(m, v[i].w);
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t red[4];
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float amax = __uint_as_float(m << 16);
+  const float s = div_rn(amax, kFp8Max);
+  if (tid == 0) scale[(int64_t)bi * nbk + bj] = s;
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = row0 + i * 16 + seg;
+    const uint2 c = e4m3_chunk(v[i], s);
+    if (full) {
+      *reinterpret_cast<uint2*>(q + r * K + col) = c;
+    } else {
+      const uint32_t cw[2] = {c.x, c.y};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (r < N && col + e < K) q[r * K + col + e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Activation groups.  16 lanes per (token, 128-feature group); a 256-thread
+// workgroup covers 16 groups.  The amax never leaves the 16 lanes.
+// ---------------------------------------------------------------------------
+template <bool kVec>
+__global__ __launch_bounds__(256) void fp8_act_group_kernel(
+    const uint16_t* __restrict__ a, int64_t M, int64_t K, uint8_t* __restrict__ q,
+    float* __restrict__ scale, int64_t G) {
+  const int tid = threadIdx.x;
+  const int64_t gid = (int64_t)blockIdx.x * 16 + (tid >> 4);
+  const int l16 = tid & 15;
+  if (gid >= M * G) return;        // whole 16-lane groups leave together
+  const int64_t mrow = gid / G;
+  const int64_t g = gid - mrow * G;
+  const int64_t col = g * kBlock + l16 * 8;
+  const uint16_t* src = a + mrow * K;
+
+  uint4 v;
+  if constexpr (kVec) {            // K % 8 == 0: a chunk is all in or all out
+    v = (col < K) ? *reinterpret_cast<const uint4*>(src + col) : make_uint4(0, 0, 0, 0);
+  } else {
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (col + e < K) ? (uint32_t)src[col + e] : 0u;
+    v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                   h[6] | (h[7] << 16));
+  }
+  uint32_t m = 0;
+  m = absmax_bf16x2(m, v.x);
+  m = absmax_bf16x2(m, v.y);
+  m = absmax_bf16x2(m, v.z);
+  m = absmax_bf16x2(m, v.w);
+  m = lane16_max_u32(m);
+  const float s = div_rn(__uint_as_float(m << 16), kFp8Max);
+  if (l16 == 0) scale[gid] = s;
+  const uint2 c = e4m3_chunk(v, s);
+  uint8_t* dst = q + mrow * K;
+  if constexpr (kVec) {
+    if (col < K) *reinterpret_cast<uint2*>(dst + col) = c;
+  } else {
+    const uint32_t cw[2] = {c.x, c.y};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (col + e < K) dst[col + e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
+  }
+}
+
+hipError_t launch_fp8_weight_block_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q,
+                                         float* scale, hipStream_t stream) {
+  const int64_t nbn = (N + kBlock - 1) / kBlock, nbk = (K + kBlock - 1) / kBlock;
+  const int64_t blocks = nbn * nbk;
+  hipLaunchKernelGGL(fp8_weight_block_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w,
+                     N, K, q, scale, (int)nbk);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_act_token_quant(const uint16_t* a, int64_t M, int64_t K, uint8_t* q,
+                                      float* scale, hipStream_t stream) {
+  const int64_t G = (K + kBlock - 1) / kBlock;
+  const int64_t wgs = (M * G + 15) / 16;
+  if (K % 8 == 0)
+    hipLaunchKernelGGL(fp8_act_group_kernel<true>, dim3((unsigned)wgs), dim3(256), 0, stream,
+                       a, M, K, q, scale, G);
+  else
+    hipLaunchKernelGGL(fp8_act_group_kernel<false>, dim3((unsigned)wgs), dim3(256), 0, stream,
+                       a, M, K, q, scale, G);
+  return hipGetLastError();
+}
+
+}  // namespace prr

@@ -1,0 +1,124 @@
+"""The C ABI of libprr.so, checked from the host (no kernel is launched).
+
+* the library loads and exports every function ``include/prr.h`` declares;
+* every argument check returns its documented status before any device
+  work (negative / oversized dimensions, NULL and misaligned pointers,
+  unsupported GEMM shapes); empty calls succeed and touch nothing;
+* without a visible device, a well-formed call returns PRR_ERR_NO_DEVICE.
+
+Pointers passed here are never dereferenced: every call fails (or is empty)
+before the library reaches a launch.
+"""
+
+import os
+import re
+
+import pytest
+
+from precision_rl_rollout_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "prr.h")
+
+OK, INVALID, SHAPE, MISALIGNED, NO_DEVICE, BAD_DEVICE, HIP = range(7)
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+ODD = 0x10008           # 8-byte aligned only
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:prr_status|const char\*|int)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+def test_header_declares_the_boundary():
+    names = set(_declared())
+    assert names == {"fp8_weight_block_quant", "fp8_act_token_quant", "w8a8_block_gemm",
+                     "int8_weight_channel_quant", "int8_act_token_quant",
+                     "w8a8_int8_channel_gemm", "prr_status_string", "prr_abi_version"}
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert binding.abi_version() == 1
+    names = [binding.status_string(s) for s in range(7)]
+    assert names == ["PRR_OK", "PRR_ERR_INVALID_ARG", "PRR_ERR_UNSUPPORTED_SHAPE",
+                     "PRR_ERR_MISALIGNED", "PRR_ERR_NO_DEVICE", "PRR_ERR_UNSUPPORTED_DEVICE",
+                     "PRR_ERR_HIP"]
+    assert binding.status_string(99) == "PRR_ERR_UNKNOWN"
+
+
+QUANTS = ["fp8_weight_block_quant", "fp8_act_token_quant", "int8_weight_channel_quant",
+          "int8_act_token_quant"]
+GEMMS = ["w8a8_block_gemm", "w8a8_int8_channel_gemm"]
+
+
+@pytest.mark.parametrize("fn", QUANTS)
+def test_quant_argument_checks(fn):
+    c = lambda *a: binding.call(fn, *a)
+    assert c(FAKE, -1, 128, FAKE, FAKE, None) == INVALID
+    assert c(FAKE, 128, -5, FAKE, FAKE, None) == INVALID
+    assert c(FAKE, 2 ** 31, 128, FAKE, FAKE, None) == INVALID
+    assert c(None, 4, 128, FAKE, FAKE, None) == INVALID
+    assert c(FAKE, 4, 128, None, FAKE, None) == INVALID
+    assert c(FAKE, 4, 128, FAKE, None, None) == INVALID
+    assert c(ODD, 4, 128, FAKE, FAKE, None) == MISALIGNED
+    assert c(FAKE, 4, 128, ODD, FAKE, None) == MISALIGNED
+    assert c(FAKE, 4, 128, FAKE, ODD, None) == MISALIGNED
+    # empty along the leading dimension: nothing to do, NULLs allowed
+    assert c(None, 0, 128, None, None, None) == OK
+
+
+@pytest.mark.parametrize("fn", ["fp8_weight_block_quant", "fp8_act_token_quant"])
+def test_fp8_quant_empty_k_is_a_no_op(fn):
+    assert binding.call(fn, None, 7, 0, None, None, None) == OK
+
+
+@pytest.mark.parametrize("fn", GEMMS)
+def test_gemm_argument_checks(fn):
+    c = lambda *a: binding.call(fn, *a)
+    P = [FAKE] * 4
+    assert c(*P, -1, 16, 128, FAKE, None) == INVALID
+    assert c(*P, 1, -16, 128, FAKE, None) == INVALID
+    assert c(*P, 1, 16, -128, FAKE, None) == INVALID
+    assert c(*P, 1, 16, 100, FAKE, None) == SHAPE
+    assert c(*P, 1, 16, 129, FAKE, None) == SHAPE
+    for i in range(4):
+        q = list(P)
+        q[i] = None
+        assert c(*q, 1, 16, 128, FAKE, None) == INVALID
+        q[i] = ODD
+        assert c(*q, 1, 16, 128, FAKE, None) == MISALIGNED
+    assert c(*P, 1, 16, 128, None, None) == INVALID
+    assert c(*P, 1, 16, 128, ODD, None) == MISALIGNED
+    assert c(None, None, None, None, 0, 16, 128, None, None) == OK
+    assert c(None, None, None, None, 5, 0, 128, None, None) == OK
+
+
+def test_int8_gemm_rejects_k_that_could_overflow_int32():
+    P = [FAKE] * 4
+    K = 133248            # first multiple of 128 above 133143
+    assert binding.call("w8a8_int8_channel_gemm", *P, 1, 16, K, FAKE, None) == SHAPE
+    if not _gpu_visible():
+        # the FP8 GEMM has no such limit: it gets as far as the device check
+        # (skipped where a device exists, since that call would launch)
+        assert binding.call("w8a8_block_gemm", *P, 1, 16, K, FAKE, None) == NO_DEVICE
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="needs a process without a GPU")
+@pytest.mark.parametrize("fn", QUANTS + GEMMS)
+def test_no_device_is_reported(fn):
+    if fn in GEMMS:
+        st = binding.call(fn, FAKE, FAKE, FAKE, FAKE, 16, 256, 256, FAKE, None)
+    else:
+        st = binding.call(fn, FAKE, 16, 256, FAKE, FAKE, None)
+    assert st == NO_DEVICE

@@ -1,0 +1,161 @@
+"""GPU parity of the W8A8 GEMMs (FP8 block-scaled and INT8 per-channel)
+against the CPU oracle, through the C ABI.
+
+Both sides start from the same bf16 inputs: the GPU quantizes and
+multiplies with its kernels, the oracle quantizes and multiplies on the
+CPU; the quantized operands are bit-identical (checked in
+test_gpu_quant.py), so the comparison is of the GEMMs.  The bar is a
+relative Frobenius error of at most 1e-3 against the fp64 result rounded
+once to bf16.  Cases: the 16 x 256 x 256 layer, ragged and edge shapes on
+both the decode (M <= 128) and the tiled (M > 128) paths, the 7B decode
+up/gate layer in full, the 32B decode sweep M = 1 .. 128, and the 32B
+prefill up/gate and down GEMMs (oracle on sampled rows).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gemm, quant
+from precision_rl_rollout_amd import binding, workloads
+from tests.gpu_util import Guarded, announce, bits_to_dev, host
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+def _gpu_fp8(A, Wt, w_dev=None):
+    a_dev = bits_to_dev(A)
+    aq, sa = binding.fp8_act_token_quant(a_dev)
+    if w_dev is None:
+        w_dev = binding.fp8_weight_block_quant(bits_to_dev(Wt))
+    wq, sw = w_dev
+    M, N = A.shape[0], wq.shape[0]
+    c = Guarded((M, N), torch.bfloat16)
+    binding.w8a8_block_gemm(aq, sa, wq, sw, out=c.t)
+    out = host(c.t)
+    assert c.intact(), "write outside C"
+    return out
+
+
+def _gpu_int8(A, Wt, w_dev=None):
+    aq, sa = binding.int8_act_token_quant(bits_to_dev(A))
+    if w_dev is None:
+        w_dev = binding.int8_weight_channel_quant(bits_to_dev(Wt))
+    wq, sw = w_dev
+    M, N = A.shape[0], wq.shape[0]
+    c = Guarded((M, N), torch.bfloat16)
+    binding.w8a8_int8_channel_gemm(aq, sa, wq, sw, out=c.t)
+    out = host(c.t)
+    assert c.intact(), "write outside C"
+    return out
+
+
+def _ref_fp8(A, Wt, rows=None, wq_sw=None):
+    aq, sa = quant.fp8_act_token_quant(A if rows is None else A[rows])
+    wq, sw = wq_sw if wq_sw is not None else quant.fp8_weight_block_quant(Wt)
+    c64 = gemm.w8a8_block_gemm(aq, sa, wq, sw)
+    return c64, gemm.round_bf16(c64)
+
+
+def _ref_int8(A, Wt, rows=None, wq_sw=None):
+    aq, sa = quant.int8_act_token_quant(A if rows is None else A[rows])
+    wq, sw = wq_sw if wq_sw is not None else quant.int8_weight_channel_quant(Wt)
+    c64 = gemm.int8_channel_gemm(aq, sa, wq, sw)
+    return c64, gemm.round_bf16(c64)
+
+
+def _check(c_gpu, ref, label):
+    c64, cref = ref
+    err = gemm.rel_frobenius(c_gpu, cref)
+    raw = np.linalg.norm(gemm.bf16_bits_to_f64(c_gpu) - c64) / max(np.linalg.norm(c64), 1e-300)
+    print(f"  {label}: rel_fro vs bf16(oracle) = {err:.3e}; vs unrounded fp64 = {raw:.3e}",
+          flush=True)
+    assert err <= TOL, f"{label}: relative Frobenius error {err:.3e} > {TOL}"
+
+
+GEMM_SHAPES = [(16, 256, 256), (5, 200, 384), (1, 16, 128), (17, 129, 256), (33, 1000, 640),
+               (128, 384, 1024), (129, 385, 512), (130, 300, 256), (256, 256, 1024),
+               (300, 520, 384), (64, 130, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_fp8_gemm_shapes(M, N, K):
+    for seed in (0, 1, 2):
+        p = workloads.gemm_problem(M, N, K, outliers=K >= 512, seed=seed)
+        announce(f"w8a8_block_gemm M{M} N{N} K{K} seed{seed}")
+        _check(_gpu_fp8(p["A"], p["Wt"]), _ref_fp8(p["A"], p["Wt"]), f"M{M} N{N} K{K} s{seed}")
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_int8_gemm_shapes(M, N, K):
+    for seed in (0, 1):
+        p = workloads.gemm_problem(M, N, K, outliers=K >= 512, seed=seed)
+        announce(f"w8a8_int8_channel_gemm M{M} N{N} K{K} seed{seed}")
+        _check(_gpu_int8(p["A"], p["Wt"]), _ref_int8(p["A"], p["Wt"]), f"M{M} N{N} K{K} s{seed}")
+
+
+def test_gemm_k_zero_writes_zeros_and_empty_is_noop():
+    announce("gemm K=0 / empty")
+    for fn, dt in ((binding.w8a8_block_gemm, torch.uint8), (binding.w8a8_int8_channel_gemm, torch.int8)):
+        a = torch.empty((3, 0), dtype=dt, device="cuda:0")
+        w = torch.empty((5, 0), dtype=dt, device="cuda:0")
+        if fn is binding.w8a8_block_gemm:
+            sa = torch.empty((3, 0), dtype=torch.float32, device="cuda:0")
+            sw = torch.empty((1, 0), dtype=torch.float32, device="cuda:0")
+        else:
+            sa = torch.ones(3, device="cuda:0")
+            sw = torch.ones(5, device="cuda:0")
+        c = torch.full((3, 5), 7.0, dtype=torch.bfloat16, device="cuda:0")
+        fn(a, sa, w, sw, out=c)
+        torch.cuda.synchronize()
+        assert torch.all(c.view(torch.int16) == 0)
+
+
+def test_gemm_determinism():
+    p = workloads.gemm_problem(64, 2048, 1024, True, seed=3)
+    announce("gemm determinism")
+    assert np.array_equal(_gpu_fp8(p["A"], p["Wt"]), _gpu_fp8(p["A"], p["Wt"]))
+    assert np.array_equal(_gpu_int8(p["A"], p["Wt"]), _gpu_int8(p["A"], p["Wt"]))
+    q = workloads.gemm_problem(300, 512, 1024, True, seed=3)
+    assert np.array_equal(_gpu_fp8(q["A"], q["Wt"]), _gpu_fp8(q["A"], q["Wt"]))
+
+
+# ----------------------------------------------------------------- full size
+def test_full_7b_decode_upgate():
+    p = workloads.gemm_problem(64, 37888, 3584, True, seed=0)
+    announce("w8a8_block_gemm full 7B decode up/gate M64 N37888 K3584")
+    _check(_gpu_fp8(p["A"], p["Wt"]), _ref_fp8(p["A"], p["Wt"]), "7B up/gate fp8")
+    announce("w8a8_int8_channel_gemm full 7B decode up/gate")
+    _check(_gpu_int8(p["A"], p["Wt"]), _ref_int8(p["A"], p["Wt"]), "7B up/gate int8")
+
+
+def test_full_32b_decode_sweep():
+    A, Wt = workloads.decode_sweep(seed=0)
+    w_ref8 = quant.fp8_weight_block_quant(Wt)
+    w_refi = quant.int8_weight_channel_quant(Wt)
+    w_dev = bits_to_dev(Wt)
+    w_gpu8 = binding.fp8_weight_block_quant(w_dev)
+    w_gpui = binding.int8_weight_channel_quant(w_dev)
+    for M in workloads.DECODE_SWEEP_M:
+        announce(f"w8a8_block_gemm full 32B decode M{M} N27648 K5120")
+        _check(_gpu_fp8(A[:M], None, w_gpu8), _ref_fp8(A[:M], None, wq_sw=w_ref8), f"32B M{M} fp8")
+        announce(f"w8a8_int8_channel_gemm full 32B decode M{M}")
+        _check(_gpu_int8(A[:M], None, w_gpui), _ref_int8(A[:M], None, wq_sw=w_refi), f"32B M{M} int8")
+
+
+@pytest.mark.parametrize("which", ["upgate", "down"])
+def test_full_32b_prefill(which):
+    down = which == "down"
+    N, K = (5120, 27648) if down else (27648, 5120)
+    p = workloads.gemm_problem(8192, N, K, True, seed=0, down=down)
+    rows = np.sort(np.random.default_rng(K).choice(8192, 48, replace=False))
+    rows = np.concatenate([[0], rows, [8191]])
+    announce(f"w8a8_block_gemm full 32B prefill {which} M8192 N{N} K{K}")
+    c = _gpu_fp8(p["A"], p["Wt"])
+    _check(c[rows], _ref_fp8(p["A"], p["Wt"], rows=rows), f"32B prefill {which} fp8 (48+2 rows)")
+    assert np.all(np.isfinite(gemm.bf16_bits_to_f64(c)))
+    announce(f"w8a8_int8_channel_gemm full 32B prefill {which}")
+    c = _gpu_int8(p["A"], p["Wt"])
+    _check(c[rows], _ref_int8(p["A"], p["Wt"], rows=rows), f"32B prefill {which} int8 (48+2 rows)")
