@@ -21,6 +21,8 @@
 // block.  The two operands are filled the same way, so whatever order the
 // instruction walks its k in, every product pairs A[m, k] with W[n, k] for
 // the same k and each k of the block is used once.
+#include <algorithm>
+
 #include "launch.h"
 #include "prr_device.h"
 
@@ -73,91 +75,219 @@ __device__ __forceinline__ void store4(uint16_t* C, int64_t M, int64_t N, int64_
 }
 
 // ---------------------------------------------------------------------------
-// Skinny-M path (decode: M <= 128).  The weight is streamed from HBM once.
-// A workgroup of 4 waves owns one 16-channel strip of the output; the waves
-// split K into 4 contiguous ranges, each wave runs MT m-tiles of 16 tokens
-// over its range, and the 4 partial sums are added through LDS at the end.
+// Skinny-M path (decode: M <= 128).  The weight is streamed from HBM once and
+// is the whole cost: every design choice below serves keeping enough weight
+// bytes in flight per CU.
+//
+// A workgroup is 4 waves arranged as (4 / KS) channel groups x KS K-groups.
+// A wave owns S strips of 16 output channels and all MT m-tiles of 16
+// tokens; K-group g takes K blocks g, g + KS, g + 2 KS, ...  Per K block a
+// wave loads its S weight fragments and MT activation fragments (32 bytes
+// per lane each) into a D-deep register ring, so D blocks of loads are in
+// flight while the MFMAs of the oldest block run.  The KS partial sums of a
+// channel group are added through LDS at the end.  Activations (at most
+// 128 x K bytes) stay in L2 and are re-read by every strip; the weight is
+// read exactly once.
 // ---------------------------------------------------------------------------
-template <int MT, bool kInt8>
+template <int MT, int S, int KS, int D>
+struct SkinnyCfg {
+  static constexpr int kMT = MT, kS = S, kKS = KS, kD = D;
+  static constexpr int kGroups = 4 / KS;                 // channel groups per workgroup
+  static constexpr int kCols = kGroups * S * 16;         // output channels per workgroup
+  static_assert(KS == 1 || KS == 2 || KS == 4, "KS divides 4");
+  static_assert(S * 16 <= 128 && (128 % (S * 16)) == 0, "a wave's strips lie in one 128-block");
+  static_assert(KS == 1 || S * MT <= 16, "the reduction buffer stays within 64 KB of LDS");
+};
+
+// Configuration per m-tile count, chosen by a sweep of (S, KS, D) on MI355X
+// over N = 27648 / 37888, K = 5120 / 3584, M = 1 .. 128 (FP8 and INT8).
+template <int MT> struct SkinnyPick;
+template <> struct SkinnyPick<1> { using type = SkinnyCfg<1, 2, 4, 2>; };
+template <> struct SkinnyPick<2> { using type = SkinnyCfg<2, 4, 4, 2>; };
+template <> struct SkinnyPick<3> { using type = SkinnyCfg<3, 4, 4, 2>; };
+template <> struct SkinnyPick<4> { using type = SkinnyCfg<4, 4, 2, 2>; };
+template <> struct SkinnyPick<5> { using type = SkinnyCfg<5, 2, 2, 2>; };
+template <> struct SkinnyPick<6> { using type = SkinnyCfg<6, 2, 2, 2>; };
+template <> struct SkinnyPick<7> { using type = SkinnyCfg<7, 2, 2, 2>; };
+template <> struct SkinnyPick<8> { using type = SkinnyCfg<8, 2, 2, 2>; };
+
+// Buffer resource (V#) over `bytes` bytes at `base`: raw loads at offsets
+// beyond the range return zeros, so tiles that run past M or N need no
+// per-lane branch (branches around loads would also force the compiler to
+// wait for every outstanding load before the first MFMA).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes),
+                                           0x00020000);
+}
+
+// 32 bytes of one operand row for one 128-deep block: bytes [16 g, 16 g + 16)
+// and [64 + 16 g, 64 + 16 g + 16) of the block, g = lane / 16 (so 4
+// consecutive lanes read 64 contiguous bytes).  Weight and activation
+// fragments are always filled the same way.
+// An offset past every buffer range (ranges are below 2^31 bytes).
+constexpr int kOutOfRange = 0x7FFFFFFF & ~0xFF;
+
+__device__ __forceinline__ v8i buffer_load32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 64, soff, 0);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Activation scales of a skinny problem staged in LDS (floats): M <= 128
+// tokens by up to 64 K blocks (K <= 8192), or fewer tokens by more blocks.
+constexpr int kSkinnyLdsScales = 128 * 64;
+
+template <class Cfg, bool kInt8>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ C) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int MT = Cfg::kMT, S = Cfg::kS, KS = Cfg::kKS, D = Cfg::kD;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kg = wave % KS, cg = wave / KS;
   const int r16 = lane & 15, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t KB = K / kBlock;
-  const int64_t kb0 = (KB * wave) / 4, kb1 = (KB * (wave + 1)) / 4;
+  const int64_t n0 = (int64_t)blockIdx.x * Cfg::kCols + cg * (S * 16);   // wave's first channel
+  const int KB = (int)(K / kBlock);
+  const int nk = (KB - kg + KS - 1) / KS;                                // K blocks of this wave
+  // A wave whose strips all lie past N (possible in the last workgroup)
+  // reads nothing (empty resource); it still joins the reduction.
+  const bool wave_live = n0 < N;                                         // wave-uniform
+  const int64_t wrows = wave_live ? min<int64_t>(S * 16, N - n0) : 0;
+  const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(W + (wave_live ? n0 : 0) * K, wrows * K);
+  const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(A, M * K);
+  // (a dead wave reads the scales of channel block 0: finite values that
+  // multiply its all-zero products)
+  const float* swp = sw + (wave_live ? (n0 >> 7) * KB : 0) + kg;
 
-  const int64_t wrow = n0 + r16;
-  const bool wvalid = wrow < N;
-  const uint8_t* wp = W + wrow * K + g * 32;
-  const uint8_t* ap[MT];
-  bool avalid[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int64_t m = mt * 16 + r16;
-    avalid[mt] = m < M;
-    ap[mt] = A + m * K + g * 32;
+  // Dynamic LDS, used twice: first for the FP8 activation scales of all
+  // MT * 16 token rows, transposed to [K block][row] so that the 16 rows of
+  // a fragment are 16 consecutive words; then, after a barrier, for the
+  // cross-wave reduction of the K-split partial sums.
+  extern __shared__ float lds_dyn[];
+  float* lsa = lds_dyn;
+  if constexpr (!kInt8) {
+    const int rows = MT * 16;
+    for (int e = threadIdx.x; e < rows * KB; e += 256) {
+      const int m = e / KB, kb = e - m * KB;
+      lsa[kb * rows + m] = (m < M) ? sa[(int64_t)m * KB + kb] : 0.f;
+    }
+    __syncthreads();
   }
 
-  float accf[MT][4];
-  v4i acci[MT];
+  int woff[S], aoff[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int s = 0; s < S; ++s) woff[s] = (int)((s * 16 + r16) * K) + g * 16 + kg * kBlock;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) accf[mt][r] = 0.f;
-    acci[mt] = v4i{0, 0, 0, 0};
-  }
+  for (int mt = 0; mt < MT; ++mt) aoff[mt] = (int)((mt * 16 + r16) * K) + g * 16 + kg * kBlock;
 
-  v8i wf = (wvalid && kb0 < kb1) ? load32(wp + kb0 * kBlock) : zero8();
-  for (int64_t kb = kb0; kb < kb1; ++kb) {
-    const v8i wcur = wf;
-    if (kb + 1 < kb1) wf = wvalid ? load32(wp + (kb + 1) * kBlock) : zero8();
-    float swv = 0.f;
-    if constexpr (!kInt8) swv = sw[(n0 >> 7) * KB + kb];
+  float accf[S][MT][4];
+  v4i acci[S][MT];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const v8i af = avalid[mt] ? load32(ap[mt] + kb * kBlock) : zero8();
-      if constexpr (kInt8) {
-        acci[mt] = mfma_i8x2(wcur, af, acci[mt]);
-      } else {
-        const v4f p = mfma_fp8(wcur, af);
-        const float s = (avalid[mt] ? sa[(mt * 16 + r16) * KB + kb] : 0.f) * swv;
+      acci[s][mt] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accf[mt][r] = fmaf(p[r], s, accf[mt][r]);
+      for (int r = 0; r < 4; ++r) accf[s][mt][r] = 0.f;
+    }
+
+  // D-deep register ring of weight and activation fragments.  The stream
+  // holds nothing but these 16-byte loads and is issued in stage order, so
+  // the wait before a stage's MFMAs lets the younger D - 1 stages stay in
+  // flight.  Stages past the wave's last K block are loaded at an offset
+  // outside every buffer (no memory traffic, zeros returned) and their
+  // MFMAs add zeros, which keeps the pipeline free of branches.
+  v8i wbuf[D][S], abuf[D][MT];
+  auto load_stage = [&](int d, int i) {
+    const int kofs = (i < nk) ? i * (KS * kBlock) : kOutOfRange;     // wave-uniform
+#pragma unroll
+    for (int s = 0; s < S; ++s) wbuf[d][s] = buffer_load32(wres, woff[s] + kofs, 0);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) abuf[d][mt] = buffer_load32(ares, aoff[mt] + kofs, 0);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load_stage(d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  for (int t = 0; t < nk; t += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int i = t + d;
+      if constexpr (kInt8) {
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acci[s][mt] = mfma_i8x2(wbuf[d][s], abuf[d][mt], acci[s][mt]);
+      } else {
+        const int ic = min(i, nk - 1);
+        const float swv = swp[ic * KS];
+        const float* srow = lsa + (kg + ic * KS) * (MT * 16) + r16;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const v4f p = mfma_fp8(wbuf[d][s], abuf[d][mt]);
+            const float sc = srow[mt * 16] * swv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accf[s][mt][r] = fmaf(p[r], sc, accf[s][mt][r]);
+          }
       }
+      load_stage(d, i + D);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // Cross-wave reduction of the K-split partial sums (int32 partials are
-  // stored bit-cast in the same array).
-  __shared__ float red[4][MT][4][64];
+  // Add the KS partial sums of each channel group (int32 partials are
+  // stored bit-cast in the same array) and store.
+  if constexpr (KS > 1) {
+    if constexpr (!kInt8) __syncthreads();          // every wave is done with lsa
+    auto red = reinterpret_cast<float (*)[S][MT][4][64]>(lds_dyn);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int s = 0; s < S; ++s)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      red[wave][mt][r][lane] = kInt8 ? __int_as_float(acci[mt][r]) : accf[mt][r];
-  __syncthreads();
-  // Wave w finishes m-tiles w, w+4, ...
-  for (int mt = wave; mt < MT; mt += 4) {
-    const int64_t m = mt * 16 + r16;
-    const int64_t n = n0 + 4 * g;
-    float v[4];
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (kInt8) {
-        const int32_t t = __float_as_int(red[0][mt][r][lane]) + __float_as_int(red[1][mt][r][lane]) +
-                          __float_as_int(red[2][mt][r][lane]) + __float_as_int(red[3][mt][r][lane]);
-        const float sm = (m < M) ? sa[m] : 0.f;
-        const float sn = (n + r < N) ? sw[n + r] : 0.f;
-        v[r] = (float)t * (sm * sn);
-      } else {
-        v[r] = (red[0][mt][r][lane] + red[1][mt][r][lane]) +
-               (red[2][mt][r][lane] + red[3][mt][r][lane]);
-      }
-    }
-    store4(C, M, N, m, n, v);
+        for (int r = 0; r < 4; ++r)
+          red[wave][s][mt][r][lane] = kInt8 ? __int_as_float(acci[s][mt][r]) : accf[s][mt][r];
+    __syncthreads();
+    if (kg != 0) return;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int j = 1; j < KS; ++j) {
+            if constexpr (kInt8)
+              acci[s][mt][r] += __float_as_int(red[wave + j][s][mt][r][lane]);
+            else
+              accf[s][mt][r] += red[wave + j][s][mt][r][lane];
+          }
   }
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int64_t m = mt * 16 + r16;
+      const int64_t n = n0 + s * 16 + 4 * g;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (kInt8) {
+          const float sm = (m < M) ? sa[m] : 0.f;
+          const float sn = (n + r < N) ? sw[n + r] : 0.f;
+          v[r] = (float)acci[s][mt][r] * (sm * sn);
+        } else {
+          v[r] = accf[s][mt][r];
+        }
+      }
+      store4(C, M, N, m, n, v);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -280,14 +410,21 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
                        stream, C, count);
     return hipGetLastError();
   }
-  if (M <= 128) {
-    const unsigned grid = (unsigned)((N + 15) / 16);
+  const int64_t mt16 = (M + 15) / 16 * 16;
+  if (M <= 128 && (kInt8 || mt16 * (K / kBlock) <= kSkinnyLdsScales)) {
     const int mt = (int)((M + 15) / 16);
-#define PRR_SKINNY(T)                                                                          \
-  case T:                                                                                      \
-    hipLaunchKernelGGL((gemm_skinny_kernel<T, kInt8>), dim3(grid), dim3(256), 0, stream, A, sa, \
-                       W, sw, M, N, K, C);                                                     \
-    break;
+#define PRR_SKINNY(X)                                                                        \
+  case X: {                                                                                  \
+    using Cfg = typename SkinnyPick<X>::type;                                                \
+    const unsigned grid = (unsigned)((N + Cfg::kCols - 1) / Cfg::kCols);                    \
+    const size_t lds_scales = kInt8 ? 0 : (size_t)(X * 16) * (K / kBlock) * sizeof(float);  \
+    const size_t lds_red =                                                                   \
+        Cfg::kKS > 1 ? (size_t)4 * Cfg::kS * X * 4 * 64 * sizeof(float) : 0;               \
+    const size_t lds = lds_scales > lds_red ? lds_scales : lds_red;                         \
+    hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, kInt8>), dim3(grid), dim3(256), lds, stream, \
+                       A, sa, W, sw, M, N, K, C);                                            \
+    break;                                                                                   \
+  }
     switch (mt) {
       PRR_SKINNY(1)
       PRR_SKINNY(2)

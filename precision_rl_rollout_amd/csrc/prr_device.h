@@ -17,12 +17,17 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Running max of |x| over a word of two bf16 values, on bit patterns: for
 // non-negative IEEE values the bit-pattern order is the value order, so a
 // max over the 15-bit magnitudes of both halves gives amax exactly.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Packed form: keeps the two running maxima in the two halves of `m`
+// (one v_pk_max_u16 per word); fold with absmax_fold() at the end.
 __device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t m, uint32_t w) {
-  const uint32_t a = w & 0x7FFF7FFFu;
-  const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
-  m = max(m, lo);
-  return max(m, hi);
+  const u16x2 a = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+  const u16x2 b = __builtin_bit_cast(u16x2, m);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
 }
+
+__device__ __forceinline__ uint32_t absmax_fold(uint32_t m) { return max(m & 0xFFFFu, m >> 16); }
 
 // Max over all 64 lanes of a wave (result in every lane).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
@@ -40,80 +45,132 @@ __device__ __forceinline__ uint32_t lane16_max_u32(uint32_t v) {
 
 // fl32(x / s), IEEE binary32 division with round-to-nearest-even.  HIP's
 // fp32 '/' is correctly rounded by default (no fast-math flags are used
-// anywhere in this library) and fp32 subnormals are preserved.
+// anywhere in this library) and fp32 subnormals are preserved.  Used once
+// per block, for the scale itself and the reciprocal below.
 __device__ __forceinline__ float div_rn(float x, float s) { return x / s; }
 
-// Saturating round-to-nearest-even OCP e4m3 code of an fp32 value, built
-// from the fp32 fields with integer arithmetic (no conversion instruction):
-//   |v| >= 448            -> 0x7E (saturate; NaN is never produced)
-//   2^-6 <= |v| < 448     -> round the 23-bit mantissa to 3 bits, ties to
-//                            even (add 0x7FFFF plus the kept LSB), then
-//                            rebias the exponent from 127 to 7
-//   |v| < 2^-6            -> subnormal: RNE(|v| * 2^9), exact scaling;
-//                            a result of 8 is the smallest normal's code
-// and the sign bit is copied (so -0 -> 0x80).
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t a = b & 0x7FFFFFFFu;
-  const uint32_t rn = a + 0x7FFFFu + ((a >> 20) & 1u);
-  const uint32_t cn = (rn >> 20) - (120u << 3);
-  const uint32_t cs = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  uint32_t c = (a < 0x3C800000u) ? cs : cn;     // 0x3C800000 = 2^-6
-  c = (a >= 0x43E00000u) ? 0x7Eu : c;           // 0x43E00000 = 448
-  return c | ((b >> 24) & 0x80u);
+// Division of every element of a block by the block's scale s > 0.
+//
+// A correctly rounded divide costs about ten VALU instructions; a block
+// divides many elements by one s, so the reciprocal r = RN(1/s) is formed
+// once and each quotient takes Markstein's correction step (P. Markstein,
+// "Computation of elementary functions on the IBM RISC System/6000
+// processor", IBM J. Res. Dev. 34(1), 1990; also Muller et al., "Handbook
+// of Floating-Point Arithmetic", on division with an FMA):
+//     y = RN(x r),  e = fma(-y, s, x)  (exact),  q = RN(e r + y).
+// Blocks with s < 2^-64 first scale s and x by 2^96 (exact: both are
+// powers-of-two multiples, and |x| <= 448 s stays tiny) so that the
+// remainder never underflows where it matters.  The fma loses the sign of
+// a zero quotient, which the copysign restores (x / s has the sign of x).
+//
+// Used only where its result is encoded to e4m3 or int8.  The encoded
+// results equal those of encode(x / s) for every pair of bf16 values with
+// |x| <= amax and s = fl32(amax / 448) or fl32(amax / 127): this was
+// checked exhaustively on gfx950 (all 32,639 positive finite amax, every
+// bf16 x of either sign up to it, ~2.1e9 pairs per divisor).  The fp32
+// quotients themselves may differ from x / s in the last bit only below
+// 2e-15, where both encode to zero.
+struct BlockDiv {
+  float s;   // s, or s * 2^96
+  float r;   // RN(1 / s) of the above
+  bool tiny;
+};
+
+__device__ __forceinline__ BlockDiv block_div(float s) {
+  BlockDiv d;
+  d.tiny = s < 0x1p-64f;
+  d.s = d.tiny ? s * 0x1p96f : s;
+  d.r = div_rn(1.0f, d.s);
+  return d;
 }
 
-// Four e4m3 codes packed little-endian into one word.
+template <bool kTiny>
+__device__ __forceinline__ float div_block(float x, const BlockDiv& d) {
+  if constexpr (kTiny) x *= 0x1p96f;
+  const float y = x * d.r;
+  const float e = __builtin_fmaf(-y, d.s, x);
+  return __builtin_copysignf(__builtin_fmaf(e, d.r, y), x);
+}
+
+// Four e4m3 codes of four quotients, packed little-endian, by the hardware
+// conversion (round to nearest even from the MODE register, e4m3 with
+// subnormals).  It does not saturate: magnitudes in (464, 480] would give
+// NaN.  Quotients of a block never exceed 448 * (1 + 2^-8) < 464 (the
+// scale is amax / 448 rounded to fp32, relative error below 2^-8 even for
+// subnormal scales), so no clamp is needed.  On every fp32 value with
+// |v| <= 464 the conversion equals the saturating RNE e4m3 code built from
+// the fp32 fields with integer arithmetic (checked exhaustively on gfx950
+// over all such fp32 patterns, both signs, zeros and subnormals included).
+__device__ __forceinline__ uint32_t cvt_e4m3x4(float q0, float q1, float q2, float q3) {
+  int d = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+  d = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, d, true);
+  return (uint32_t)d;
+}
+
+// Eight bf16 values (one 16-byte chunk) -> eight e4m3 codes (8 bytes).
+template <bool kTiny>
+__device__ __forceinline__ uint2 e4m3_chunk(uint4 w, const BlockDiv& d) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w0 = ws[2 * h], w1 = ws[2 * h + 1];
+    out[h] = cvt_e4m3x4(div_block<kTiny>(bf16_lo(w0), d), div_block<kTiny>(bf16_hi(w0), d),
+                        div_block<kTiny>(bf16_lo(w1), d), div_block<kTiny>(bf16_hi(w1), d));
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+// An all-zero block (s == 0): every element is a signed zero and its code
+// is its sign bit.
+__device__ __forceinline__ uint2 e4m3_zero_chunk(uint4 w) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w0 = ws[2 * h], w1 = ws[2 * h + 1];
+    out[h] = ((w0 >> 8) & 0x80u) | ((w0 >> 16) & 0x8000u) | ((w1 << 8) & 0x800000u) |
+             (w1 & 0x80000000u);
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+// e4m3 chunk for any block: dispatch on the block-uniform scale class.
+__device__ __forceinline__ uint2 e4m3_chunk_any(uint4 w, float s, const BlockDiv& d) {
+  if (s == 0.0f) return e4m3_zero_chunk(w);
+  return d.tiny ? e4m3_chunk<true>(w, d) : e4m3_chunk<false>(w, d);
+}
+
+// Four bytes packed little-endian into one word.
 __device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
   return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
 }
 
-// Eight bf16 values (one 16-byte chunk) -> eight e4m3 codes (8 bytes).
-// s == 0 only for an all-zero block, where every x is a signed zero and the
-// code is its sign.
-__device__ __forceinline__ uint2 e4m3_chunk(uint4 w, float s) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  uint32_t out[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint32_t c[4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t word = ws[2 * h + j];
-      const float x0 = bf16_lo(word), x1 = bf16_hi(word);
-      const float v0 = (s != 0.0f) ? div_rn(x0, s) : x0;
-      const float v1 = (s != 0.0f) ? div_rn(x1, s) : x1;
-      c[2 * j] = e4m3_code(v0);
-      c[2 * j + 1] = e4m3_code(v1);
-    }
-    out[h] = pack4(c[0], c[1], c[2], c[3]);
-  }
-  return make_uint2(out[0], out[1]);
-}
-
 // clamp(RNE(v), -127, 127) as a byte.
 __device__ __forceinline__ uint32_t int8_code(float v) {
-  float r = __builtin_rintf(v);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(v), -127.0f, 127.0f);
   return (uint32_t)((int32_t)r) & 0xFFu;
 }
 
-__device__ __forceinline__ uint2 int8_chunk(uint4 w, float s) {
+template <bool kTiny>
+__device__ __forceinline__ uint2 int8_chunk(uint4 w, const BlockDiv& d) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t out[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    uint32_t c[4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t word = ws[2 * h + j];
-      const float x0 = bf16_lo(word), x1 = bf16_hi(word);
-      c[2 * j] = (s != 0.0f) ? int8_code(div_rn(x0, s)) : 0u;
-      c[2 * j + 1] = (s != 0.0f) ? int8_code(div_rn(x1, s)) : 0u;
-    }
-    out[h] = pack4(c[0], c[1], c[2], c[3]);
+    const uint32_t w0 = ws[2 * h], w1 = ws[2 * h + 1];
+    out[h] = pack4(int8_code(div_block<kTiny>(bf16_lo(w0), d)),
+                   int8_code(div_block<kTiny>(bf16_hi(w0), d)),
+                   int8_code(div_block<kTiny>(bf16_lo(w1), d)),
+                   int8_code(div_block<kTiny>(bf16_hi(w1), d)));
   }
   return make_uint2(out[0], out[1]);
+}
+
+// int8 chunk for any row: an all-zero row (s == 0) has codes 0.
+__device__ __forceinline__ uint2 int8_chunk_any(uint4 w, float s, const BlockDiv& d) {
+  if (s == 0.0f) return make_uint2(0u, 0u);
+  return d.tiny ? int8_chunk<true>(w, d) : int8_chunk<false>(w, d);
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).

@@ -17,6 +17,29 @@ namespace prr {
 // bytes, a fully coalesced row); the workgroup walks 16 rows per step, 8
 // steps, so every lane holds 64 bf16 in 8 x 16-byte registers.
 // ---------------------------------------------------------------------------
+// Encode the 8 chunks a lane holds and store them (block-uniform class:
+// kClass 0 = all-zero block, 1 = ordinary, 2 = tiny scale).
+template <int kClass>
+__device__ __forceinline__ void encode_block_rows(const uint4 (&v)[8], const BlockDiv& d,
+                                                  bool full, uint8_t* __restrict__ q, int64_t N,
+                                                  int64_t K, int64_t row0, int seg, int64_t col) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = row0 + i * 16 + seg;
+    uint2 c;
+    if constexpr (kClass == 0) c = e4m3_zero_chunk(v[i]);
+    else c = e4m3_chunk<kClass == 2>(v[i], d);
+    if (full) {
+      *reinterpret_cast<uint2*>(q + r * K + col) = c;
+    } else {
+      const uint32_t cw[2] = {c.x, c.y};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (r < N && col + e < K) q[r * K + col + e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ q,
     float* __restrict__ scale, int nbk) {
@@ -32,7 +55,6 @@ __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
   const bool full = (row0 + kBlock <= N) && ((int64_t)(bj + 1) * kBlock <= K) && (K % 8 == 0);
 
   uint4 v[8];
-  uint32_t m = 0;
   if (full) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -51,6 +73,7 @@ __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
                         h[6] | (h[7] << 16));
     }
   }
+  uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     m = absmax_bf16x2(m, v[i].x);
@@ -58,7 +81,7 @@ __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
     m = absmax_bf16x2(m, v[i].z);
     m = absmax_bf16x2(m, v[i].w);
   }
-  m = wave_max_u32(m);
+  m = wave_max_u32(absmax_fold(m));
   __shared__ uint32_t red[4];
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
@@ -67,19 +90,10 @@ __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
   const float s = div_rn(amax, kFp8Max);
   if (tid == 0) scale[(int64_t)bi * nbk + bj] = s;
 
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t r = row0 + i * 16 + seg;
-    const uint2 c = e4m3_chunk(v[i], s);
-    if (full) {
-      *reinterpret_cast<uint2*>(q + r * K + col) = c;
-    } else {
-      const uint32_t cw[2] = {c.x, c.y};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (r < N && col + e < K) q[r * K + col + e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
-    }
-  }
+  const BlockDiv d = block_div(s);
+  if (s == 0.0f) encode_block_rows<0>(v, d, full, q, N, K, row0, seg, col);
+  else if (d.tiny) encode_block_rows<2>(v, d, full, q, N, K, row0, seg, col);
+  else encode_block_rows<1>(v, d, full, q, N, K, row0, seg, col);
 }
 
 // ---------------------------------------------------------------------------
@@ -114,10 +128,10 @@ __global__ __launch_bounds__(256) void fp8_act_group_kernel(
   m = absmax_bf16x2(m, v.y);
   m = absmax_bf16x2(m, v.z);
   m = absmax_bf16x2(m, v.w);
-  m = lane16_max_u32(m);
+  m = lane16_max_u32(absmax_fold(m));
   const float s = div_rn(__uint_as_float(m << 16), kFp8Max);
   if (l16 == 0) scale[gid] = s;
-  const uint2 c = e4m3_chunk(v, s);
+  const uint2 c = e4m3_chunk_any(v, s, block_div(s));
   uint8_t* dst = q + mrow * K;
   if constexpr (kVec) {
     if (col < K) *reinterpret_cast<uint2*>(dst + col) = c;

@@ -3,104 +3,135 @@
 // article: INT8 rollout with the weights re-quantized after every update;
 // the granularity is fixed by this library).
 //
-// One 256-thread workgroup per row.  Rows up to kResident elements stay in
-// registers between the amax reduction and the encode, so every element is
-// read from HBM once; longer rows are read twice, the second time from the
-// L2 that the first pass just filled.
+// A row is held in registers between its amax reduction and the encode, so
+// every element is read from HBM once:
+//   * K <= 8192:  one wave per row (up to 16 x 16-byte chunks per lane),
+//                 4 rows per 256-thread workgroup, reduction inside the wave;
+//   * K <= 32768: one 256-thread workgroup per row, reduction through LDS;
+//   * longer rows (and K % 8 != 0): a workgroup per row reads the row twice,
+//                 the second time from the L2 the first pass filled.
 #include "launch.h"
 #include "prr_device.h"
 
 namespace prr {
 
-constexpr int kRowThreads = 256;
-constexpr int kResidentChunks = 8;                           // 16-byte chunks per lane
-constexpr int64_t kResident = kRowThreads * 8 * kResidentChunks;  // 16384 elements
+constexpr int kMaxChunks = 16;       // 16-byte chunks a lane keeps in registers
 
-__device__ __forceinline__ float block_amax(uint32_t m, uint32_t* red) {
-  m = wave_max_u32(m);
-  const int tid = threadIdx.x;
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  __syncthreads();
-  m = max(max(red[0], red[1]), max(red[2], red[3]));
-  return __uint_as_float(m << 16);
+template <int kClass>
+__device__ __forceinline__ uint2 int8_chunk_class(uint4 w, const BlockDiv& d) {
+  if constexpr (kClass == 0) return make_uint2(0u, 0u);
+  else return int8_chunk<kClass == 2>(w, d);
 }
 
-// K % 8 == 0: 16-byte chunks.
-template <bool kResidentRow>
-__global__ __launch_bounds__(kRowThreads) void int8_row_kernel_vec(
+template <int kClass, int kLanes>
+__device__ __forceinline__ void int8_store_row(const uint4 (&v)[kMaxChunks], const BlockDiv& d,
+                                               uint8_t* __restrict__ dst, int64_t chunks,
+                                               int lane) {
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int64_t c = (int64_t)i * kLanes + lane;
+    if (c < chunks) *reinterpret_cast<uint2*>(dst + c * 8) = int8_chunk_class<kClass>(v[i], d);
+  }
+}
+
+// Register-resident row: kLanes lanes (64: a wave, 256: the workgroup) per row.
+template <int kLanes>
+__global__ __launch_bounds__(256) void int8_row_resident_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t K, int8_t* __restrict__ q,
+    float* __restrict__ scale) {
+  constexpr int kRowsPerWg = 256 / kLanes;
+  const int tid = threadIdx.x;
+  const int lane = tid % kLanes;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + tid / kLanes;
+  const bool live = row < R;                    // uniform per row group
+  const int64_t chunks = K / 8;
+  const uint16_t* src = x + row * K;
+  uint4 v[kMaxChunks];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int64_t c = (int64_t)i * kLanes + lane;
+    v[i] = (live && c < chunks) ? *reinterpret_cast<const uint4*>(src + c * 8)
+                                : make_uint4(0, 0, 0, 0);
+    m = absmax_bf16x2(m, v[i].x);
+    m = absmax_bf16x2(m, v[i].y);
+    m = absmax_bf16x2(m, v[i].z);
+    m = absmax_bf16x2(m, v[i].w);
+  }
+  m = wave_max_u32(absmax_fold(m));
+  if constexpr (kLanes == 256) {
+    __shared__ uint32_t red[4];
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+  }
+  if (!live) return;
+  const float s = div_rn(__uint_as_float(m << 16), kInt8Max);
+  if (lane == 0) scale[row] = s;
+  const BlockDiv d = block_div(s);
+  uint8_t* dst = reinterpret_cast<uint8_t*>(q) + row * K;
+  if (s == 0.0f) int8_store_row<0, kLanes>(v, d, dst, chunks, lane);
+  else if (d.tiny) int8_store_row<2, kLanes>(v, d, dst, chunks, lane);
+  else int8_store_row<1, kLanes>(v, d, dst, chunks, lane);
+}
+
+// Any K: a workgroup per row, two passes; 16-byte chunks when K % 8 == 0,
+// single elements otherwise.
+__global__ __launch_bounds__(256) void int8_row_twopass_kernel(
     const uint16_t* __restrict__ x, int64_t K, int8_t* __restrict__ q,
     float* __restrict__ scale) {
   __shared__ uint32_t red[4];
   const int64_t row = blockIdx.x;
   const uint16_t* src = x + row * K;
   uint8_t* dst = reinterpret_cast<uint8_t*>(q) + row * K;
-  const int64_t chunks = K / 8;
   const int tid = threadIdx.x;
+  const bool vec = (K % 8) == 0;
   uint32_t m = 0;
-  if constexpr (kResidentRow) {
-    uint4 v[kResidentChunks];
-#pragma unroll
-    for (int i = 0; i < kResidentChunks; ++i) {
-      const int64_t c = (int64_t)i * kRowThreads + tid;
-      v[i] = (c < chunks) ? *reinterpret_cast<const uint4*>(src + c * 8) : make_uint4(0, 0, 0, 0);
-      m = absmax_bf16x2(m, v[i].x);
-      m = absmax_bf16x2(m, v[i].y);
-      m = absmax_bf16x2(m, v[i].z);
-      m = absmax_bf16x2(m, v[i].w);
-    }
-    const float s = div_rn(block_amax(m, red), kInt8Max);
-    if (tid == 0) scale[row] = s;
-#pragma unroll
-    for (int i = 0; i < kResidentChunks; ++i) {
-      const int64_t c = (int64_t)i * kRowThreads + tid;
-      if (c < chunks) *reinterpret_cast<uint2*>(dst + c * 8) = int8_chunk(v[i], s);
-    }
-  } else {
-    for (int64_t c = tid; c < chunks; c += kRowThreads) {
+  if (vec) {
+    for (int64_t c = tid; c < K / 8; c += 256) {
       const uint4 v = *reinterpret_cast<const uint4*>(src + c * 8);
       m = absmax_bf16x2(m, v.x);
       m = absmax_bf16x2(m, v.y);
       m = absmax_bf16x2(m, v.z);
       m = absmax_bf16x2(m, v.w);
     }
-    const float s = div_rn(block_amax(m, red), kInt8Max);
-    if (tid == 0) scale[row] = s;
-    for (int64_t c = tid; c < chunks; c += kRowThreads) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src + c * 8);
-      *reinterpret_cast<uint2*>(dst + c * 8) = int8_chunk(v, s);
-    }
+    m = absmax_fold(m);
+  } else {
+    for (int64_t k = tid; k < K; k += 256) m = max(m, (uint32_t)(src[k] & 0x7FFFu));
   }
-}
-
-// Any K: element-wise, bounds-checked.
-__global__ __launch_bounds__(kRowThreads) void int8_row_kernel_any(
-    const uint16_t* __restrict__ x, int64_t K, int8_t* __restrict__ q,
-    float* __restrict__ scale) {
-  __shared__ uint32_t red[4];
-  const int64_t row = blockIdx.x;
-  const uint16_t* src = x + row * K;
-  const int tid = threadIdx.x;
-  uint32_t m = 0;
-  for (int64_t k = tid; k < K; k += kRowThreads) m = max(m, (uint32_t)(src[k] & 0x7FFFu));
-  const float s = div_rn(block_amax(m, red), kInt8Max);
+  m = wave_max_u32(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float s = div_rn(__uint_as_float(m << 16), kInt8Max);
   if (tid == 0) scale[row] = s;
-  for (int64_t k = tid; k < K; k += kRowThreads) {
-    const float xv = __uint_as_float((uint32_t)src[k] << 16);
-    q[row * K + k] = (int8_t)(s != 0.0f ? int8_code(div_rn(xv, s)) : 0u);
+  const BlockDiv d = block_div(s);
+  if (vec) {
+    for (int64_t c = tid; c < K / 8; c += 256) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + c * 8);
+      *reinterpret_cast<uint2*>(dst + c * 8) = int8_chunk_any(v, s, d);
+    }
+  } else {
+    for (int64_t k = tid; k < K; k += 256) {
+      const float xv = __uint_as_float((uint32_t)src[k] << 16);
+      uint32_t c = 0;
+      if (s != 0.0f) c = int8_code(d.tiny ? div_block<true>(xv, d) : div_block<false>(xv, d));
+      dst[k] = (uint8_t)c;
+    }
   }
 }
 
 static hipError_t launch_int8_rows(const uint16_t* x, int64_t R, int64_t K, int8_t* q,
                                    float* scale, hipStream_t stream) {
-  if (K % 8 == 0 && K <= kResident)
-    hipLaunchKernelGGL(int8_row_kernel_vec<true>, dim3((unsigned)R), dim3(kRowThreads), 0,
-                       stream, x, K, q, scale);
-  else if (K % 8 == 0)
-    hipLaunchKernelGGL(int8_row_kernel_vec<false>, dim3((unsigned)R), dim3(kRowThreads), 0,
-                       stream, x, K, q, scale);
+  if (K % 8 == 0 && K <= 64 * 8 * kMaxChunks)
+    hipLaunchKernelGGL(int8_row_resident_kernel<64>, dim3((unsigned)((R + 3) / 4)), dim3(256), 0,
+                       stream, x, R, K, q, scale);
+  else if (K % 8 == 0 && K <= 256 * 8 * kMaxChunks)
+    hipLaunchKernelGGL(int8_row_resident_kernel<256>, dim3((unsigned)R), dim3(256), 0, stream, x,
+                       R, K, q, scale);
   else
-    hipLaunchKernelGGL(int8_row_kernel_any, dim3((unsigned)R), dim3(kRowThreads), 0, stream, x,
-                       K, q, scale);
+    hipLaunchKernelGGL(int8_row_twopass_kernel, dim3((unsigned)R), dim3(256), 0, stream, x, K, q,
+                       scale);
   return hipGetLastError();
 }
 
