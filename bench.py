@@ -79,11 +79,13 @@ KERNEL_SOURCES = {
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if
     it was taken on the kernel's current sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
-    with open(path) as f:
-        table = json.load(f)
+    text = open(path).read()
+    if "```json" not in text:
+        return None
+    table = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     rec = table.get(f"{kernel}@{workload}")
     if not rec or rec.get("sources") != _sources_digest(KERNEL_SOURCES[kernel]):
         return None
@@ -199,12 +201,12 @@ def run_decode7b(args, torch, B, W):
 
 
 def cpu_baseline_decode7b(W, step_bytes):
-    """The oracle, as it stands, on a bounded sample of the same step: the
-    full activation and the first `rows` weight rows (one N slice), all six
-    operations; scaled to the step's unit (algorithmic GB/s)."""
+    """The oracle, as it stands, on one whole step of the same workload (all
+    six operations on the full A and Wt, about 10-20 s on 8-16 host cores),
+    in the step's unit (algorithmic GB/s)."""
     from oracle import gemm, quant
     M, N, K = 64, 37888, 3584
-    rows = 2048
+    rows = N
     p = W.gemm_problem(M, N, K, True, seed=0)
     A, Wt = p["A"], p["Wt"][:rows]
     t0 = time.perf_counter()
@@ -221,8 +223,8 @@ def cpu_baseline_decode7b(W, step_bytes):
                     + gemm_bytes(M, rows, K, M, rows))
     return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"all six operations with the full A [64, 3584] and Wt rows 0..{rows - 1} "
-                      f"of 37888 (N = {rows}); numpy elementwise (1 thread) + fp64 BLAS"}
+            "sample": f"one whole step: all six operations on A [64, 3584] and Wt [{rows}, 3584]; "
+                      f"numpy elementwise (1 thread) + fp64 BLAS ({cpu_threads()} threads)"}
 
 
 def _cold_copies(torch, make, nbytes, budget=600 << 20):
@@ -365,6 +367,10 @@ def main(argv=None):
     ap.add_argument("--workload", default="decode7b_upgate",
                     choices=["decode7b_upgate", "decode32b_sweep", "prefill32b", "stack32b_requant"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 512 MiB device copy three times (outside the "
+                         "timed region): the reference kernel for scaling rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path is a single-GPU kernel library "
@@ -378,6 +384,13 @@ def main(argv=None):
     from precision_rl_rollout_amd import binding as B
     from precision_rl_rollout_amd import workloads as W
     B.load()
+    if args.copy_calibration:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     run = {"decode7b_upgate": run_decode7b, "decode32b_sweep": run_decode32b,
            "prefill32b": run_prefill32b, "stack32b_requant": run_stack32b}[args.workload]
     line = run(args, torch, B, W)
