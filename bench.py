@@ -73,6 +73,9 @@ KERNEL_SOURCES = {
     "int8_act_token_quant": ["quant_int8.hip", "prr_device.h"],
     "w8a8_block_gemm": ["gemm.hip", "prr_device.h"],
     "w8a8_int8_channel_gemm": ["gemm.hip", "prr_device.h"],
+    # M <= 64 runs the persistent decode kernel.
+    "w8a8_block_gemm@decode7b_upgate": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
+    "w8a8_int8_channel_gemm@decode7b_upgate": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
 }
 
 
@@ -87,7 +90,8 @@ def measured_traffic(kernel, workload):
         return None
     table = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     rec = table.get(f"{kernel}@{workload}")
-    if not rec or rec.get("sources") != _sources_digest(KERNEL_SOURCES[kernel]):
+    files = KERNEL_SOURCES.get(f"{kernel}@{workload}", KERNEL_SOURCES[kernel])
+    if not rec or rec.get("sources") != _sources_digest(files):
         return None
     return rec.get("bytes_per_launch")
 
