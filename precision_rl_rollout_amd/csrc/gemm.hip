@@ -375,6 +375,10 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
 #undef PRR_SKINNY
     return hipGetLastError();
   }
+  {
+    hipError_t err = hipSuccess;
+    if (launch_gemm_prefill<kInt8>(A, sa, W, sw, M, N, K, C, stream, &err)) return err;
+  }
   const int64_t ntn = (N + 127) / 128, ntm = (M + 127) / 128;
   hipLaunchKernelGGL((gemm_tile_kernel<kInt8>), dim3((unsigned)(ntn * ntm)), dim3(256), 0, stream,
                      A, sa, W, sw, M, N, K, C, (int)ntn);

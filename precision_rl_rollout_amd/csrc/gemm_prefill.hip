@@ -1,0 +1,311 @@
+// W8A8 GEMM for many tokens (prefill / log-prob forward): compute-bound, on
+// the gfx950 FP8 (or INT8) matrix cores.
+//
+// A workgroup of 8 waves owns a 256 (m) x 256 (n) output tile.  Per 128-deep
+// K block it stages the activation and weight tiles (32 KB each) and the 256
+// activation scales of that block in LDS, written there directly by buffer
+// loads (no trip through registers), in a two-stage ring: the loads for K
+// block kb + 1 are in flight while the waves multiply block kb.  Each wave
+// owns a 64 (m) x 128 (n) sub-tile, 4 x 8 MFMA tiles of 16 x 16, so its n
+// range is one 128-wide weight block and its per-block scale is one scalar.
+//
+// Block-scaled FP8 (FP8-RL: blockwise W8A8): each 16 x 16 x 128 MFMA covers
+// exactly one K block, so it starts from zero and its fp32 result is scaled
+// by sa[m, kb] * sw[n / 128, kb] and added to the fp32 accumulator.
+// INT8 per channel (FlashRL: INT8 rollout): the int32 accumulator runs over
+// the whole K and the two scales are applied once at the end.
+//
+// LDS rows are 128 bytes; 16-byte chunk c of row r is stored at chunk
+// c ^ ((r >> 1) & 7): the 16 rows one fragment read touches then fall on 16
+// distinct 16-byte bank groups.
+#include "launch.h"
+#include "mfma.h"
+
+namespace prr {
+namespace {
+
+constexpr int kTileM = 256, kTileN = 256;
+constexpr int kWaves = 8;
+constexpr int kTileBytes = kTileM * kBlock;   // one operand tile per K block: 32 KB
+
+// Scales of one K block (FP8): 64 floats per wave slot.  Slots 0..3 hold
+// the activation scales of the tile's 256 rows, slot 4 the weight scales of
+// its two 128-wide n blocks ([0], [1]); slots 5..7 are filled with zeros.
+struct Stage {
+  uint8_t a[kTileBytes];
+  uint8_t w[kTileBytes];
+  float scales[kWaves][64];
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+
+// Buffer descriptor as four scalar words (raw buffer, no stride, dword data
+// format): base, num_records = bytes (clamped to 2^31 - 1).
+__device__ __forceinline__ v4i sgpr_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  r[1] = (int)(__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xFFFFu);
+  r[2] = __builtin_amdgcn_readfirstlane((int)(bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Direct-to-LDS buffer loads: lane l's 16 (4) bytes land at LDS byte address
+// lds + 16 l (4 l); offsets at or past num_records read zeros.  Issued as
+// inline assembly so that the compiler adds no wait of its own on them
+// before LDS reads (its tracking cannot tell the two stages apart and would
+// wait for the next stage's loads before reading the current one); the
+// kernel waits for them itself (vmcnt(0)) before the barrier that hands a
+// stage to the other waves.
+__device__ __forceinline__ void dma_b128(v4i rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (no wait on them).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+__device__ __forceinline__ int swz(int r, int c) { return r * kBlock + ((c ^ ((r >> 1) & 7)) << 4); }
+
+// Per-lane byte offsets of the tile loads.  Wave w loads rows
+// [32 w, 32 w + 32) of both tiles as 4 slabs of 8 rows (1 KB each; lane l
+// fills bytes [16 l, 16 l + 16) of a slab); the chunk a lane fetches depends
+// on the slab's parity through the swizzle, hence two offsets.  Rows past
+// the buffer range (M or N) read zeros.
+struct DmaOffsets {
+  int even, odd;   // offset of row 32 w + l / 8 (+ 8 for odd) at K block 0
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets(int K, int wave, int lane) {
+  const int r0 = wave * 32 + (lane >> 3), r1 = r0 + 8;
+  return DmaOffsets{r0 * K + (((lane & 7) ^ ((r0 >> 1) & 7)) << 4),
+                    r1 * K + (((lane & 7) ^ ((r1 >> 1) & 7)) << 4)};
+}
+
+// DMA of K block kb into a stage: both tiles, and (FP8) the activation
+// scales (waves 0..3, 64 rows each) and the two weight-block scales (wave 4).
+template <bool kInt8>
+__device__ __forceinline__ void stage_load(Stage& st, v4i ra, v4i rw, v4i rsa, v4i rsw,
+                                           DmaOffsets d, int K, int KB, int kb, int wave,
+                                           int lane) {
+  const int soff = kb * kBlock;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = wave * 4 + q;
+    const int v = ((q & 1) ? d.odd : d.even) + (q >> 1) * 16 * K;
+    dma_b128(ra, lds_addr(st.a + t * 1024), v, soff);
+    dma_b128(rw, lds_addr(st.w + t * 1024), v, soff);
+  }
+  if constexpr (!kInt8) {
+    // Branch-free (a branch here makes the register allocator shuffle the
+    // accumulators around the join): every wave fills its own slot.
+    const int row = wave < 4 ? wave * 64 + lane : lane;
+    const bool valid = wave < 4 || (wave == 4 && lane < 2);
+    const int vs = valid ? (row * KB + kb) * 4 : kOutOfRange;
+    dma_b32(wave < 4 ? rsa : rsw, lds_addr(st.scales[wave]), vs);
+  }
+}
+
+// Fragment rows always start at a multiple of 16, so the swizzle of row
+// base + (lane % 16) depends on the lane only: each lane keeps the byte
+// offsets of its two chunks (g and g + 4) within a 16-row group.
+struct FragOffsets {
+  int lo, hi;
+};
+
+__device__ __forceinline__ FragOffsets frag_offsets(int lane) {
+  const int r16 = lane & 15, g = lane >> 4;
+  return FragOffsets{swz(r16, g), swz(r16, g + 4)};
+}
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row0, FragOffsets o) {
+  const uint8_t* p = base + row0 * kBlock;
+  const uint4 lo = *reinterpret_cast<const uint4*>(p + o.lo);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + o.hi);
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+template <bool kInt8>
+struct Acc;
+template <>
+struct Acc<false> {
+  v4f v[8][4];
+};
+template <>
+struct Acc<true> {
+  v4i v[8][4];
+};
+
+// One K block from one stage: 8 weight fragments x 4 activation fragments.
+// Each weight fragment is one scheduling region (the next one's LDS read is
+// issued ahead of the current one's MFMAs); without the fences the compiler
+// hoists every read to the top and runs out of registers.
+template <bool kInt8>
+__device__ __forceinline__ void stage_compute(const Stage& st, Acc<kInt8>& acc, int wm, int wn,
+                                              int lane, FragOffsets o) {
+  v8i af[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) af[i] = lds_frag(st.a, wm * 64 + i * 16, o);
+  float s[4];
+  if constexpr (!kInt8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = st.scales[wm][i * 16 + (lane & 15)] * st.scales[4][wn];
+  }
+  v8i wf = lds_frag(st.w, wn * 128, o);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v8i wn_next = wf;
+    if (j < 7) wn_next = lds_frag(st.w, wn * 128 + (j + 1) * 16, o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (kInt8) {
+        acc.v[j][i] = mfma_i8x2(wf, af[i], acc.v[j][i]);
+      } else {
+        const v4f p = mfma_fp8(wf, af[i]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc.v[j][i][r] = fmaf(p[r], s[i], acc.v[j][i][r]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wf = wn_next;
+  }
+}
+
+// Workgroup b -> output tile.  Consecutive workgroups go to the 8 XCDs in
+// turn; the remap hands each XCD a contiguous run of logical tiles, and the
+// logical order walks groups of 8 m tiles n-tile by n-tile, so the 32
+// workgroups an XCD runs at once share 8 activation and 4 weight tiles
+// through its L2.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int T8 = T / 8 * 8;
+  const int L = b < T8 ? (b % 8) * (T8 / 8) + b / 8 : b;
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int group = L / per_group;
+  const int first_m = group * GM;
+  const int gsize = min(GM, tiles_m - first_m);
+  const int in_group = L - group * per_group;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+template <bool kInt8>
+__global__ __launch_bounds__(512) void gemm_prefill_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int tiles_m,
+    int tiles_n) {
+  // Two stages as two objects, so the compiler can tell that the fragment
+  // reads of one stage do not wait for the loads into the other.
+  __shared__ __align__(16) Stage st0;
+  __shared__ __align__(16) Stage st1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * kTileM, n0 = tn * kTileN;
+  const int KB = K / kBlock;
+  const int rows_a = min(M - m0, kTileM), rows_w = min(N - n0, kTileN);
+
+  // Every buffer range ends at the tile's last valid row, so rows past M or
+  // N (offsets at or beyond it) read zeros.
+  const v4i ra = sgpr_rsrc(A + (int64_t)m0 * K, (int64_t)rows_a * K);
+  const v4i rw = sgpr_rsrc(W + (int64_t)n0 * K, (int64_t)rows_w * K);
+  const v4i rsa = sgpr_rsrc(sa + (int64_t)m0 * KB, (int64_t)rows_a * KB * (int64_t)sizeof(float));
+  const int nb0 = n0 / kBlock, NB = (N + kBlock - 1) / kBlock;
+  const v4i rsw =
+      sgpr_rsrc(sw + (int64_t)nb0 * KB, (int64_t)min(2, NB - nb0) * KB * (int64_t)sizeof(float));
+  const DmaOffsets dmo = dma_offsets(K, wave, lane);
+  const FragOffsets fo = frag_offsets(lane);
+  Acc<kInt8> acc;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc.v[j][i][r] = 0;
+
+  stage_load<kInt8>(st0, ra, rw, rsa, rsw, dmo, K, KB, 0, wave, lane);
+  // K blocks in pairs (stage 0, stage 1), then an odd last block; one exit
+  // keeps the accumulators in place across iterations.
+  int kb = 0;
+  for (; kb + 2 <= KB; kb += 2) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's loads into st0 have landed
+    lds_barrier();                             // everyone's have; st1 is no longer read
+    stage_load<kInt8>(st1, ra, rw, rsa, rsw, dmo, K, KB, kb + 1, wave, lane);
+    stage_compute<kInt8>(st0, acc, wm, wn, lane, fo);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    lds_barrier();
+    // After the last pair this reloads the last block (unused): no branch.
+    stage_load<kInt8>(st0, ra, rw, rsa, rsw, dmo, K, KB, min(kb + 2, KB - 1), wave, lane);
+    stage_compute<kInt8>(st1, acc, wm, wn, lane, fo);
+  }
+  if (kb < KB) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    lds_barrier();
+    stage_compute<kInt8>(st0, acc, wm, wn, lane, fo);
+  }
+
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + wm * 64 + i * 16 + r16;
+    const float sm = kInt8 ? ((m < M) ? sa[m] : 0.f) : 1.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t n = n0 + wn * 128 + j * 16 + 4 * g;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (kInt8)
+          v[r] = (float)acc.v[j][i][r] * (sm * ((n + r < N) ? sw[n + r] : 0.f));
+        else
+          v[r] = acc.v[j][i][r];
+      }
+      store4(C, M, N, m, n, v);
+    }
+  }
+}
+
+}  // namespace
+
+template <bool kInt8>
+bool launch_gemm_prefill(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
+                         int64_t M, int64_t N, int64_t K, uint16_t* C, hipStream_t stream,
+                         hipError_t* err) {
+  // Buffer offsets inside one 256-row tile are 32-bit; dims fit int.
+  if (M < 1 || N < 1 || K < kBlock || (int64_t)kTileM * K >= kOutOfRange) return false;
+  if (M > 0x7FFFFFFF || N > 0x7FFFFFFF) return false;
+  const int64_t tiles_m = (M + kTileM - 1) / kTileM, tiles_n = (N + kTileN - 1) / kTileN;
+  if (tiles_m * tiles_n > 0x7FFFFFFF) return false;
+  hipLaunchKernelGGL((gemm_prefill_kernel<kInt8>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(kWaves * 64), 0, stream, A, sa, W, sw, (int)M, (int)N, (int)K, C,
+                     (int)tiles_m, (int)tiles_n);
+  *err = hipGetLastError();
+  return true;
+}
+
+template bool launch_gemm_prefill<false>(const uint8_t*, const float*, const uint8_t*,
+                                         const float*, int64_t, int64_t, int64_t, uint16_t*,
+                                         hipStream_t, hipError_t*);
+template bool launch_gemm_prefill<true>(const uint8_t*, const float*, const uint8_t*,
+                                        const float*, int64_t, int64_t, int64_t, uint16_t*,
+                                        hipStream_t, hipError_t*);
+
+}  // namespace prr

@@ -29,4 +29,11 @@ bool launch_gemm_decode(const uint8_t* A, const float* sa, const uint8_t* W, con
                         int64_t M, int64_t N, int64_t K, uint16_t* C, hipStream_t stream,
                         hipError_t* err);
 
+// Many-token W8A8 GEMM (256 x 256 tiles, LDS ring fed by direct-to-LDS
+// loads).  Returns false, launching nothing, outside the shapes it handles.
+template <bool kInt8>
+bool launch_gemm_prefill(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
+                         int64_t M, int64_t N, int64_t K, uint16_t* C, hipStream_t stream,
+                         hipError_t* err);
+
 }  // namespace prr
