@@ -97,25 +97,32 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int K, int wave, int lane) {
                     r1 * K + (((lane & 7) ^ ((r1 >> 1) & 7)) << 4)};
 }
 
+// Buffer-load instructions one wave issues per stage.
+template <bool kInt8>
+constexpr int kDmaPerStage = kInt8 ? 8 : 9;
+
 // DMA of K block kb into a stage: both tiles, and (FP8) the activation
 // scales (waves 0..3, 64 rows each) and the two weight-block scales (wave 4).
+// A block at or past KB loads nothing (every offset out of range, no memory
+// traffic) but still issues the same instructions, so the wait counts stay
+// the same.  Branch-free: a branch here makes the register allocator
+// shuffle the accumulators around the join.
 template <bool kInt8>
 __device__ __forceinline__ void stage_load(Stage& st, v4i ra, v4i rw, v4i rsa, v4i rsw,
                                            DmaOffsets d, int K, int KB, int kb, int wave,
                                            int lane) {
-  const int soff = kb * kBlock;
+  const bool live = kb < KB;
+  const int soff = live ? kb * kBlock : 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int t = wave * 4 + q;
-    const int v = ((q & 1) ? d.odd : d.even) + (q >> 1) * 16 * K;
+    const int v = live ? ((q & 1) ? d.odd : d.even) + (q >> 1) * 16 * K : kOutOfRange;
     dma_b128(ra, lds_addr(st.a + t * 1024), v, soff);
     dma_b128(rw, lds_addr(st.w + t * 1024), v, soff);
   }
   if constexpr (!kInt8) {
-    // Branch-free (a branch here makes the register allocator shuffle the
-    // accumulators around the join): every wave fills its own slot.
     const int row = wave < 4 ? wave * 64 + lane : lane;
-    const bool valid = wave < 4 || (wave == 4 && lane < 2);
+    const bool valid = live && (wave < 4 || (wave == 4 && lane < 2));
     const int vs = valid ? (row * KB + kb) * 4 : kOutOfRange;
     dma_b32(wave < 4 ? rsa : rsw, lds_addr(st.scales[wave]), vs);
   }
@@ -151,40 +158,103 @@ struct Acc<true> {
   v4i v[8][4];
 };
 
-// One K block from one stage: 8 weight fragments x 4 activation fragments.
-// Each weight fragment is one scheduling region (the next one's LDS read is
-// issued ahead of the current one's MFMAs); without the fences the compiler
-// hoists every read to the top and runs out of registers.
-template <bool kInt8>
-__device__ __forceinline__ void stage_compute(const Stage& st, Acc<kInt8>& acc, int wm, int wn,
-                                              int lane, FragOffsets o) {
+// Operand fragments a wave holds when it starts a K block: its 4 activation
+// fragments, their per-row scales times the weight-block scale (FP8), and
+// its first two weight fragments.
+struct Front {
   v8i af[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) af[i] = lds_frag(st.a, wm * 64 + i * 16, o);
   float s[4];
+  v8i wf, wf1;
+};
+
+template <bool kInt8>
+__device__ __forceinline__ void load_front(const Stage& st, Front& f, int wm, int wn, int lane,
+                                           FragOffsets o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.af[i] = lds_frag(st.a, wm * 64 + i * 16, o);
   if constexpr (!kInt8) {
+    const float swv = st.scales[4][wn];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = st.scales[wm][i * 16 + (lane & 15)] * st.scales[4][wn];
+    for (int i = 0; i < 4; ++i) f.s[i] = st.scales[wm][i * 16 + (lane & 15)] * swv;
   }
-  v8i wf = lds_frag(st.w, wn * 128, o);
+  f.wf = lds_frag(st.w, wn * 128, o);
+  f.wf1 = lds_frag(st.w, wn * 128 + 16, o);
+}
+
+// FP8 partial products of the previous region, still to be scaled into the
+// accumulator, and the scales they take.
+struct Pending {
+  v4f p[4];
+  float s[4];
+};
+
+// Region j: 4 MFMAs of weight fragment j against the 4 activation
+// fragments.  FP8: each MFMA's product is scaled into the accumulator one
+// region later (the FMAs of region j - 1 run here, in the shadow of these
+// MFMAs, on results that are complete by now, so they never stall on the
+// matrix pipeline); region 0 takes over the last region of the previous
+// block.  INT8 accumulates in the MFMA itself.
+template <bool kInt8>
+__device__ __forceinline__ void mma_region(Acc<kInt8>& acc, int j, const v8i& wf, const Front& f,
+                                           Pending& pend) {
+  if constexpr (kInt8) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    v8i wn_next = wf;
-    if (j < 7) wn_next = lds_frag(st.w, wn * 128 + (j + 1) * 16, o);
+    for (int i = 0; i < 4; ++i) acc.v[j][i] = mfma_i8x2(wf, f.af[i], acc.v[j][i]);
+  } else {
+    const int jp = (j + 7) & 7;
+    v4f p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if constexpr (kInt8) {
-        acc.v[j][i] = mfma_i8x2(wf, af[i], acc.v[j][i]);
-      } else {
-        const v4f p = mfma_fp8(wf, af[i]);
+      p[i] = mfma_fp8(wf, f.af[i]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc.v[j][i][r] = fmaf(p[r], s[i], acc.v[j][i][r]);
-      }
+      for (int r = 0; r < 4; ++r) acc.v[jp][i][r] = fmaf(pend.p[i][r], pend.s[i], acc.v[jp][i][r]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    wf = wn_next;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pend.p[i] = p[i];
+      pend.s[i] = f.s[i];
+    }
   }
 }
+
+// One K block.  On entry `cur` holds block kb (landed and published), `f`
+// its front fragments (including the first two weight fragments), and block
+// kb + 1 is in flight into `nxt`.  Region j reads weight fragment j + 2 and
+// runs the 4 MFMAs of fragment j; each region is one scheduling region
+// (without the fences the compiler hoists every read and runs out of
+// registers).  Region 5 issues the last read of `cur`; after region 6 the
+// wave waits for its block kb + 1 loads, meets the others at the barrier
+// (after which nobody reads `cur`), starts block kb + 2 into `cur`, runs
+// region 7 and reads the front of block kb + 1 from `nxt`.  (Reading that
+// front during region 7 holds 32 more registers at the peak and measured
+// slower; a prefetch distance of one fragment measured slower too.)
+template <bool kInt8>
+__device__ __forceinline__ void k_block(Stage& cur, const Stage& nxt, Acc<kInt8>& acc, Front& f,
+                                        Pending& pend, v4i ra, v4i rw, v4i rsa, v4i rsw,
+                                        DmaOffsets d, int K, int KB, int kb, int wave, int wm,
+                                        int wn, int lane, FragOffsets o) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v8i w2 = f.wf1;
+    if (j + 2 < 8) w2 = lds_frag(cur.w, wn * 128 + (j + 2) * 16, o);
+    mma_region<kInt8>(acc, j, f.wf, f, pend);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j == 6) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's loads of block kb + 1 landed
+      lds_barrier();                             // everyone's have; nobody reads `cur` any more
+      stage_load<kInt8>(cur, ra, rw, rsa, rsw, d, K, KB, kb + 2, wave, lane);
+    }
+    f.wf = f.wf1;
+    f.wf1 = w2;
+  }
+  load_front<kInt8>(nxt, f, wm, wn, lane, o);
+}
+
+// Epilogue staging: the bf16 output tile, rows 0..127 in stage 0 and
+// 128..255 in stage 1, 512 bytes per row; 16-byte chunk q of row r sits at
+// chunk q ^ (r % 16), so the 16 rows one store instruction touches, and the
+// 32 chunks one row read touches, fall on distinct banks.
+__device__ __forceinline__ int c_swz(int r, int q) { return r * 512 + ((q ^ (r & 15)) << 4); }
 
 // Workgroup b -> output tile.  Consecutive workgroups go to the 8 XCDs in
 // turn; the remap hands each XCD a contiguous run of logical tiles, and the
@@ -242,43 +312,85 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
       for (int r = 0; r < 4; ++r) acc.v[j][i][r] = 0;
 
   stage_load<kInt8>(st0, ra, rw, rsa, rsw, dmo, K, KB, 0, wave, lane);
+  stage_load<kInt8>(st1, ra, rw, rsa, rsw, dmo, K, KB, 1, wave, lane);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | kDmaPerStage<kInt8>);   // block 0 landed
+  lds_barrier();
+  Front f;
+  load_front<kInt8>(st0, f, wm, wn, lane, fo);
+  Pending pend;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pend.p[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    pend.s[i] = 0.f;
+  }
   // K blocks in pairs (stage 0, stage 1), then an odd last block; one exit
   // keeps the accumulators in place across iterations.
   int kb = 0;
   for (; kb + 2 <= KB; kb += 2) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's loads into st0 have landed
-    lds_barrier();                             // everyone's have; st1 is no longer read
-    stage_load<kInt8>(st1, ra, rw, rsa, rsw, dmo, K, KB, kb + 1, wave, lane);
-    stage_compute<kInt8>(st0, acc, wm, wn, lane, fo);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    lds_barrier();
-    // After the last pair this reloads the last block (unused): no branch.
-    stage_load<kInt8>(st0, ra, rw, rsa, rsw, dmo, K, KB, min(kb + 2, KB - 1), wave, lane);
-    stage_compute<kInt8>(st1, acc, wm, wn, lane, fo);
+    k_block<kInt8>(st0, st1, acc, f, pend, ra, rw, rsa, rsw, dmo, K, KB, kb, wave, wm, wn, lane, fo);
+    k_block<kInt8>(st1, st0, acc, f, pend, ra, rw, rsa, rsw, dmo, K, KB, kb + 1, wave, wm, wn, lane, fo);
   }
-  if (kb < KB) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    lds_barrier();
-    stage_compute<kInt8>(st0, acc, wm, wn, lane, fo);
+  if (kb < KB)
+    k_block<kInt8>(st0, st1, acc, f, pend, ra, rw, rsa, rsw, dmo, K, KB, kb, wave, wm, wn, lane, fo);
+  if constexpr (!kInt8) {   // the last region's products
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc.v[7][i][r] = fmaf(pend.p[i][r], pend.s[i], acc.v[7][i][r]);
   }
+  // Every load (the trailing ones are out of range) has landed and every
+  // wave is done with the stages before they hold the output tile.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  lds_barrier();
 
+  // Output tile -> bf16 in LDS -> 16-byte row-contiguous stores.
   const int r16 = lane & 15, g = lane >> 4;
+  uint8_t* const lds0 = reinterpret_cast<uint8_t*>(&st0);   // 64 KB of each stage's
+  uint8_t* const lds1 = reinterpret_cast<uint8_t*>(&st1);   // 66.5 KB hold 128 rows
+  uint8_t* half = wm < 2 ? lds0 : lds1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int rr = (wm & 1) * 64 + i * 16 + r16;   // row within the half
     const int64_t m = m0 + wm * 64 + i * 16 + r16;
     const float sm = kInt8 ? ((m < M) ? sa[m] : 0.f) : 1.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t n = n0 + wn * 128 + j * 16 + 4 * g;
+      const int nl = wn * 128 + j * 16 + 4 * g;    // column within the tile
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (kInt8)
-          v[r] = (float)acc.v[j][i][r] * (sm * ((n + r < N) ? sw[n + r] : 0.f));
-        else
+        if constexpr (kInt8) {
+          const int64_t n = n0 + nl + r;
+          v[r] = (float)acc.v[j][i][r] * (sm * ((n < N) ? sw[n] : 0.f));
+        } else {
           v[r] = acc.v[j][i][r];
+        }
       }
-      store4(C, M, N, m, n, v);
+      const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+      const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+      *reinterpret_cast<uint2*>(half + c_swz(rr, nl >> 3) + ((nl & 4) << 1)) = make_uint2(lo, hi);
+    }
+  }
+  lds_barrier();
+  const bool vec = (N & 7) == 0;   // rows start 16-byte aligned
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int c = it * 512 + tid;
+    const int row = c >> 5, q = c & 31;
+    const int64_t m = m0 + row;
+    const int64_t n = n0 + q * 8;
+    if (m >= M || n >= N) continue;
+    const uint8_t* src = (row < 128 ? lds0 : lds1) + c_swz(row & 127, q);
+    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    uint16_t* dst = C + m * N + n;
+    if (vec && n + 8 <= N) {
+      // Streaming store: the output is not read again here, and letting it
+      // allocate in L2 evicts the operand tiles other workgroups still read.
+      __builtin_nontemporal_store(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w},
+                                  reinterpret_cast<v4i*>(dst));
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
   }
 }
