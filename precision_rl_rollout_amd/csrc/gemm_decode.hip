@@ -27,6 +27,8 @@
 // FP8: per K block, C += sa[m, kb] * sw[n / 128, kb] * MFMA(Wq, Aq) (one
 // v_mfma_f32_16x16x128_f8f6f4 per block, zero accumulator).  INT8: the
 // int32 MFMA accumulates the wave's whole piece; scales in the epilogue.
+#include <atomic>
+
 #include "launch.h"
 #include "mfma.h"
 #include "prr_device.h"
@@ -246,15 +248,18 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
 }
 
 // Compute units of the current device (cached per device ordinal).
-static int compute_units() {
-  static int cache[64];
+int compute_units() {
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int v = 0;
   if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
     v = 256;
-  if (dev < 64) cache[dev] = v;
+  if (dev < 64) cache[dev].store(v, std::memory_order_relaxed);
   return v;
 }
 

@@ -1,13 +1,14 @@
 // W8A8 GEMM for many tokens (prefill / log-prob forward): compute-bound, on
 // the gfx950 FP8 (or INT8) matrix cores.
 //
-// A workgroup of 8 waves owns a 256 (m) x 256 (n) output tile.  Per 128-deep
-// K block it stages the activation and weight tiles (32 KB each) and the 256
-// activation scales of that block in LDS, written there directly by buffer
-// loads (no trip through registers), in a two-stage ring: the loads for K
-// block kb + 1 are in flight while the waves multiply block kb.  Each wave
-// owns a 64 (m) x 128 (n) sub-tile, 4 x 8 MFMA tiles of 16 x 16, so its n
-// range is one 128-wide weight block and its per-block scale is one scalar.
+// A workgroup of 8 waves owns a 256 (m) x TN (n) output tile, TN = 256 or
+// 128.  Per 128-deep K block it stages the activation and weight tiles and
+// the activation scales of that block in LDS, written there directly by
+// buffer loads (no trip through registers), in a two-stage ring: the loads
+// for K block kb + 1 are in flight while the waves multiply block kb.  Each
+// wave owns a 64 (m) x TN/2 (n) sub-tile, 4 x TN/32 MFMA tiles of 16 x 16,
+// whose n range lies in one 128-wide weight block, so its per-block weight
+// scale is one scalar.
 //
 // Block-scaled FP8 (FP8-RL: blockwise W8A8): each 16 x 16 x 128 MFMA covers
 // exactly one K block, so it starts from zero and its fp32 result is scaled
@@ -24,16 +25,16 @@
 namespace prr {
 namespace {
 
-constexpr int kTileM = 256, kTileN = 256;
+constexpr int kTileM = 256;
 constexpr int kWaves = 8;
-constexpr int kTileBytes = kTileM * kBlock;   // one operand tile per K block: 32 KB
 
 // Scales of one K block (FP8): 64 floats per wave slot.  Slots 0..3 hold
 // the activation scales of the tile's 256 rows, slot 4 the weight scales of
-// its two 128-wide n blocks ([0], [1]); slots 5..7 are filled with zeros.
+// its TN / 128 n blocks; slots 5..7 are filled with zeros.
+template <int TN>
 struct Stage {
-  uint8_t a[kTileBytes];
-  uint8_t w[kTileBytes];
+  uint8_t a[kTileM * kBlock];   // 32 KB
+  uint8_t w[TN * kBlock];       // 32 KB or 16 KB
   float scales[kWaves][64];
 };
 
@@ -76,53 +77,61 @@ __device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t lds, int voff) {
                : "memory", "m0");
 }
 
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
 // maxima (no wait on them).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kBlock + ((c ^ ((r >> 1) & 7)) << 4); }
 
-// Per-lane byte offsets of the tile loads.  Wave w loads rows
-// [32 w, 32 w + 32) of both tiles as 4 slabs of 8 rows (1 KB each; lane l
-// fills bytes [16 l, 16 l + 16) of a slab); the chunk a lane fetches depends
-// on the slab's parity through the swizzle, hence two offsets.  Rows past
-// the buffer range (M or N) read zeros.
+// Per-lane byte offsets of the tile loads.  A tile of R rows is loaded as
+// R / 8 slabs of 8 rows (1 KB each; lane l fills bytes [16 l, 16 l + 16) of
+// a slab), R / 64 consecutive slabs per wave; the chunk a lane fetches
+// depends on the slab's parity through the swizzle, hence two offsets.
+// Rows past the buffer range (M or N) read zeros.
 struct DmaOffsets {
-  int even, odd;   // offset of row 32 w + l / 8 (+ 8 for odd) at K block 0
+  int even, odd;   // offsets of the wave's first two slab rows at K block 0
 };
 
-__device__ __forceinline__ DmaOffsets dma_offsets(int K, int wave, int lane) {
-  const int r0 = wave * 32 + (lane >> 3), r1 = r0 + 8;
+__device__ __forceinline__ DmaOffsets dma_offsets(int K, int first_row, int lane) {
+  const int r0 = first_row + (lane >> 3), r1 = r0 + 8;
   return DmaOffsets{r0 * K + (((lane & 7) ^ ((r0 >> 1) & 7)) << 4),
                     r1 * K + (((lane & 7) ^ ((r1 >> 1) & 7)) << 4)};
 }
 
-// Buffer-load instructions one wave issues per stage.
-template <bool kInt8>
-constexpr int kDmaPerStage = kInt8 ? 8 : 9;
+// Buffer-load instructions one wave issues per stage: 4 activation slabs,
+// TN / 64 weight slabs, one scale load (FP8).
+template <bool kInt8, int TN>
+constexpr int kDmaPerStage = 4 + TN / 64 + (kInt8 ? 0 : 1);
 
 // DMA of K block kb into a stage: both tiles, and (FP8) the activation
-// scales (waves 0..3, 64 rows each) and the two weight-block scales (wave 4).
+// scales (waves 0..3, 64 rows each) and the weight-block scales (wave 4).
 // A block at or past KB loads nothing (every offset out of range, no memory
 // traffic) but still issues the same instructions, so the wait counts stay
 // the same.  Branch-free: a branch here makes the register allocator
 // shuffle the accumulators around the join.
-template <bool kInt8>
-__device__ __forceinline__ void stage_load(Stage& st, v4i ra, v4i rw, v4i rsa, v4i rsw,
-                                           DmaOffsets d, int K, int KB, int kb, int wave,
-                                           int lane) {
+template <bool kInt8, int TN>
+__device__ __forceinline__ void stage_load(Stage<TN>& st, v4i ra, v4i rw, v4i rsa, v4i rsw,
+                                           DmaOffsets da, DmaOffsets dw, int K, int KB, int kb,
+                                           int wave, int lane) {
   const bool live = kb < KB;
   const int soff = live ? kb * kBlock : 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int t = wave * 4 + q;
-    const int v = live ? ((q & 1) ? d.odd : d.even) + (q >> 1) * 16 * K : kOutOfRange;
-    dma_b128(ra, lds_addr(st.a + t * 1024), v, soff);
-    dma_b128(rw, lds_addr(st.w + t * 1024), v, soff);
+    const int v = live ? ((q & 1) ? da.odd : da.even) + (q >> 1) * 16 * K : kOutOfRange;
+    dma_b128(ra, lds_addr(st.a + (wave * 4 + q) * 1024), v, soff);
+  }
+  constexpr int kWs = TN / 64;   // weight slabs per wave
+#pragma unroll
+  for (int q = 0; q < kWs; ++q) {
+    const int v = live ? ((q & 1) ? dw.odd : dw.even) + (q >> 1) * 16 * K : kOutOfRange;
+    dma_b128(rw, lds_addr(st.w + (wave * kWs + q) * 1024), v, soff);
   }
   if constexpr (!kInt8) {
     const int row = wave < 4 ? wave * 64 + lane : lane;
-    const bool valid = live && (wave < 4 || (wave == 4 && lane < 2));
+    const bool valid = live && (wave < 4 || (wave == 4 && lane < TN / kBlock));
     const int vs = valid ? (row * KB + kb) * 4 : kOutOfRange;
     dma_b32(wave < 4 ? rsa : rsw, lds_addr(st.scales[wave]), vs);
   }
@@ -147,15 +156,16 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row0, FragOffse
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <bool kInt8>
+// Accumulators: [weight fragment j][activation fragment i].
+template <bool kInt8, int NJ>
 struct Acc;
-template <>
-struct Acc<false> {
-  v4f v[8][4];
+template <int NJ>
+struct Acc<false, NJ> {
+  v4f v[NJ][4];
 };
-template <>
-struct Acc<true> {
-  v4i v[8][4];
+template <int NJ>
+struct Acc<true, NJ> {
+  v4i v[NJ][4];
 };
 
 // Operand fragments a wave holds when it starts a K block: its 4 activation
@@ -167,18 +177,19 @@ struct Front {
   v8i wf, wf1;
 };
 
-template <bool kInt8>
-__device__ __forceinline__ void load_front(const Stage& st, Front& f, int wm, int wn, int lane,
+template <bool kInt8, int TN>
+__device__ __forceinline__ void load_front(const Stage<TN>& st, Front& f, int wm, int wn, int lane,
                                            FragOffsets o) {
+  constexpr int kWaveN = TN / 2;
 #pragma unroll
   for (int i = 0; i < 4; ++i) f.af[i] = lds_frag(st.a, wm * 64 + i * 16, o);
   if constexpr (!kInt8) {
-    const float swv = st.scales[4][wn];
+    const float swv = st.scales[4][wn * kWaveN / kBlock];
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.s[i] = st.scales[wm][i * 16 + (lane & 15)] * swv;
   }
-  f.wf = lds_frag(st.w, wn * 128, o);
-  f.wf1 = lds_frag(st.w, wn * 128 + 16, o);
+  f.wf = lds_frag(st.w, wn * kWaveN, o);
+  f.wf1 = lds_frag(st.w, wn * kWaveN + 16, o);
 }
 
 // FP8 partial products of the previous region, still to be scaled into the
@@ -194,14 +205,14 @@ struct Pending {
 // MFMAs, on results that are complete by now, so they never stall on the
 // matrix pipeline); region 0 takes over the last region of the previous
 // block.  INT8 accumulates in the MFMA itself.
-template <bool kInt8>
-__device__ __forceinline__ void mma_region(Acc<kInt8>& acc, int j, const v8i& wf, const Front& f,
-                                           Pending& pend) {
+template <bool kInt8, int NJ>
+__device__ __forceinline__ void mma_region(Acc<kInt8, NJ>& acc, int j, const v8i& wf,
+                                           const Front& f, Pending& pend) {
   if constexpr (kInt8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc.v[j][i] = mfma_i8x2(wf, f.af[i], acc.v[j][i]);
   } else {
-    const int jp = (j + 7) & 7;
+    const int jp = (j + NJ - 1) % NJ;
     v4f p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -222,39 +233,56 @@ __device__ __forceinline__ void mma_region(Acc<kInt8>& acc, int j, const v8i& wf
 // kb + 1 is in flight into `nxt`.  Region j reads weight fragment j + 2 and
 // runs the 4 MFMAs of fragment j; each region is one scheduling region
 // (without the fences the compiler hoists every read and runs out of
-// registers).  Region 5 issues the last read of `cur`; after region 6 the
-// wave waits for its block kb + 1 loads, meets the others at the barrier
-// (after which nobody reads `cur`), starts block kb + 2 into `cur`, runs
-// region 7 and reads the front of block kb + 1 from `nxt`.  (Reading that
-// front during region 7 holds 32 more registers at the peak and measured
-// slower; a prefetch distance of one fragment measured slower too.)
-template <bool kInt8>
-__device__ __forceinline__ void k_block(Stage& cur, const Stage& nxt, Acc<kInt8>& acc, Front& f,
-                                        Pending& pend, v4i ra, v4i rw, v4i rsa, v4i rsw,
-                                        DmaOffsets d, int K, int KB, int kb, int wave, int wm,
-                                        int wn, int lane, FragOffsets o) {
+// registers).  Region NJ - 3 issues the last read of `cur`; after region
+// NJ - 2 the wave waits for its block kb + 1 loads, meets the others at the
+// barrier (after which nobody reads `cur`), starts block kb + 2 into `cur`,
+// runs the last region and reads the front of block kb + 1 from `nxt`.
+// (Reading that front during the last region holds 32 more registers at the
+// peak and measured slower; a prefetch distance of one fragment measured
+// slower too.)
+template <bool kInt8, int TN>
+__device__ __forceinline__ void k_block(Stage<TN>& cur, const Stage<TN>& nxt,
+                                        Acc<kInt8, TN / 32>& acc, Front& f, Pending& pend, v4i ra,
+                                        v4i rw, v4i rsa, v4i rsw, DmaOffsets da, DmaOffsets dw,
+                                        int K, int KB, int kb, int wave, int wm, int wn, int lane,
+                                        FragOffsets o) {
+  constexpr int NJ = TN / 32, kWaveN = TN / 2;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     v8i w2 = f.wf1;
-    if (j + 2 < 8) w2 = lds_frag(cur.w, wn * 128 + (j + 2) * 16, o);
-    mma_region<kInt8>(acc, j, f.wf, f, pend);
+    if (j + 2 < NJ) w2 = lds_frag(cur.w, wn * kWaveN + (j + 2) * 16, o);
+    mma_region<kInt8, NJ>(acc, j, f.wf, f, pend);
+    if constexpr (!kInt8) {
+      // Issue order: each MFMA followed by 4 of the previous region's scale
+      // FMAs (they run while it does), the two LDS reads early.
+      if (j + 2 < NJ) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+      if (j + 2 < NJ) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if (j == 6) {
+    if (j == NJ - 2) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's loads of block kb + 1 landed
       lds_barrier();                             // everyone's have; nobody reads `cur` any more
-      stage_load<kInt8>(cur, ra, rw, rsa, rsw, d, K, KB, kb + 2, wave, lane);
+      stage_load<kInt8, TN>(cur, ra, rw, rsa, rsw, da, dw, K, KB, kb + 2, wave, lane);
     }
     f.wf = f.wf1;
     f.wf1 = w2;
   }
-  load_front<kInt8>(nxt, f, wm, wn, lane, o);
+  load_front<kInt8, TN>(nxt, f, wm, wn, lane, o);
 }
 
 // Epilogue staging: the bf16 output tile, rows 0..127 in stage 0 and
-// 128..255 in stage 1, 512 bytes per row; 16-byte chunk q of row r sits at
+// 128..255 in stage 1, 2 TN bytes per row; 16-byte chunk q of row r sits at
 // chunk q ^ (r % 16), so the 16 rows one store instruction touches, and the
-// 32 chunks one row read touches, fall on distinct banks.
-__device__ __forceinline__ int c_swz(int r, int q) { return r * 512 + ((q ^ (r & 15)) << 4); }
+// chunks one row read touches, fall on distinct banks.
+template <int TN>
+__device__ __forceinline__ int c_swz(int r, int q) { return r * (2 * TN) + ((q ^ (r & 15)) << 4); }
 
 // Workgroup b -> output tile.  Consecutive workgroups go to the 8 XCDs in
 // turn; the remap hands each XCD a contiguous run of logical tiles, and the
@@ -275,23 +303,25 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
   tn = in_group / gsize;
 }
 
-template <bool kInt8>
+// Output columns [n_base, N) in tiles_m x tiles_n tiles of 256 x TN.
+template <bool kInt8, int TN>
 __global__ __launch_bounds__(512) void gemm_prefill_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
-    const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int tiles_m,
-    int tiles_n) {
+    const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int n_base,
+    int tiles_m, int tiles_n) {
+  constexpr int NJ = TN / 32, kWaveN = TN / 2;
   // Two stages as two objects, so the compiler can tell that the fragment
   // reads of one stage do not wait for the loads into the other.
-  __shared__ __align__(16) Stage st0;
-  __shared__ __align__(16) Stage st1;
+  __shared__ __align__(16) Stage<TN> st0;
+  __shared__ __align__(16) Stage<TN> st1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 3, wn = wave >> 2;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * kTileM, n0 = tn * kTileN;
+  const int m0 = tm * kTileM, n0 = n_base + tn * TN;
   const int KB = K / kBlock;
-  const int rows_a = min(M - m0, kTileM), rows_w = min(N - n0, kTileN);
+  const int rows_a = min(M - m0, kTileM), rows_w = min(N - n0, TN);
 
   // Every buffer range ends at the tile's last valid row, so rows past M or
   // N (offsets at or beyond it) read zeros.
@@ -299,24 +329,25 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
   const v4i rw = sgpr_rsrc(W + (int64_t)n0 * K, (int64_t)rows_w * K);
   const v4i rsa = sgpr_rsrc(sa + (int64_t)m0 * KB, (int64_t)rows_a * KB * (int64_t)sizeof(float));
   const int nb0 = n0 / kBlock, NB = (N + kBlock - 1) / kBlock;
-  const v4i rsw =
-      sgpr_rsrc(sw + (int64_t)nb0 * KB, (int64_t)min(2, NB - nb0) * KB * (int64_t)sizeof(float));
-  const DmaOffsets dmo = dma_offsets(K, wave, lane);
+  const v4i rsw = sgpr_rsrc(sw + (int64_t)nb0 * KB,
+                            (int64_t)min(TN / kBlock, NB - nb0) * KB * (int64_t)sizeof(float));
+  const DmaOffsets da = dma_offsets(K, wave * 32, lane);
+  const DmaOffsets dw = TN == kTileM ? da : dma_offsets(K, wave * (TN / 8), lane);
   const FragOffsets fo = frag_offsets(lane);
-  Acc<kInt8> acc;
+  Acc<kInt8, NJ> acc;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc.v[j][i][r] = 0;
 
-  stage_load<kInt8>(st0, ra, rw, rsa, rsw, dmo, K, KB, 0, wave, lane);
-  stage_load<kInt8>(st1, ra, rw, rsa, rsw, dmo, K, KB, 1, wave, lane);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | kDmaPerStage<kInt8>);   // block 0 landed
+  stage_load<kInt8, TN>(st0, ra, rw, rsa, rsw, da, dw, K, KB, 0, wave, lane);
+  stage_load<kInt8, TN>(st1, ra, rw, rsa, rsw, da, dw, K, KB, 1, wave, lane);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | kDmaPerStage<kInt8, TN>);   // block 0 landed
   lds_barrier();
   Front f;
-  load_front<kInt8>(st0, f, wm, wn, lane, fo);
+  load_front<kInt8, TN>(st0, f, wm, wn, lane, fo);
   Pending pend;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -327,16 +358,20 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
   // keeps the accumulators in place across iterations.
   int kb = 0;
   for (; kb + 2 <= KB; kb += 2) {
-    k_block<kInt8>(st0, st1, acc, f, pend, ra, rw, rsa, rsw, dmo, K, KB, kb, wave, wm, wn, lane, fo);
-    k_block<kInt8>(st1, st0, acc, f, pend, ra, rw, rsa, rsw, dmo, K, KB, kb + 1, wave, wm, wn, lane, fo);
+    k_block<kInt8, TN>(st0, st1, acc, f, pend, ra, rw, rsa, rsw, da, dw, K, KB, kb, wave, wm, wn,
+                       lane, fo);
+    k_block<kInt8, TN>(st1, st0, acc, f, pend, ra, rw, rsa, rsw, da, dw, K, KB, kb + 1, wave, wm,
+                       wn, lane, fo);
   }
   if (kb < KB)
-    k_block<kInt8>(st0, st1, acc, f, pend, ra, rw, rsa, rsw, dmo, K, KB, kb, wave, wm, wn, lane, fo);
+    k_block<kInt8, TN>(st0, st1, acc, f, pend, ra, rw, rsa, rsw, da, dw, K, KB, kb, wave, wm, wn,
+                       lane, fo);
   if constexpr (!kInt8) {   // the last region's products
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc.v[7][i][r] = fmaf(pend.p[i][r], pend.s[i], acc.v[7][i][r]);
+      for (int r = 0; r < 4; ++r)
+        acc.v[NJ - 1][i][r] = fmaf(pend.p[i][r], pend.s[i], acc.v[NJ - 1][i][r]);
   }
   // Every load (the trailing ones are out of range) has landed and every
   // wave is done with the stages before they hold the output tile.
@@ -345,8 +380,8 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
 
   // Output tile -> bf16 in LDS -> 16-byte row-contiguous stores.
   const int r16 = lane & 15, g = lane >> 4;
-  uint8_t* const lds0 = reinterpret_cast<uint8_t*>(&st0);   // 64 KB of each stage's
-  uint8_t* const lds1 = reinterpret_cast<uint8_t*>(&st1);   // 66.5 KB hold 128 rows
+  uint8_t* const lds0 = reinterpret_cast<uint8_t*>(&st0);   // 128 rows of 2 TN bytes
+  uint8_t* const lds1 = reinterpret_cast<uint8_t*>(&st1);   // fit in each stage
   uint8_t* half = wm < 2 ? lds0 : lds1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -354,8 +389,8 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
     const int64_t m = m0 + wm * 64 + i * 16 + r16;
     const float sm = kInt8 ? ((m < M) ? sa[m] : 0.f) : 1.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int nl = wn * 128 + j * 16 + 4 * g;    // column within the tile
+    for (int j = 0; j < NJ; ++j) {
+      const int nl = wn * kWaveN + j * 16 + 4 * g;   // column within the tile
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -368,19 +403,21 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
       }
       const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
       const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-      *reinterpret_cast<uint2*>(half + c_swz(rr, nl >> 3) + ((nl & 4) << 1)) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(half + c_swz<TN>(rr, nl >> 3) + ((nl & 4) << 1)) =
+          make_uint2(lo, hi);
     }
   }
   lds_barrier();
   const bool vec = (N & 7) == 0;   // rows start 16-byte aligned
+  constexpr int kChunks = TN / 8;   // 16-byte chunks per output row
 #pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
+  for (int it = 0; it < kTileM * kChunks / 512; ++it) {
     const int c = it * 512 + tid;
-    const int row = c >> 5, q = c & 31;
+    const int row = c / kChunks, q = c % kChunks;
     const int64_t m = m0 + row;
     const int64_t n = n0 + q * 8;
     if (m >= M || n >= N) continue;
-    const uint8_t* src = (row < 128 ? lds0 : lds1) + c_swz(row & 127, q);
+    const uint8_t* src = (row < 128 ? lds0 : lds1) + c_swz<TN>(row & 127, q);
     const uint4 v = *reinterpret_cast<const uint4*>(src);
     uint16_t* dst = C + m * N + n;
     if (vec && n + 8 <= N) {
@@ -397,6 +434,17 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
 
 }  // namespace
 
+// Output columns [n_base, n_end) in 256 x TN tiles.
+template <bool kInt8, int TN>
+static void launch_cols(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
+                        int64_t M, int64_t N, int64_t K, uint16_t* C, int64_t n_base,
+                        int64_t n_end, hipStream_t stream) {
+  const int64_t tiles_m = (M + kTileM - 1) / kTileM, tiles_n = (n_end - n_base + TN - 1) / TN;
+  hipLaunchKernelGGL((gemm_prefill_kernel<kInt8, TN>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(kWaves * 64), 0, stream, A, sa, W, sw, (int)M, (int)N, (int)K, C,
+                     (int)n_base, (int)tiles_m, (int)tiles_n);
+}
+
 template <bool kInt8>
 bool launch_gemm_prefill(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
                          int64_t M, int64_t N, int64_t K, uint16_t* C, hipStream_t stream,
@@ -404,11 +452,25 @@ bool launch_gemm_prefill(const uint8_t* A, const float* sa, const uint8_t* W, co
   // Buffer offsets inside one 256-row tile are 32-bit; dims fit int.
   if (M < 1 || N < 1 || K < kBlock || (int64_t)kTileM * K >= kOutOfRange) return false;
   if (M > 0x7FFFFFFF || N > 0x7FFFFFFF) return false;
-  const int64_t tiles_m = (M + kTileM - 1) / kTileM, tiles_n = (N + kTileN - 1) / kTileN;
-  if (tiles_m * tiles_n > 0x7FFFFFFF) return false;
-  hipLaunchKernelGGL((gemm_prefill_kernel<kInt8>), dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(kWaves * 64), 0, stream, A, sa, W, sw, (int)M, (int)N, (int)K, C,
-                     (int)tiles_m, (int)tiles_n);
+  const int64_t tiles_m = (M + kTileM - 1) / kTileM;
+  if (tiles_m * ((N + 127) / 128) > 0x7FFFFFFF) return false;
+  // 256-wide tiles, except that when they leave a last partial round of at
+  // most half the compute units busy, the trailing tile columns of that
+  // round run as twice as many 128-wide tiles in a second launch (whole
+  // rounds first, then one round of half-size tiles instead of a half-empty
+  // round of full ones).
+  const int64_t cus = compute_units();
+  const int64_t tn256 = (N + 255) / 256;
+  int64_t c = 0;
+  for (int64_t cc = 1; cc < tn256 && c == 0; ++cc)
+    if (((tn256 - cc) * tiles_m) % cus == 0 && 2 * cc * tiles_m <= cus) c = cc;
+  if (c == 0) {
+    launch_cols<kInt8, 256>(A, sa, W, sw, M, N, K, C, 0, N, stream);
+  } else {
+    const int64_t n_split = (tn256 - c) * 256;
+    launch_cols<kInt8, 256>(A, sa, W, sw, M, N, K, C, 0, n_split, stream);
+    launch_cols<kInt8, 128>(A, sa, W, sw, M, N, K, C, n_split, N, stream);
+  }
   *err = hipGetLastError();
   return true;
 }

@@ -22,6 +22,9 @@ hipError_t launch_w8a8_int8_channel_gemm(const int8_t* A, const float* sa, const
                                          const float* sw, int64_t M, int64_t N, int64_t K,
                                          uint16_t* C, hipStream_t stream);
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int compute_units();
+
 // Decode-sized W8A8 GEMM (activation-resident, persistent).  Returns false,
 // launching nothing, when the shape is outside what it handles.
 template <bool kInt8>

@@ -99,6 +99,15 @@ def test_int8_gemm_shapes(M, N, K):
         _check(_gpu_int8(p["A"], p["Wt"]), _ref_int8(p["A"], p["Wt"]), f"M{M} N{N} K{K} s{seed}")
 
 
+def test_prefill_split_launch():
+    # 32 x 9 tiles of 256 x 256 on 256 compute units: the first 8 tile
+    # columns fill whole rounds, the ragged last one runs as 128-wide tiles.
+    p = workloads.gemm_problem(8192, 2300, 256, outliers=True, seed=0)
+    announce("w8a8 GEMMs M8192 N2300 K256 (256- and 128-wide tiles)")
+    _check(_gpu_fp8(p["A"], p["Wt"]), _ref_fp8(p["A"], p["Wt"]), "split fp8")
+    _check(_gpu_int8(p["A"], p["Wt"]), _ref_int8(p["A"], p["Wt"]), "split int8")
+
+
 def test_gemm_k_zero_writes_zeros_and_empty_is_noop():
     announce("gemm K=0 / empty")
     for fn, dt in ((binding.w8a8_block_gemm, torch.uint8), (binding.w8a8_int8_channel_gemm, torch.int8)):
