@@ -30,7 +30,8 @@
 namespace prr {
 
 // ---------------------------------------------------------------------------
-// Skinny-M path (decode: M <= 128).  The weight is streamed from HBM once and
+// Skinny-M path (M <= 64 where the persistent decode kernel cannot hold the
+// activations in registers, i.e. long K).  The weight is streamed from HBM once and
 // is the whole cost: every design choice below serves keeping enough weight
 // bytes in flight per CU.
 //
@@ -41,7 +42,7 @@ namespace prr {
 // per lane each) into a D-deep register ring, so D blocks of loads are in
 // flight while the MFMAs of the oldest block run.  The KS partial sums of a
 // channel group are added through LDS at the end.  Activations (at most
-// 128 x K bytes) stay in L2 and are re-read by every strip; the weight is
+// 64 x K bytes) stay in L2 and are re-read by every strip; the weight is
 // read exactly once.
 // ---------------------------------------------------------------------------
 template <int MT, int S, int KS, int D>
@@ -55,16 +56,12 @@ struct SkinnyCfg {
 };
 
 // Configuration per m-tile count, chosen by a sweep of (S, KS, D) on MI355X
-// over N = 27648 / 37888, K = 5120 / 3584, M = 1 .. 128 (FP8 and INT8).
+// over N = 27648 / 37888, K = 5120 / 3584, M = 1 .. 64 (FP8 and INT8).
 template <int MT> struct SkinnyPick;
 template <> struct SkinnyPick<1> { using type = SkinnyCfg<1, 2, 4, 2>; };
 template <> struct SkinnyPick<2> { using type = SkinnyCfg<2, 4, 4, 2>; };
 template <> struct SkinnyPick<3> { using type = SkinnyCfg<3, 4, 4, 2>; };
 template <> struct SkinnyPick<4> { using type = SkinnyCfg<4, 4, 2, 2>; };
-template <> struct SkinnyPick<5> { using type = SkinnyCfg<5, 2, 2, 2>; };
-template <> struct SkinnyPick<6> { using type = SkinnyCfg<6, 2, 2, 2>; };
-template <> struct SkinnyPick<7> { using type = SkinnyCfg<7, 2, 2, 2>; };
-template <> struct SkinnyPick<8> { using type = SkinnyCfg<8, 2, 2, 2>; };
 
 template <class Cfg, bool kInt8>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(
@@ -345,7 +342,8 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
   // The skinny kernel addresses A and one 128-row weight slab with 32-bit
   // buffer offsets.
   const int64_t mt16 = (M + 15) / 16 * 16;
-  if (M <= 128 && 128 * K < kOutOfRange &&
+  // Above 64 rows the many-token kernel (128-wide tiles when few) is faster.
+  if (M <= 64 && 128 * K < kOutOfRange &&
       (kInt8 || mt16 * (K / kBlock) <= kSkinnyLdsScales)) {
     const int mt = (int)((M + 15) / 16);
 #define PRR_SKINNY(X)                                                                        \
@@ -365,10 +363,6 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
       PRR_SKINNY(2)
       PRR_SKINNY(3)
       PRR_SKINNY(4)
-      PRR_SKINNY(5)
-      PRR_SKINNY(6)
-      PRR_SKINNY(7)
-      PRR_SKINNY(8)
       default:
         return hipErrorInvalidValue;
     }

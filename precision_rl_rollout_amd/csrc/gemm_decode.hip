@@ -1,4 +1,4 @@
-// W8A8 GEMM for decode-sized batches (M <= 128): activation-resident,
+// W8A8 GEMM for decode-sized batches (M <= 64): activation-resident,
 // weight-streaming, persistent.
 //
 // Long-tail decode runs the linear layers at small effective batch, where
@@ -306,7 +306,8 @@ bool launch_gemm_decode(const uint8_t* A, const float* sa, const uint8_t* W, con
                         int64_t M, int64_t N, int64_t K, uint16_t* C, hipStream_t stream,
                         hipError_t* err) {
   // 32-bit offsets: a 16-row strip and all of A must stay below 2^31 bytes.
-  if (M < 1 || M > 128 || K < kBlock || 128 * K >= 0x7FFFFF00LL || N > 0x7FFFFFFFLL - 16)
+  // Activations of more than 64 rows do not fit in registers.
+  if (M < 1 || M > 64 || K < kBlock || 128 * K >= 0x7FFFFF00LL || N > 0x7FFFFFFFLL - 16)
     return false;
   if (!kInt8 && ((M + 15) / 16 * 16) * (K / kBlock) > 8192) return false;   // scales in LDS
   switch ((M + 15) / 16) {
@@ -314,7 +315,7 @@ bool launch_gemm_decode(const uint8_t* A, const float* sa, const uint8_t* W, con
     case 2: return launch_decode_mt<2, kInt8>(A, sa, W, sw, M, N, K, C, stream, err);
     case 3:
     case 4: return launch_decode_mt<4, kInt8>(A, sa, W, sw, M, N, K, C, stream, err);
-    default: return false;      // M > 64: activations do not fit in registers
+    default: return false;
   }
 }
 

@@ -458,13 +458,16 @@ bool launch_gemm_prefill(const uint8_t* A, const float* sa, const uint8_t* W, co
   // most half the compute units busy, the trailing tile columns of that
   // round run as twice as many 128-wide tiles in a second launch (whole
   // rounds first, then one round of half-size tiles instead of a half-empty
-  // round of full ones).
+  // round of full ones).  With fewer 256-wide tiles than compute units
+  // (few tokens), 128-wide tiles throughout.
   const int64_t cus = compute_units();
   const int64_t tn256 = (N + 255) / 256;
   int64_t c = 0;
   for (int64_t cc = 1; cc < tn256 && c == 0; ++cc)
     if (((tn256 - cc) * tiles_m) % cus == 0 && 2 * cc * tiles_m <= cus) c = cc;
-  if (c == 0) {
+  if (tiles_m * tn256 < cus) {
+    launch_cols<kInt8, 128>(A, sa, W, sw, M, N, K, C, 0, N, stream);
+  } else if (c == 0) {
     launch_cols<kInt8, 256>(A, sa, W, sw, M, N, K, C, 0, N, stream);
   } else {
     const int64_t n_split = (tn256 - c) * 256;

@@ -6,6 +6,14 @@
 
 namespace prr {
 
+// 16-byte load of data read exactly once (quantizer inputs): marked
+// non-temporal so it streams past the caches instead of displacing lines.
+__device__ __forceinline__ uint4 load_once16(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
 constexpr int kBlock = 128;          // weight block edge, activation group
 constexpr float kFp8Max = 448.0f;    // largest finite e4m3 magnitude
 constexpr float kInt8Max = 127.0f;

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t r = row0 + i * 16 + seg;
-      v[i] = *reinterpret_cast<const uint4*>(w + r * K + col);
+      v[i] = load_once16(w + r * K + col);
     }
   } else {
 #pragma unroll
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void fp8_act_group_kernel(
 
   uint4 v;
   if constexpr (kVec) {            // K % 8 == 0: a chunk is all in or all out
-    v = (col < K) ? *reinterpret_cast<const uint4*>(src + col) : make_uint4(0, 0, 0, 0);
+    v = (col < K) ? load_once16(src + col) : make_uint4(0, 0, 0, 0);
   } else {
     uint32_t h[8];
 #pragma unroll

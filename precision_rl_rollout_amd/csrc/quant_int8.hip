@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void int8_row_resident_kernel(
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int64_t c = (int64_t)i * kLanes + lane;
-    v[i] = (live && c < chunks) ? *reinterpret_cast<const uint4*>(src + c * 8)
+    v[i] = (live && c < chunks) ? load_once16(src + c * 8)
                                 : make_uint4(0, 0, 0, 0);
     m = absmax_bf16x2(m, v[i].x);
     m = absmax_bf16x2(m, v[i].y);
