@@ -76,6 +76,9 @@ KERNEL_SOURCES = {
     # M <= 64 runs the persistent decode kernel.
     "w8a8_block_gemm@decode7b_upgate": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
     "w8a8_int8_channel_gemm@decode7b_upgate": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
+    # M = 8192 runs the many-token kernel.
+    "w8a8_block_gemm@prefill32b": ["gemm_prefill.hip", "mfma.h", "prr_device.h"],
+    "w8a8_int8_channel_gemm@prefill32b": ["gemm_prefill.hip", "mfma.h", "prr_device.h"],
 }
 
 
