@@ -11,18 +11,23 @@
 //    output (strip s, s + G, s + 2G, ...; G = grid size), so every CU stays
 //    busy to the end with at most one strip of imbalance.
 //  * K is split 8 ways across the waves.  Each wave loads the activation
-//    fragments of all m-tiles for its K piece (and their FP8 scales) once,
-//    at the start, and keeps them in registers: activations are never
-//    re-read per strip.
-//  * Per strip a wave loads only the weight fragments of its K piece
-//    (16 rows x 32 bytes per lane per K block, through raw buffer loads)
-//    into a D-deep register ring, so D strips are in flight; the ring is
-//    branch-free (pieces or strips past the end load at an out-of-range
-//    offset: no traffic, zeros) so the compiler waits only for the oldest
-//    stage.
+//    fragments of all m-tiles for its K piece once, at the start, and keeps
+//    them in registers: activations are never re-read per strip.
+//  * The weight reaches each wave through its own ring of R LDS slots.  A
+//    slot holds one task, one K block (16 rows x 128 bytes) of one strip,
+//    written by two direct-to-LDS buffer loads of 8 whole 128-byte rows
+//    (full cache lines), plus a 4-byte load of the task's weight scale
+//    (FP8; INT8: the strip's 16 channel scales, with its first task).  The
+//    wave keeps R - 1 tasks in flight: it starts task t + R - 1, waits for
+//    task t, reads the fragment from LDS and runs its MFMAs.  No other wave
+//    touches the slots, so the ring needs no barrier.  (Loading fragments
+//    straight into registers makes each load instruction read 16 rows x 64
+//    bytes, half lines, which held the stream near 4.8 TB/s, and the
+//    register ring limited how much K a wave could hold.)  Tasks past the
+//    end load at out-of-range offsets: no traffic, zeros, no branch.
 //  * The 8 partial sums of a strip meet in LDS; MT waves add them, apply
 //    the epilogue and store bf16.  The barriers order LDS only, so they do
-//    not drain the weight loads in flight.
+//    not drain the loads in flight.
 //
 // FP8: per K block, C += sa[m, kb] * sw[n / 128, kb] * MFMA(Wq, Aq) (one
 // v_mfma_f32_16x16x128_f8f6f4 per block, zero accumulator).  INT8: the
@@ -36,14 +41,31 @@
 namespace prr {
 
 constexpr int kDecodeWaves = 8;
+constexpr int kDecodeRing = 6;       // LDS slots per wave (5 tasks in flight)
+constexpr int kLdsBytes = 163840;    // LDS per workgroup on gfx950
 
-// D: strips of weight fragments held per wave.  Each fragment is reloaded
-// (for strip i + D) right after the MFMA that consumed it, so about D
-// strips are always in flight.
-template <int MT, int P, int D, bool kInt8>
+// One ring slot: a task's weight block (row r at bytes [128 r, 128 r + 128),
+// 16-byte chunk c of the row at position c ^ ((r >> 1) & 7), so the 16 rows
+// of one fragment read fall on distinct banks) and its scales.
+struct DecodeSlot {
+  uint8_t w[16 * kBlock];
+  float s[64];
+};
+
+// s_waitcnt vmcnt(n) that is also a compiler memory barrier, so no LDS read
+// of the awaited slot can be moved above it.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(n) : "memory");
+}
+
+// P: K blocks of the wave's piece held in registers (>= ceil(K/128 / 8)).
+template <int MT, int P, bool kInt8>
 __global__ __launch_bounds__(512) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int nstrips) {
+  constexpr int R = kDecodeRing;
+  __shared__ __align__(16) DecodeSlot ring[kDecodeWaves][R];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -65,8 +87,9 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
       afr[mt][j] = buffer_load32(ares, off, 0);
     }
 
-  // LDS: the FP8 activation scales of all rows, transposed to [K block][row]
-  // (kept for the whole kernel), then the partial-sum exchange buffer.
+  // Dynamic LDS: the FP8 activation scales of all rows, transposed to
+  // [K block][row] (kept for the whole kernel), then the partial-sum
+  // exchange buffer.
   extern __shared__ float lds_dyn[];
   constexpr int kRows = MT * 16;
   float* lsa = lds_dyn;
@@ -78,173 +101,153 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
     }
     lds_barrier();
   }
-
-  const int G = gridDim.x;
-  const int my_n = (nstrips - (int)blockIdx.x + G - 1) / G;   // strips of this workgroup
-
-  // Strip index math is made provably uniform (readfirstlane) so that the
-  // weight resource and the scale addresses live in scalar registers: a
-  // vector load of a scale would queue behind every weight refill in flight.
-  auto strip_n0 = [&](int i) -> int64_t {
-    return (int64_t)__builtin_amdgcn_readfirstlane((int)blockIdx.x + i * G) * 16;
-  };
-
-  // INT8 epilogue scales: the lane's token rows (once) and, per strip, the
-  // lane's four channels (loaded with the strip's weight, D strips ahead).
   float sa_row[MT];
-  float4 swq[D];
-  const __amdgpu_buffer_rsrc_t swres = buffer_rsrc(sw, kInt8 ? (int64_t)N * 4 : 0);
   if constexpr (kInt8) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) sa_row[mt] = (mt * 16 + r16 < M) ? sa[mt * 16 + r16] : 0.f;
   }
-  auto load_swq = [&](int i) -> float4 {
-    const int off = (i < my_n) ? (int)(strip_n0(i) + 4 * g) * 4 : kOutOfRange;
-    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(swres, off, 0, 0);
-    return make_float4(__int_as_float(v[0]), __int_as_float(v[1]), __int_as_float(v[2]),
-                       __int_as_float(v[3]));
+
+  const int G = gridDim.x;
+  // Strips of this workgroup (uniform; the integer division runs on the
+  // vector unit, so the compiler needs telling).
+  const int my_n = __builtin_amdgcn_readfirstlane((nstrips - (int)blockIdx.x + G - 1) / G);
+  // Strip index math is made provably uniform (readfirstlane) so that the
+  // descriptors and LDS addresses live in scalar registers.
+  auto strip_n0 = [&](int i) -> int {
+    return __builtin_amdgcn_readfirstlane((int)blockIdx.x + i * G) * 16;
   };
 
-  // Weight ring: D strips, each this wave's P fragments of one strip.
-  v8i wbuf[D][P];
-  auto load_strip = [&](int d, int i) {
-    const bool live = i < my_n;                                 // workgroup-uniform
-    const int64_t n0 = strip_n0(i);
-    const int64_t rows = live ? min<int64_t>(16, N - n0) : 0;
-    const __amdgpu_buffer_rsrc_t wres = buffer_rsrc(W + (live ? n0 : 0) * K, rows * K);
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int off = (j < pw) ? r16 * K + (kb0 + j) * kBlock + g * 16 : kOutOfRange;
-      wbuf[d][j] = buffer_load32(wres, off, 0);
-    }
+  // Task loads.  Lane l fills bytes [16 l, 16 l + 16) of each half of a
+  // slot: row 8 h + l / 8, slot position l % 8, i.e. global chunk
+  // (l % 8) ^ ((row >> 1) & 7).
+  const int NB = (N + kBlock - 1) / kBlock;
+  const v4i rsw = sgpr_rsrc(sw, kInt8 ? (int64_t)N * 4 : (int64_t)NB * KB * 4);
+  const int lrow0 = lane >> 3, lrow1 = lrow0 + 8;
+  const int lofs0 = lrow0 * K + (((lane & 7) ^ ((lrow0 >> 1) & 7)) << 4);
+  const int lofs1 = lrow1 * K + (((lane & 7) ^ ((lrow1 >> 1) & 7)) << 4);
+  auto load_task = [&](int t) {
+    const int i = t / P, j = t - i * P;
+    const bool live = i < my_n;
+    const int n0 = strip_n0(live ? i : 0);
+    const int rows = live ? min(16, N - n0) : 0;   // rows past N read zeros
+    const v4i rw = sgpr_rsrc(W + (int64_t)n0 * K, (int64_t)rows * K);
+    const bool jl = j < pw;
+    const int kofs = (kb0 + j) * kBlock;
+    DecodeSlot& sl = ring[wave][t % R];
+    dma_b128(rw, lds_addr(sl.w), jl ? lofs0 + kofs : kOutOfRange, 0);
+    dma_b128(rw, lds_addr(sl.w + 1024), jl ? lofs1 + kofs : kOutOfRange, 0);
+    int vs;
+    if constexpr (kInt8)
+      vs = (live && j == 0 && lane < 16 && n0 + lane < N) ? (n0 + lane) * 4 : kOutOfRange;
+    else
+      vs = (live && jl && lane == 0) ? ((n0 >> 7) * KB + kb0 + j) * 4 : kOutOfRange;
+    dma_b32(rsw, lds_addr(sl.s), vs);
   };
+  constexpr int kLoadsPerTask = 3;
+
+  // Fragment read offsets of this lane within a slot (chunks g and g + 4).
+  const int rbase = r16 * kBlock;
+  const int roff_lo = rbase + ((g ^ ((r16 >> 1) & 7)) << 4);
+  const int roff_hi = rbase + (((g + 4) ^ ((r16 >> 1) & 7)) << 4);
+
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    load_strip(d, d);
-    if constexpr (kInt8) swq[d] = load_swq(d);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  for (int q = 0; q < R - 1; ++q) load_task(q);
 
   auto red = reinterpret_cast<float (*)[MT][4][64]>(lred);      // [wave][mt][r][lane]
-
-  for (int t = 0; t < my_n; t += D) {
+  for (int i = 0; i < my_n; ++i) {
+    const int n0 = strip_n0(i);
+    float accf[MT][4];
+    v4i acci[MT];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int i = t + d;
-      const int64_t n0 = strip_n0(i);
-      float accf[MT][4];
-      v4i acci[MT];
+    for (int mt = 0; mt < MT; ++mt) {
+      acci[mt] = v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acci[mt] = v4i{0, 0, 0, 0};
+      for (int r = 0; r < 4; ++r) accf[mt][r] = 0.f;
+    }
+    float swcur[4] = {0.f, 0.f, 0.f, 0.f};
+    // An opaque zero keeps the compiler from hoisting the (strip-invariant)
+    // activation-scale reads out of the loop into registers.
+    int opaque0;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(opaque0));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accf[mt][r] = 0.f;
-      }
-      // The next strip's fragments for this slot, issued one by one as the
-      // current ones are consumed (same resource for the whole strip).
-      const int inext = i + D;
-      const bool nlive = inext < my_n;
-      const int64_t nn0 = strip_n0(inext);
-      const int64_t nrows = nlive ? min<int64_t>(16, N - nn0) : 0;
-      const __amdgpu_buffer_rsrc_t nres = buffer_rsrc(W + (nlive ? nn0 : 0) * K, nrows * K);
-      float4 swcur = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < P; ++j) {
+      const int t = i * P + j;
+      load_task(t + R - 1);
+      wait_vmcnt<kLoadsPerTask * (R - 1)>();   // task t has landed
+      const DecodeSlot& sl = ring[wave][t % R];
+      const uint4 lo = *reinterpret_cast<const uint4*>(sl.w + roff_lo);
+      const uint4 hi = *reinterpret_cast<const uint4*>(sl.w + roff_hi);
+      const v8i wf = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       if constexpr (kInt8) {
+        if (j == 0) {
+          // Read now (the slot is reloaded before the epilogue needs them):
+          // the asm consumes the registers, so the read completes here.
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acci[mt] = mfma_i8x2(wbuf[d][j], afr[mt][j], acci[mt]);
-          wbuf[d][j] = buffer_load32(
-              nres, (j < pw) ? r16 * K + (kb0 + j) * kBlock + g * 16 : kOutOfRange, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        swcur = swq[d];
-        swq[d] = load_swq(inext);
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        // The strip's weight scales for this wave's K blocks (the index is
-        // clamped into the array; blocks past the piece multiply zeros).
-        const float* swrow =
-            sw + (int64_t)__builtin_amdgcn_readfirstlane((int)(((i < my_n ? n0 : 0) >> 7) * KB));
-        // An opaque zero keeps the compiler from hoisting the (strip-
-        // invariant) activation-scale reads out of the loop into registers.
-        int opaque0;
-        asm volatile("v_mov_b32 %0, 0" : "=v"(opaque0));
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-          const int kb = min(kb0 + j, KB - 1);
-          const float swv = swrow[kb];
-          // (blocks past the piece read a real scale and multiply zeros)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const v4f p = mfma_fp8(wbuf[d][j], afr[mt][j]);
-            const float sc = lsa[kb * kRows + mt * 16 + r16 + opaque0] * swv;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) accf[mt][r] = fmaf(p[r], sc, accf[mt][r]);
+          for (int r = 0; r < 4; ++r) {
+            swcur[r] = sl.s[4 * g + r];
+            asm volatile("" : "+v"(swcur[r]));
           }
-          wbuf[d][j] = buffer_load32(
-              nres, (j < pw) ? r16 * K + (kb0 + j) * kBlock + g * 16 : kOutOfRange, 0);
-          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acci[mt] = mfma_i8x2(wf, afr[mt][j], acci[mt]);
+      } else {
+        // (blocks past the piece multiply zeros; their scale index is clamped)
+        const int kb = min(kb0 + j, KB - 1);
+        const float swv = sl.s[0];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const v4f p = mfma_fp8(wf, afr[mt][j]);
+          const float sc = lsa[kb * kRows + mt * 16 + r16 + opaque0] * swv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) accf[mt][r] = fmaf(p[r], sc, accf[mt][r]);
         }
       }
-
-      // Add the 8 partial sums of the strip through LDS (for 8 m-tiles the
-      // upper 4 waves first fold theirs into the lower 4, so the buffer
-      // holds at most 4 waves x 8 KB).
-      constexpr int kHeld = (MT > 4) ? kDecodeWaves / 2 : kDecodeWaves;
-      if constexpr (MT > 4) {
-        if (wave >= kHeld) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              red[wave - kHeld][mt][r][lane] =
-                  kInt8 ? __int_as_float(acci[mt][r]) : accf[mt][r];
-        }
-        lds_barrier();
-        if (wave < kHeld) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if constexpr (kInt8) acci[mt][r] += __float_as_int(red[wave][mt][r][lane]);
-              else accf[mt][r] += red[wave][mt][r][lane];
-            }
-        }
-        lds_barrier();
-      }
-      if (wave < kHeld) {
+      // One task per scheduling region: hoisting later tasks' LDS reads, or
+      // sinking this task's FMAs to the end of the strip (which keeps every
+      // MFMA product live), would cost registers the resident activations
+      // need.  The empty volatile asm pins the FMAs before the next task.
+      if constexpr (!kInt8) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            red[wave][mt][r][lane] = kInt8 ? __int_as_float(acci[mt][r]) : accf[mt][r];
+          for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(accf[mt][r]));
       }
-      lds_barrier();
-      if (i < my_n && wave < MT) {
-        const int mt = wave;
-        const int64_t m = mt * 16 + r16;
-        const int64_t n = n0 + 4 * g;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if constexpr (kInt8) {
-            int32_t tsum = 0;
-#pragma unroll
-            for (int w = 0; w < kHeld; ++w) tsum += __float_as_int(red[w][mt][r][lane]);
-            const float sn = r == 0 ? swcur.x : r == 1 ? swcur.y : r == 2 ? swcur.z : swcur.w;
-            v[r] = (float)tsum * (sa_row[mt] * sn);
-          } else {
-            float fsum = 0.f;
-#pragma unroll
-            for (int w = 0; w < kHeld; ++w) fsum += red[w][mt][r][lane];
-            v[r] = fsum;
-          }
-        }
-        store4(C, M, N, m, n, v);
-      }
-      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
     }
+
+    // Add the 8 partial sums of the strip through LDS.
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[wave][mt][r][lane] = kInt8 ? __int_as_float(acci[mt][r]) : accf[mt][r];
+    lds_barrier();
+    if (wave < MT) {
+      const int mt = wave;
+      const int64_t m = mt * 16 + r16;
+      const int64_t n = n0 + 4 * g;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (kInt8) {
+          int32_t tsum = 0;
+#pragma unroll
+          for (int w = 0; w < kDecodeWaves; ++w) tsum += __float_as_int(red[w][mt][r][lane]);
+          v[r] = (float)tsum * (sa_row[mt] * swcur[r]);
+        } else {
+          float fsum = 0.f;
+#pragma unroll
+          for (int w = 0; w < kDecodeWaves; ++w) fsum += red[w][mt][r][lane];
+          v[r] = fsum;
+        }
+      }
+      store4(C, M, N, m, n, v);
+    }
+    lds_barrier();
   }
+  // The trailing (out-of-range) loads land before the LDS is released.
+  wait_vmcnt<0>();
 }
 
 // Compute units of the current device (cached per device ordinal).
@@ -263,8 +266,9 @@ int compute_units() {
   return v;
 }
 
-// Largest P (K blocks per wave) whose resident activations fit the
-// register budget for each m-tile count: MT * P * 8 VGPRs.
+// Smallest P (K blocks per wave) that covers the wave's piece.  Resident
+// activations take MT * P * 8 VGPRs; these ranges compile without spills
+// (K up to 8192 for M <= 32, 6144 for M <= 64).
 template <int MT, bool kInt8>
 static bool launch_decode_mt(const uint8_t* A, const float* sa, const uint8_t* W,
                              const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* C,
@@ -274,28 +278,23 @@ static bool launch_decode_mt(const uint8_t* A, const float* sa, const uint8_t* W
   const int nstrips = (int)((N + 15) / 16);
   const int cus = compute_units();
   const int grid = nstrips < cus ? nstrips : cus;
-  const size_t lds =
-      ((size_t)(MT > 4 ? kDecodeWaves / 2 : kDecodeWaves) * MT * 4 * 64 + (kInt8 ? 0 : (size_t)MT * 16 * KB)) *
-      sizeof(float);
-  constexpr int D = MT >= 4 ? 1 : 2;
+  const size_t lds = ((size_t)kDecodeWaves * MT * 4 * 64 + (kInt8 ? 0 : (size_t)MT * 16 * KB)) *
+                     sizeof(float);
+  if (lds + sizeof(DecodeSlot) * kDecodeWaves * kDecodeRing > (size_t)kLdsBytes) return false;
 #define PRR_DECODE_P(PV)                                                                  \
   if (pw <= PV) {                                                                         \
-    hipLaunchKernelGGL((gemm_decode_kernel<MT, PV, D, kInt8>), dim3(grid), dim3(512), lds, \
+    hipLaunchKernelGGL((gemm_decode_kernel<MT, PV, kInt8>), dim3(grid), dim3(512), lds,   \
                        stream, A, sa, W, sw, (int)M, (int)N, (int)K, C, nstrips);         \
     *err = hipGetLastError();                                                             \
     return true;                                                                          \
   }
-  // Resident activations take MT * P * 8 of a wave's 256 registers and the
-  // weight ring D * P * 8; these ranges compile without spills (so K up to
-  // 6144 for M <= 16, 5120 for M <= 32, 4096 for M <= 64).
   PRR_DECODE_P(2)
   PRR_DECODE_P(3)
   PRR_DECODE_P(4)
+  PRR_DECODE_P(5)
+  PRR_DECODE_P(6)
   if constexpr (MT <= 2) {
-    PRR_DECODE_P(5)
-  }
-  if constexpr (MT <= 1) {
-    PRR_DECODE_P(6)
+    PRR_DECODE_P(8)
   }
 #undef PRR_DECODE_P
   return false;
@@ -307,8 +306,9 @@ bool launch_gemm_decode(const uint8_t* A, const float* sa, const uint8_t* W, con
                         hipError_t* err) {
   // 32-bit offsets: a 16-row strip and all of A must stay below 2^31 bytes.
   // Activations of more than 64 rows do not fit in registers.
-  if (M < 1 || M > 64 || K < kBlock || 128 * K >= 0x7FFFFF00LL || N > 0x7FFFFFFFLL - 16)
-    return false;
+  // Scale offsets (4 N for INT8, 4 ceil(N/128) K/128 for FP8) are 32-bit too.
+  if (M < 1 || M > 64 || K < kBlock || 128 * K >= 0x7FFFFF00LL || N > 0x1FFFFFF0LL) return false;
+  if (!kInt8 && 4 * ((N + kBlock - 1) / kBlock) * (K / kBlock) >= 0x7FFFFF00LL) return false;
   if (!kInt8 && ((M + 15) / 16 * 16) * (K / kBlock) > 8192) return false;   // scales in LDS
   switch ((M + 15) / 16) {
     case 1: return launch_decode_mt<1, kInt8>(A, sa, W, sw, M, N, K, C, stream, err);

@@ -38,51 +38,10 @@ struct Stage {
   float scales[kWaves][64];
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
-}
-
-// Buffer descriptor as four scalar words (raw buffer, no stride, dword data
-// format): base, num_records = bytes (clamped to 2^31 - 1).
-__device__ __forceinline__ v4i sgpr_rsrc(const void* base, int64_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  v4i r;
-  r[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  r[1] = (int)(__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xFFFFu);
-  r[2] = __builtin_amdgcn_readfirstlane((int)(bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes));
-  r[3] = 0x00020000;
-  return r;
-}
-
-// Direct-to-LDS buffer loads: lane l's 16 (4) bytes land at LDS byte address
-// lds + 16 l (4 l); offsets at or past num_records read zeros.  Issued as
-// inline assembly so that the compiler adds no wait of its own on them
-// before LDS reads (its tracking cannot tell the two stages apart and would
-// wait for the next stage's loads before reading the current one); the
-// kernel waits for them itself (vmcnt(0)) before the barrier that hands a
-// stage to the other waves.
-__device__ __forceinline__ void dma_b128(v4i rsrc, uint32_t lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
-// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
-// maxima (no wait on them).
-constexpr int kWaitVmcnt0 = 0x0F70;
+constexpr int kWaitVmcnt0 = vmcnt_imm(0);
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kBlock + ((c ^ ((r >> 1) & 7)) << 4); }
 
@@ -344,7 +303,7 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
 
   stage_load<kInt8, TN>(st0, ra, rw, rsa, rsw, da, dw, K, KB, 0, wave, lane);
   stage_load<kInt8, TN>(st1, ra, rw, rsa, rsw, da, dw, K, KB, 1, wave, lane);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | kDmaPerStage<kInt8, TN>);   // block 0 landed
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerStage<kInt8, TN>));   // block 0 landed
   lds_barrier();
   Front f;
   load_front<kInt8, TN>(st0, f, wm, wn, lane, fo);

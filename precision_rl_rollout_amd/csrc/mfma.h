@@ -92,6 +92,48 @@ __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int v
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+
+// Buffer descriptor as four scalar words (raw buffer, no stride, dword data
+// format): base, num_records = bytes (clamped to 2^31 - 1).
+__device__ __forceinline__ v4i sgpr_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  r[1] = (int)(__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xFFFFu);
+  r[2] = __builtin_amdgcn_readfirstlane((int)(bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Direct-to-LDS buffer loads: lane l's 16 (4) bytes land at LDS byte address
+// lds + 16 l (4 l); offsets at or past num_records read zeros.  Issued as
+// inline assembly so that the compiler adds no wait of its own on them
+// before LDS reads (its alias tracking of such loads cannot tell ring slots
+// or stages apart, and waited for the next slot's loads before reading the
+// current one); the kernels wait for them explicitly with s_waitcnt vmcnt.
+__device__ __forceinline__ void dma_b128(v4i rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// s_waitcnt immediate for vmcnt(n), n < 64, with expcnt and lgkmcnt left at
+// their maxima (no wait on them).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences
 // global memory, which waits for every outstanding global load and would
 // drain the load pipelines below at each barrier.

@@ -78,6 +78,9 @@ def _check(c_gpu, ref, label):
 GEMM_SHAPES = [(16, 256, 256), (5, 200, 384), (1, 16, 128), (17, 129, 256), (33, 1000, 640),
                (128, 384, 1024), (129, 385, 512), (130, 300, 256), (256, 256, 1024),
                (300, 520, 384), (64, 130, 128),
+               # decode kernel: 5, 6 and 8 K blocks per wave; 601 strips, so a
+               # workgroup streams several strips through its LDS ring
+               (64, 640, 5120), (48, 500, 6144), (24, 300, 8192), (40, 9607, 1024),
                # many-token kernel (256 x 256 tiles): odd K-block count over a
                # 3 x 4 tile grid, a single K block over 9 x 2 tiles, 4 x 4 tiles
                (513, 777, 1152), (2304, 512, 128), (1024, 1024, 256)]
