@@ -22,6 +22,10 @@ What it computes, with the passage each part follows:
   weight scales and per-token activation scales ``amax / 127`` (FlashRL
   article, sections on 8-bit rollout and online quantization with parameter
   updates: INT8 and FP8 rollout).
+* ``oracle.kv`` -- the FP8 KV cache: one scale ``amax / 448`` per tensor,
+  recalibrated every step, and quantize-on-write of token rows into cache
+  slots (FP8-RL abstract, item (ii): FP8 KV cache with per-step QKV scale
+  recalibration; granularity and write rule are readings, listed there).
 * ``oracle.gemm`` -- the W8A8 linear layer: fp64 accumulation over the
   exactly decoded 8-bit operands with the per-K-block (FP8) or per-row and
   per-channel (INT8) scales, rounded once to bf16.
