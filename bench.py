@@ -366,13 +366,78 @@ def run_stack32b(args, torch, B, W):
                         "int8_weight_channel_quant(stack)": {"us": round(peri, 1), "GB/s": round(bi / peri / 1e3, 1)}}}
 
 
+def run_kv32b(args, torch, B, W):
+    """FP8 KV cache of a 32B-class layer for a 16,384-token prefill: per
+    step, recalibrate the K and V scales on the new rows and write both into
+    a 65,536-slot cache (16-slot pages in random order)."""
+    cfg = W.KV_32B
+    T, C, S = cfg["T"], cfg["C"], cfg["num_slots"]
+    kb, vb = W.kv_rows(T, C, 0, "K"), W.kv_rows(T, C, 0, "V")
+    k = torch.from_numpy(kb.view(np.int16)).cuda()
+    v = torch.from_numpy(vb.view(np.int16)).cuda()
+    slots_np = W.kv_slot_mapping(T, S, cfg["page"], 0)
+    slots = torch.from_numpy(slots_np).cuda()
+    kc = torch.zeros((S, C), dtype=torch.uint8, device="cuda:0")
+    vc = torch.zeros_like(kc)
+    ks = torch.empty(1, dtype=torch.float32, device="cuda:0")
+    vs = torch.empty_like(ks)
+
+    def step(timer=None):
+        calls = [("fp8_kv_scale_recalibrate", lambda: B.fp8_kv_scale_recalibrate(k, out=ks)),
+                 ("fp8_kv_scale_recalibrate", lambda: B.fp8_kv_scale_recalibrate(v, out=vs)),
+                 ("fp8_kv_cache_write", lambda: B.fp8_kv_cache_write(k, slots, ks, kc)),
+                 ("fp8_kv_cache_write", lambda: B.fp8_kv_cache_write(v, slots, vs, vc))]
+        for name, fn in calls:
+            timer.run(name, fn) if timer else fn()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    us = timer.avg_us()
+    b_recal = 2 * T * C + 4
+    b_write = 3 * T * C + 8 * T + 4
+    step_bytes = 2 * b_recal + 2 * b_write
+    line = {"metric": METRIC, "value": round(step_bytes / dt / 1e9, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "vs_baseline": None,
+            "dtype": "fp8e4m3", "data": "synthetic",
+            "config": {"workload": "kv32b_prefill", "tokens": T, "row": C, "slots": S},
+            "roofline": {"bound": "hbm", "kernel": "fp8_kv_cache_write",
+                         "achieved": round(b_write / us["fp8_kv_cache_write"] / 1e3, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(b_write / us["fp8_kv_cache_write"] / 1e3 / HBM_PEAK_GBS, 4),
+                         "traffic": None},
+            "kernels": {"fp8_kv_scale_recalibrate": {"us": round(us["fp8_kv_scale_recalibrate"], 2),
+                                                     "algorithmic_bytes": b_recal,
+                                                     "GB/s": round(b_recal / us["fp8_kv_scale_recalibrate"] / 1e3, 1)},
+                        "fp8_kv_cache_write": {"us": round(us["fp8_kv_cache_write"], 2),
+                                               "algorithmic_bytes": b_write,
+                                               "GB/s": round(b_write / us["fp8_kv_cache_write"] / 1e3, 1)}}}
+    if not args.no_cpu_baseline:
+        from oracle import kv as okv
+        t0 = time.perf_counter()
+        for xb in (kb, vb):
+            okv.kv_cache_write(np.zeros((S, C), np.uint8), xb, slots_np, okv.kv_scale(xb))
+        ct = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(step_bytes / ct / 1e9, 3), "unit": "GB/s",
+                                "cores": cpu_threads(), "kind": "oracle",
+                                "sample": "one whole step (K and V: recalibration and cache write)"}
+    return line
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode7b_upgate",
-                    choices=["decode7b_upgate", "decode32b_sweep", "prefill32b", "stack32b_requant"])
+                    choices=["decode7b_upgate", "decode32b_sweep", "prefill32b", "stack32b_requant",
+                             "kv32b_prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (outside the "
@@ -399,7 +464,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
     run = {"decode7b_upgate": run_decode7b, "decode32b_sweep": run_decode32b,
-           "prefill32b": run_prefill32b, "stack32b_requant": run_stack32b}[args.workload]
+           "prefill32b": run_prefill32b, "stack32b_requant": run_stack32b,
+           "kv32b_prefill": run_kv32b}[args.workload]
     line = run(args, torch, B, W)
     print(json.dumps(line), flush=True)
     return 0

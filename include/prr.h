@@ -3,18 +3,21 @@
  *
  * The calls implement the per-step re-quantization of freshly updated bf16
  * policy weights and activations into FP8 e4m3 with block scales, the W8A8
- * block-scaled linear layer with bf16 output, and an INT8 per-channel
- * variant of both.  Sources:
+ * block-scaled linear layer with bf16 output, an INT8 per-channel variant
+ * of both, and the FP8 KV cache (per-step scale recalibration and
+ * quantize-on-write).  Sources:
  *   - "FP8-RL: A Practical and Stable Low-Precision Stack for LLM
  *     Reinforcement Learning", abstract: policy weights change every step
  *     and must be quantized again every step; item (i): FP8 W8A8
- *     linear-layer rollout with blockwise FP8 quantization.
+ *     linear-layer rollout with blockwise FP8 quantization; item (ii): FP8
+ *     KV cache with per-step QKV scale recalibration.
  *   - FlashRL article ("FlashRL: 8Bit Rollouts, Full Power RL"), sections
  *     on rollout quantization and online quantization with parameter
  *     updates: INT8 and FP8 rollout.
  * Block sizes (128 x 128 weight blocks, 1 x 128 activation groups), the
- * e4m3 format with scale amax / 448, and the INT8 per-channel granularity
- * are fixed by this library; the pages do not state them.
+ * e4m3 format with scale amax / 448, the INT8 per-channel granularity and
+ * the per-tensor KV-cache scale are fixed by this library; the pages do not
+ * state them.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -49,8 +52,9 @@
  *     and returns without synchronizing.  Buffers must stay valid until
  *     that work has completed.  Faults inside a kernel surface at the
  *     caller's next synchronization with the stream.
- *   - Calls are stateless, thread-safe and deterministic (no atomics; the
- *     same inputs give the same bits).
+ *   - Calls are stateless, thread-safe and deterministic: the same inputs
+ *     give the same bits.  The only atomic is the integer maximum of the
+ *     KV-scale recalibration, whose result does not depend on order.
  * Errors (returned synchronously, after argument checks and the launch):
  *   - PRR_ERR_INVALID_ARG: a negative dimension, a dimension above
  *     2^31 - 1, or a NULL pointer for a non-empty operand;
@@ -71,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PRR_ABI_VERSION 1
+#define PRR_ABI_VERSION 2
 
 typedef enum prr_status {
   PRR_OK = 0,
@@ -166,6 +170,44 @@ prr_status w8a8_int8_channel_gemm(const int8_t* a_i8, const float* a_scale,
                                   const int8_t* w_i8, const float* w_scale,
                                   int64_t M, int64_t N, int64_t K,
                                   uint16_t* c_bf16, hipStream_t stream);
+
+/*
+ * fp8_kv_scale_recalibrate -- per-step recalibration of one FP8 KV-cache
+ * scale (FP8-RL, abstract, item (ii): the Q/K/V scales are recalibrated at
+ * every step; one scale per tensor is this library's reading).  Call once
+ * per tensor (K, V, and Q for an FP8 attention read path) per step.
+ *   x_bf16 in   [T, C] bf16 bits: a calibration batch of the tensor, e.g.
+ *               the K projection output (C = kv_heads x head_dim).  May be
+ *               NULL when T x C == 0.
+ *   T, C        >= 0.
+ *   scale  out  one fp32: s = fl32(max |x| / 448) over all T x C values
+ *               (+0.0 for an all-zero or empty tensor).  The word is the
+ *               reduction's accumulator while the call's kernels run, so
+ *               nothing may read it before they complete.
+ */
+prr_status fp8_kv_scale_recalibrate(const uint16_t* x_bf16, int64_t T, int64_t C,
+                                    float* scale, hipStream_t stream);
+
+/*
+ * fp8_kv_cache_write -- quantize-on-write of new K or V rows into an FP8
+ * cache (FP8-RL, abstract, item (ii)).
+ *   kv_bf16      in     [T, C] bf16 bits, one row per new token.
+ *   slot_mapping in     [T] int64: the cache row of each token.  A slot
+ *                       outside [0, num_slots) -- negative for a padding
+ *                       token -- skips that token.  Slots in range must be
+ *                       distinct (otherwise which token lands is undefined).
+ *   scale        in     one fp32 in device memory, e.g. written by
+ *                       fp8_kv_scale_recalibrate.  Codes are
+ *                       E4M3_saturating_RNE(fl32(x / s)): values beyond the
+ *                       calibrated range saturate to +-448; s = 0 writes the
+ *                       signed zeros of x.
+ *   cache        in/out [num_slots, C] e4m3 codes; rows no token maps to
+ *                       are not touched.
+ *   T, C, num_slots >= 0; T == 0, C == 0 or num_slots == 0 is a no-op.
+ */
+prr_status fp8_kv_cache_write(const uint16_t* kv_bf16, const int64_t* slot_mapping,
+                              int64_t T, int64_t C, const float* scale, uint8_t* cache,
+                              int64_t num_slots, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* prr_status_string(prr_status status);

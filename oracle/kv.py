@@ -38,9 +38,13 @@ def kv_scale(x_bits) -> np.float32:
 
 
 def kv_encode_rows(x_bits, s: np.float32) -> np.ndarray:
-    """bf16 [T, C] -> e4m3 codes [T, C] with the tensor scale s."""
+    """bf16 [T, C] -> e4m3 codes [T, C] with the tensor scale s; s == 0
+    gives the signed zeros of x (rows may be nonzero here, unlike an
+    all-zero weight block, so this is spelled out)."""
     x = bf16_to_f32(x_bits)
     _check_finite(x)
+    if np.float32(s) == 0:
+        return np.where(np.signbit(x), np.uint8(0x80), np.uint8(0x00)).astype(np.uint8)
     return e4m3.encode(_quotient(x, np.float32(s)))
 
 

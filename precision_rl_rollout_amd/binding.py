@@ -32,6 +32,8 @@ _SIGNATURES = {
     "int8_weight_channel_quant": [_P, _I64, _I64, _P, _P, _P],
     "int8_act_token_quant": [_P, _I64, _I64, _P, _P, _P],
     "w8a8_int8_channel_gemm": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P],
+    "fp8_kv_scale_recalibrate": [_P, _I64, _I64, _P, _P],
+    "fp8_kv_cache_write": [_P, _P, _I64, _I64, _P, _P, _I64, _P],
 }
 
 _lib = None
@@ -188,3 +190,32 @@ def w8a8_int8_channel_gemm(a_i8, a_scale, w_i8, w_scale, out=None):
            load().w8a8_int8_channel_gemm(_ptr(a_i8), _ptr(a_scale), _ptr(w_i8), _ptr(w_scale),
                                          M, N, K, _ptr(c), _stream(a_i8)))
     return c
+
+
+def fp8_kv_scale_recalibrate(x: torch.Tensor, out=None):
+    """x [T, C] bf16 (a calibration batch of K, V or Q) -> scale fp32 [1]
+    (stays on the device: fl32(max |x| / 448))."""
+    x = _bf16_bits(x, "x")
+    T, C = x.shape
+    s = _out(out, torch.float32, (1,), x, "out")
+    _check("fp8_kv_scale_recalibrate",
+           load().fp8_kv_scale_recalibrate(_ptr(x), T, C, s.data_ptr(), _stream(x)))
+    return s
+
+
+def fp8_kv_cache_write(kv: torch.Tensor, slot_mapping: torch.Tensor, scale: torch.Tensor,
+                       cache: torch.Tensor):
+    """Quantize kv [T, C] bf16 with scale (fp32 [1], on the device) into rows
+    slot_mapping[t] (int64 [T]; out-of-range / negative: skipped) of cache
+    (uint8 [num_slots, C], updated in place).  Returns cache."""
+    kv = _bf16_bits(kv, "kv")
+    T, C = kv.shape
+    _operand(slot_mapping, torch.int64, (T,), "slot_mapping")
+    _operand(scale, torch.float32, (1,), "scale")
+    if cache.dtype != torch.uint8 or cache.dim() != 2 or cache.shape[1] != C \
+            or not cache.is_cuda or not cache.is_contiguous():
+        raise ValueError(f"cache: expected a contiguous CUDA uint8 tensor [num_slots, {C}]")
+    _check("fp8_kv_cache_write",
+           load().fp8_kv_cache_write(_ptr(kv), _ptr(slot_mapping), T, C, scale.data_ptr(),
+                                     _ptr(cache), cache.shape[0], _stream(kv)))
+    return cache

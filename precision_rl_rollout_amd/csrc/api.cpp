@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "launch.h"
 #include "prr.h"
 
@@ -41,12 +43,15 @@ prr_status check_device() {
   }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PRR_ERR_NO_DEVICE;
-  static int cache[64];   // 0 unknown, 1 gfx950, 2 other
-  if (dev < 64 && cache[dev] != 0) return cache[dev] == 1 ? PRR_OK : PRR_ERR_UNSUPPORTED_DEVICE;
+  static std::atomic<int> cache[64];   // 0 unknown, 1 gfx950, 2 other
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c != 0) return c == 1 ? PRR_OK : PRR_ERR_UNSUPPORTED_DEVICE;
+  }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PRR_ERR_HIP;
   const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < 64) cache[dev] = ok ? 1 : 2;
+  if (dev < 64) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? PRR_OK : PRR_ERR_UNSUPPORTED_DEVICE;
 }
 
@@ -152,6 +157,30 @@ prr_status w8a8_int8_channel_gemm(const int8_t* a_i8, const float* a_scale, cons
   if (M == 0 || N == 0) return PRR_OK;
   return from_hip(
       prr::launch_w8a8_int8_channel_gemm(a_i8, a_scale, w_i8, w_scale, M, N, K, c_bf16, stream));
+}
+
+prr_status fp8_kv_scale_recalibrate(const uint16_t* x_bf16, int64_t T, int64_t C, float* scale,
+                                    hipStream_t stream) {
+  PRR_TRY(check_dims(T, C));
+  const int64_t n = T * C;
+  if (n > 0) {
+    PRR_TRY(check_ptrs({x_bf16, scale}));
+  } else {
+    PRR_TRY(check_ptrs({scale}));
+  }
+  PRR_TRY(check_device());
+  return from_hip(prr::launch_fp8_kv_scale_recalibrate(x_bf16, n, scale, stream));
+}
+
+prr_status fp8_kv_cache_write(const uint16_t* kv_bf16, const int64_t* slot_mapping, int64_t T,
+                              int64_t C, const float* scale, uint8_t* cache, int64_t num_slots,
+                              hipStream_t stream) {
+  PRR_TRY(check_dims(T, C, num_slots));
+  if (T == 0 || C == 0 || num_slots == 0) return PRR_OK;
+  PRR_TRY(check_ptrs({kv_bf16, slot_mapping, scale, cache}));
+  PRR_TRY(check_device());
+  return from_hip(
+      prr::launch_fp8_kv_cache_write(kv_bf16, slot_mapping, T, C, scale, cache, num_slots, stream));
 }
 
 const char* prr_status_string(prr_status status) {

@@ -1,0 +1,154 @@
+// FP8 KV cache: per-step scale recalibration and quantize-on-write
+// ("FP8-RL: A Practical and Stable Low-Precision Stack for LLM Reinforcement
+// Learning", abstract, item (ii): FP8 KV cache with per-step QKV scale
+// recalibration).  One scale per tensor, s = fl32(amax / 448), and the same
+// saturating round-to-nearest-even e4m3 encode of fl32(x / s) as the weight
+// and activation quantizers.  Both kernels are bound by HBM: 2 bytes read
+// per element for the recalibration, 2 read + 1 written for the write.
+#include "launch.h"
+#include "prr_device.h"
+
+namespace prr {
+
+// The amax is accumulated in the caller's scale word as the bit pattern of
+// a non-negative float (bit order = value order, so an integer maximum is
+// exact and its result does not depend on the order of the updates), then
+// turned into the scale in place.
+__global__ void kv_amax_clear_kernel(uint32_t* acc) { *acc = 0u; }
+
+// Each thread takes kAmaxLoads 16-byte chunks per pass, all loads issued
+// before any is used (one load in flight per thread held it to ~1.9 TB/s).
+constexpr int kAmaxLoads = 16;
+
+__global__ __launch_bounds__(256) void kv_amax_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                      uint32_t* __restrict__ acc) {
+  __shared__ uint32_t red[4];
+  const int tid = threadIdx.x;
+  const int64_t chunks = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  uint32_t m = 0;
+  for (int64_t c0 = (int64_t)blockIdx.x * 256 + tid; c0 < chunks; c0 += stride * kAmaxLoads) {
+    uint4 v[kAmaxLoads];
+#pragma unroll
+    for (int u = 0; u < kAmaxLoads; ++u) {
+      const int64_t c = c0 + u * stride;
+      v[u] = c < chunks ? load_once16(x + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxLoads; ++u) {
+      m = absmax_bf16x2(m, v[u].x);
+      m = absmax_bf16x2(m, v[u].y);
+      m = absmax_bf16x2(m, v[u].z);
+      m = absmax_bf16x2(m, v[u].w);
+    }
+  }
+  m = absmax_fold(m);
+  if (blockIdx.x == 0) {
+    for (int64_t e = chunks * 8 + tid; e < n; e += 256) m = max(m, (uint32_t)(x[e] & 0x7FFFu));
+  }
+  m = wave_max_u32(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (m) atomicMax(acc, m << 16);
+  }
+}
+
+__global__ void kv_scale_finalize_kernel(uint32_t* acc) {
+  const float amax = __uint_as_float(*acc);
+  *reinterpret_cast<float*>(acc) = div_rn(amax, kFp8Max);
+}
+
+hipError_t launch_fp8_kv_scale_recalibrate(const uint16_t* x, int64_t n, float* scale,
+                                           hipStream_t stream) {
+  uint32_t* acc = reinterpret_cast<uint32_t*>(scale);
+  hipLaunchKernelGGL(kv_amax_clear_kernel, dim3(1), dim3(1), 0, stream, acc);
+  if (n > 0) {
+    const int64_t chunks = n / 8;
+    int64_t grid = (chunks + 256 * kAmaxLoads - 1) / (256 * kAmaxLoads);
+    const int64_t cap = 4 * (int64_t)compute_units();
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(kv_amax_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, n, acc);
+  }
+  hipLaunchKernelGGL(kv_scale_finalize_kernel, dim3(1), dim3(1), 0, stream, acc);
+  return hipGetLastError();
+}
+
+// Quantize-on-write.  A workgroup of 256 threads covers `rpw` token rows of
+// C values with lpr = 256 / rpw threads per row; a thread takes up to
+// kWriteChunks 16-byte chunks of its row (8 values each; chunk i of the
+// thread is chunk lane + i * lpr of the row), issuing every load before the
+// first encode, and the slot lookup after them, so the loads overlap.  Rows
+// whose slot is outside [0, num_slots) are skipped.  The scale comes from an
+// earlier batch, so quotients are not bounded by 448 and are clamped before
+// the conversion.
+constexpr int kWriteChunks = 4;
+
+template <bool kVec>
+__global__ __launch_bounds__(256) void kv_cache_write_kernel(
+    const uint16_t* __restrict__ kv, const int64_t* __restrict__ slots, int64_t T, int64_t C,
+    const float* __restrict__ scale, uint8_t* __restrict__ cache, int64_t num_slots, int rpw) {
+  const int lpr = 256 / rpw;                      // threads per row
+  const int64_t t = (int64_t)blockIdx.x * rpw + threadIdx.x / lpr;
+  if (t >= T) return;
+  const uint16_t* src = kv + t * C;
+  const int64_t lane8 = (int64_t)(threadIdx.x % lpr) * 8;
+  const int64_t step = (int64_t)lpr * 8;
+  for (int64_t col0 = lane8; col0 < C; col0 += step * kWriteChunks) {
+    uint4 v[kWriteChunks];
+#pragma unroll
+    for (int i = 0; i < kWriteChunks; ++i) {
+      const int64_t col = col0 + i * step;
+      if constexpr (kVec) {         // C % 8 == 0: whole 16-byte chunks, aligned
+        v[i] = col < C ? load_once16(src + col) : make_uint4(0, 0, 0, 0);
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (col + e < C) ? (uint32_t)src[col + e] : 0u;
+        v[i] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                          h[6] | (h[7] << 16));
+      }
+    }
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) return;
+    const float s = *scale;
+    const BlockDiv d = block_div(s);
+    uint8_t* dst = cache + slot * C;
+#pragma unroll
+    for (int i = 0; i < kWriteChunks; ++i) {
+      const int64_t col = col0 + i * step;
+      if (col >= C) break;
+      const uint2 c = e4m3_chunk_any<true>(v[i], s, d);
+      if constexpr (kVec) {
+        *reinterpret_cast<uint2*>(dst + col) = c;
+      } else {
+        const uint32_t cw[2] = {c.x, c.y};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < C) dst[col + e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
+      }
+    }
+  }
+}
+
+hipError_t launch_fp8_kv_cache_write(const uint16_t* kv, const int64_t* slots, int64_t T,
+                                     int64_t C, const float* scale, uint8_t* cache,
+                                     int64_t num_slots, hipStream_t stream) {
+  // Threads per row: enough for kWriteChunks chunks each (at most 256).
+  const int64_t chunks = (C + 7) / 8;
+  const int64_t per = (chunks + kWriteChunks - 1) / kWriteChunks;
+  int rpw = 1;                                    // rows per workgroup
+  while (rpw < 256 && 256 / (rpw * 2) >= per) rpw *= 2;
+  const unsigned grid = (unsigned)((T + rpw - 1) / rpw);
+  if (C % 8 == 0)
+    hipLaunchKernelGGL(kv_cache_write_kernel<true>, dim3(grid), dim3(256), 0, stream, kv, slots,
+                       T, C, scale, cache, num_slots, rpw);
+  else
+    hipLaunchKernelGGL(kv_cache_write_kernel<false>, dim3(grid), dim3(256), 0, stream, kv,
+                       slots, T, C, scale, cache, num_slots, rpw);
+  return hipGetLastError();
+}
+
+}  // namespace prr

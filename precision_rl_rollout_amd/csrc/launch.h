@@ -22,6 +22,14 @@ hipError_t launch_w8a8_int8_channel_gemm(const int8_t* A, const float* sa, const
                                          const float* sw, int64_t M, int64_t N, int64_t K,
                                          uint16_t* C, hipStream_t stream);
 
+// FP8 KV cache: recalibration over n = T x C values (the scale word doubles
+// as the reduction's accumulator) and quantize-on-write.
+hipError_t launch_fp8_kv_scale_recalibrate(const uint16_t* x, int64_t n, float* scale,
+                                           hipStream_t stream);
+hipError_t launch_fp8_kv_cache_write(const uint16_t* kv, const int64_t* slots, int64_t T,
+                                     int64_t C, const float* scale, uint8_t* cache,
+                                     int64_t num_slots, hipStream_t stream);
+
 // Compute units of the current device (cached per device; 256 if unknown).
 int compute_units();
 

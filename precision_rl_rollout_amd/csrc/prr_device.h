@@ -115,16 +115,29 @@ __device__ __forceinline__ uint32_t cvt_e4m3x4(float q0, float q1, float q2, flo
   return (uint32_t)d;
 }
 
+// Quotient clamped to [-448, 448] (sign of zero kept): the saturating RNE
+// code is unchanged, and the conversion then never sees |v| > 464.  Needed
+// where a scale does not bound the quotients (a KV-cache scale calibrated
+// on an earlier batch); block scales do bound them.
+__device__ __forceinline__ float clamp448(float v) {
+  return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+}
+
 // Eight bf16 values (one 16-byte chunk) -> eight e4m3 codes (8 bytes).
-template <bool kTiny>
+template <bool kTiny, bool kClamp = false>
 __device__ __forceinline__ uint2 e4m3_chunk(uint4 w, const BlockDiv& d) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t out[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t w0 = ws[2 * h], w1 = ws[2 * h + 1];
-    out[h] = cvt_e4m3x4(div_block<kTiny>(bf16_lo(w0), d), div_block<kTiny>(bf16_hi(w0), d),
-                        div_block<kTiny>(bf16_lo(w1), d), div_block<kTiny>(bf16_hi(w1), d));
+    float q[4] = {div_block<kTiny>(bf16_lo(w0), d), div_block<kTiny>(bf16_hi(w0), d),
+                  div_block<kTiny>(bf16_lo(w1), d), div_block<kTiny>(bf16_hi(w1), d)};
+    if constexpr (kClamp) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] = clamp448(q[e]);
+    }
+    out[h] = cvt_e4m3x4(q[0], q[1], q[2], q[3]);
   }
   return make_uint2(out[0], out[1]);
 }
@@ -144,9 +157,10 @@ __device__ __forceinline__ uint2 e4m3_zero_chunk(uint4 w) {
 }
 
 // e4m3 chunk for any block: dispatch on the block-uniform scale class.
+template <bool kClamp = false>
 __device__ __forceinline__ uint2 e4m3_chunk_any(uint4 w, float s, const BlockDiv& d) {
   if (s == 0.0f) return e4m3_zero_chunk(w);
-  return d.tiny ? e4m3_chunk<true>(w, d) : e4m3_chunk<false>(w, d);
+  return d.tiny ? e4m3_chunk<true, kClamp>(w, d) : e4m3_chunk<false, kClamp>(w, d);
 }
 
 // Four bytes packed little-endian into one word.

@@ -32,7 +32,13 @@ _STREAMS = {
     "A": 1, "W": 2, "A_down": 3, "W_down": 4, "A_cols": 5, "A_down_cols": 6,
     "q": 11, "k": 12, "v": 13, "o": 14, "gate": 15, "up": 16, "down": 17,
     "special": 21,
+    "kv_K": 31, "kv_V": 32, "kv_K_cols": 33, "kv_V_cols": 34, "kv_slots": 35,
 }
+
+# FP8 KV cache of a 32B-class layer: 8 KV heads of 128 (C = 1024 per token),
+# a prefill batch of 16,384 tokens written into a cache of 65,536 slots in
+# 16-slot pages.
+KV_32B = dict(T=16384, C=1024, num_slots=65536, page=16)
 
 # Layer shapes as Wt [N, K] of one 32B-class decoder layer (hidden 5120,
 # 8 KV heads of 128, FFN 27648).
@@ -55,6 +61,7 @@ CONFIGS = {
     "decode32b_sweep": dict(gemms=[(m, 27648, 5120, True) for m in DECODE_SWEEP_M]),
     "prefill32b": dict(gemms=[(8192, 27648, 5120, True), (8192, 5120, 27648, True)]),
     "stack32b_requant": dict(layers=STACK_32B, gemm_m=64),
+    "kv32b_prefill": dict(kv=KV_32B),
 }
 
 
@@ -130,3 +137,26 @@ def special_values_bf16() -> np.ndarray:
     allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     exp = (allbits >> np.uint16(7)) & np.uint16(0xFF)
     return allbits[exp != 0xFF]
+
+
+def kv_rows(T: int, C: int, seed: int = 0, which: str = "K") -> np.ndarray:
+    """New K or V rows [T, C] bf16 bits: N(0, 1) with x20 outlier channels
+    (the activation recipe; projection outputs carry outlier channels)."""
+    return activation(T, C, seed, True, "kv_" + which)
+
+
+def kv_slot_mapping(T: int, num_slots: int, page: int = 16, seed: int = 0,
+                    pad_every: int = 0) -> np.ndarray:
+    """int64 [T]: token t goes to slot page_order[t // page] * page + t % page
+    for a random order of the cache's pages (paged-cache style); with
+    pad_every > 0, every pad_every-th token is a padding token (slot -1)."""
+    pages = num_slots // page
+    need = -(-T // page)
+    if need > pages:
+        raise ValueError("cache too small for T tokens")
+    order = _rng(seed, "kv_slots").permutation(pages)[:need]
+    t = np.arange(T, dtype=np.int64)
+    slots = order[t // page].astype(np.int64) * page + t % page
+    if pad_every > 0:
+        slots[::pad_every] = -1
+    return slots

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     names = set(_declared())
     assert names == {"fp8_weight_block_quant", "fp8_act_token_quant", "w8a8_block_gemm",
                      "int8_weight_channel_quant", "int8_act_token_quant",
-                     "w8a8_int8_channel_gemm", "prr_status_string", "prr_abi_version"}
+                     "w8a8_int8_channel_gemm", "fp8_kv_scale_recalibrate",
+                     "fp8_kv_cache_write", "prr_status_string", "prr_abi_version"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -49,7 +50,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.abi_version() == 1
+    assert binding.abi_version() == 2
     names = [binding.status_string(s) for s in range(7)]
     assert names == ["PRR_OK", "PRR_ERR_INVALID_ARG", "PRR_ERR_UNSUPPORTED_SHAPE",
                      "PRR_ERR_MISALIGNED", "PRR_ERR_NO_DEVICE", "PRR_ERR_UNSUPPORTED_DEVICE",
@@ -122,3 +123,37 @@ def test_no_device_is_reported(fn):
     else:
         st = binding.call(fn, FAKE, 16, 256, FAKE, FAKE, None)
     assert st == NO_DEVICE
+
+
+def test_kv_recalibrate_argument_checks():
+    c = lambda *a: binding.call("fp8_kv_scale_recalibrate", *a)
+    assert c(FAKE, -1, 8, FAKE, None) == INVALID
+    assert c(FAKE, 8, 2 ** 31, FAKE, None) == INVALID
+    assert c(None, 4, 8, FAKE, None) == INVALID
+    assert c(FAKE, 4, 8, None, None) == INVALID
+    assert c(ODD, 4, 8, FAKE, None) == MISALIGNED
+    assert c(FAKE, 4, 8, ODD, None) == MISALIGNED
+    # an empty tensor still writes its scale (0): the output pointer is needed
+    assert c(None, 0, 8, None, None) == INVALID
+
+
+def test_kv_cache_write_argument_checks():
+    c = lambda *a: binding.call("fp8_kv_cache_write", *a)
+    assert c(FAKE, FAKE, -1, 8, FAKE, FAKE, 4, None) == INVALID
+    assert c(FAKE, FAKE, 4, 8, FAKE, FAKE, -4, None) == INVALID
+    for i in (0, 1, 4, 5):
+        args = [FAKE, FAKE, 4, 8, FAKE, FAKE, 16, None]
+        args[i] = None
+        assert c(*args) == INVALID
+        args[i] = ODD
+        assert c(*args) == MISALIGNED
+    # nothing to write: no pointer is needed
+    assert c(None, None, 0, 8, None, None, 16, None) == OK
+    assert c(None, None, 4, 0, None, None, 16, None) == OK
+    assert c(None, None, 4, 8, None, None, 0, None) == OK
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="needs a process without a GPU")
+def test_kv_no_device_is_reported():
+    assert binding.call("fp8_kv_scale_recalibrate", FAKE, 4, 8, FAKE, None) == NO_DEVICE
+    assert binding.call("fp8_kv_cache_write", FAKE, FAKE, 4, 8, FAKE, FAKE, 16, None) == NO_DEVICE

@@ -1,0 +1,126 @@
+"""GPU parity of the FP8 KV-cache calls against the oracle, bit for bit.
+
+* fp8_kv_scale_recalibrate: the scale's bits, on ragged sizes (tails that are
+  not whole 16-byte chunks), an all-zero and an empty tensor, values spread
+  so the maximum sits in different workgroups, and the full 32B-layer size;
+* fp8_kv_cache_write: every byte of the cache after the write, which covers
+  the codes of written rows and the untouched rows (filled with a canary
+  first), with padding and out-of-range slots, ragged C (per-element path),
+  saturation beyond the calibrated range, a zero scale, and the full
+  32B-layer prefill write.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kv
+from precision_rl_rollout_amd import binding, workloads
+from tests.gpu_util import announce, bits_to_dev, host
+
+pytestmark = pytest.mark.gpu
+
+CANARY = 0x5A
+
+
+def _scale_gpu(xbits):
+    return binding.fp8_kv_scale_recalibrate(bits_to_dev(xbits))
+
+
+def _f32_bits(v) -> int:
+    return int(np.asarray(v, dtype=np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("T,C", [(1, 1), (1, 7), (3, 5), (7, 40), (128, 1024), (333, 1001),
+                                 (4096, 1024)])
+def test_recalibrate_matches_oracle(T, C):
+    for seed in (0, 1):
+        xb = workloads.kv_rows(T, C, seed, "K")
+        announce(f"fp8_kv_scale_recalibrate T{T} C{C} seed{seed}")
+        got = host(_scale_gpu(xb))
+        assert _f32_bits(got[0]) == _f32_bits(kv.kv_scale(xb))
+
+
+def test_recalibrate_max_in_every_position():
+    # one large value, moved through the first chunk, a middle chunk and the
+    # ragged tail: every workgroup / tail path must see it
+    T, C = 97, 123
+    base = workloads.kv_rows(T, C, 4, "V")
+    for pos in (0, 5, 8, T * C // 2, T * C - 8, T * C - 1):
+        xb = base.copy().ravel()
+        xb[pos] = 0xC3A0                        # -320.0
+        xb = xb.reshape(T, C)
+        announce(f"fp8_kv_scale_recalibrate max at {pos}")
+        assert _f32_bits(host(_scale_gpu(xb))[0]) == _f32_bits(kv.kv_scale(xb))
+
+
+def test_recalibrate_zero_and_empty():
+    announce("fp8_kv_scale_recalibrate zero / empty")
+    z = np.zeros((5, 64), dtype=np.uint16)
+    z[2, 3] = 0x8000
+    assert _f32_bits(host(_scale_gpu(z))[0]) == 0
+    s = torch.full((1,), 7.0, device="cuda:0")
+    e = torch.empty((0, 64), dtype=torch.int16, device="cuda:0")
+    binding.fp8_kv_scale_recalibrate(e, out=s)
+    torch.cuda.synchronize()
+    assert _f32_bits(host(s)[0]) == 0
+
+
+def _write_case(T, C, num_slots, seed, pad_every=0, extra_slots=None, scale=None, xb=None):
+    if xb is None:
+        xb = workloads.kv_rows(T, C, seed, "V")
+    slots = workloads.kv_slot_mapping(T, num_slots, 16, seed, pad_every)
+    if extra_slots is not None:
+        for t, sl in extra_slots.items():
+            slots[t] = sl
+    s = kv.kv_scale(xb) if scale is None else np.float32(scale)
+    cache0 = np.full((num_slots, C), CANARY, dtype=np.uint8)
+    want = kv.kv_cache_write(cache0, xb, slots, s)
+    cache = torch.from_numpy(cache0).cuda()
+    sd = torch.tensor([s], dtype=torch.float32, device="cuda:0")
+    binding.fp8_kv_cache_write(bits_to_dev(xb), torch.from_numpy(slots).cuda(), sd, cache)
+    return host(cache), want
+
+
+@pytest.mark.parametrize("T,C,num_slots,pad", [(1, 8, 16, 0), (7, 40, 64, 3), (128, 1024, 512, 0),
+                                               (333, 1001, 1024, 5), (100, 3, 2048, 0),
+                                               (1000, 256, 4096, 9)])
+def test_cache_write_matches_oracle(T, C, num_slots, pad):
+    announce(f"fp8_kv_cache_write T{T} C{C} slots{num_slots} pad{pad}")
+    got, want = _write_case(T, C, num_slots, seed=T + C, pad_every=pad)
+    assert np.array_equal(got, want)
+
+
+def test_cache_write_skips_out_of_range_slots():
+    announce("fp8_kv_cache_write out-of-range slots")
+    got, want = _write_case(40, 64, 128, seed=3,
+                            extra_slots={0: -7, 5: 128, 6: 2 ** 40, 39: -(2 ** 62)})
+    assert np.array_equal(got, want)
+
+
+def test_cache_write_saturates_and_zero_scale():
+    announce("fp8_kv_cache_write saturation / zero scale")
+    xb = workloads.kv_rows(64, 128, 8, "K")
+    small = np.float32(kv.kv_scale(xb) / 16)    # calibration range 16x too small
+    got, want = _write_case(64, 128, 256, seed=8, scale=small, xb=xb)
+    assert np.array_equal(got, want)
+    assert np.count_nonzero((got == 0x7E) | (got == 0xFE)) > 0
+    got, want = _write_case(64, 128, 256, seed=8, scale=0.0, xb=xb)
+    assert np.array_equal(got, want)
+
+
+def test_full_32b_prefill_write():
+    cfg = workloads.KV_32B
+    T, C, S = cfg["T"], cfg["C"], cfg["num_slots"]
+    xb = workloads.kv_rows(T, C, 0, "K")
+    announce(f"fp8_kv_scale_recalibrate + fp8_kv_cache_write full T{T} C{C} slots{S}")
+    xd = bits_to_dev(xb)
+    sd = binding.fp8_kv_scale_recalibrate(xd)
+    s = kv.kv_scale(xb)
+    assert _f32_bits(host(sd)[0]) == _f32_bits(s)
+    slots = workloads.kv_slot_mapping(T, S, cfg["page"], 0)
+    cache0 = np.full((S, C), CANARY, dtype=np.uint8)
+    want = kv.kv_cache_write(cache0, xb, slots, s)
+    cache = torch.from_numpy(cache0).cuda()
+    binding.fp8_kv_cache_write(xd, torch.from_numpy(slots).cuda(), sd, cache)
+    assert np.array_equal(host(cache), want)

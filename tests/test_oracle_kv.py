@@ -57,6 +57,13 @@ def test_all_zero_tensor():
     assert np.array_equal(codes, want)
 
 
+def test_zero_scale_writes_signed_zeros_of_nonzero_rows():
+    xb = _bits((3, 10), seed=9)
+    codes = kv.kv_encode_rows(xb, np.float32(0.0))
+    x = pins.f32_of_bf16(xb)
+    assert np.array_equal(codes, np.where(np.signbit(x), 0x80, 0x00).astype(np.uint8))
+
+
 def test_values_beyond_calibration_saturate():
     cal = _bits((16, 64), seed=11)
     s = kv.kv_scale(cal)
