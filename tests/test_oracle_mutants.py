@@ -77,3 +77,56 @@ def test_quantizer_mutants_are_caught():
     assert np.any((bad & 0x7F) != (codes & 0x7F))
     recip = _quant_reciprocal(w)
     assert not np.array_equal(recip, codes)
+
+
+# ----------------------------------------------------------------- KV cache
+from oracle import kv as _kv                                     # noqa: E402
+
+
+def _kv_write_ignoring_mapping(cache, x_bits, slots, s):
+    """Token t written to row t instead of row slot_mapping[t]."""
+    out = np.array(cache, copy=True)
+    codes = _kv.kv_encode_rows(x_bits, s)
+    n = min(len(slots), out.shape[0])
+    out[:n] = codes[:n]
+    return out
+
+
+def _kv_write_unclamped_slots(cache, x_bits, slots, s):
+    """Negative slots taken as Python indices from the end of the cache."""
+    out = np.array(cache, copy=True)
+    codes = _kv.kv_encode_rows(x_bits, s)
+    for t, sl in enumerate(np.asarray(slots)):
+        if sl < out.shape[0]:
+            out[sl] = codes[t]
+    return out
+
+
+def _kv_zero_scale_encodes_x(x_bits, s):
+    """s == 0 handled by encoding x itself (the weight-block shortcut)."""
+    return e4m3.encode(quant.bf16_to_f32(x_bits))
+
+
+def _kv_scatter_check(write):
+    xb = workloads.bf16_normal((4, 3), 1.0, 2, "special")
+    s = _kv.kv_scale(xb)
+    cache = np.full((5, 3), 0x5A, dtype=np.uint8)
+    slots = np.array([3, -1, 0, 7])
+    x = pins.f32_of_bf16(xb)
+    want = cache.copy()
+    q = pins.e4m3_nearest((x / np.float64(s)).astype(np.float32)).reshape(4, 3)
+    want[3], want[0] = q[0], q[2]
+    return np.array_equal(write(cache, xb, slots, s), want)
+
+
+def test_kv_write_mutants_fail_the_scatter_pin():
+    assert _kv_scatter_check(_kv.kv_cache_write)
+    assert not _kv_scatter_check(_kv_write_ignoring_mapping)
+    assert not _kv_scatter_check(_kv_write_unclamped_slots)
+
+
+def test_kv_zero_scale_mutant_fails_the_signed_zero_pin():
+    xb = workloads.bf16_normal((3, 10), 1.0, 9, "special")
+    want = np.where(np.signbit(pins.f32_of_bf16(xb)), 0x80, 0x00).astype(np.uint8)
+    assert np.array_equal(_kv.kv_encode_rows(xb, np.float32(0)), want)
+    assert not np.array_equal(_kv_zero_scale_encodes_x(xb, np.float32(0)), want)
