@@ -25,9 +25,10 @@
 //    bytes, half lines, which held the stream near 4.8 TB/s, and the
 //    register ring limited how much K a wave could hold.)  Tasks past the
 //    end load at out-of-range offsets: no traffic, zeros, no branch.
-//  * The 8 partial sums of a strip meet in LDS; MT waves add them, apply
-//    the epilogue and store bf16.  The barriers order LDS only, so they do
-//    not drain the loads in flight.
+//  * The 8 partial sums of a strip meet in LDS (two buffers, alternate
+//    strips, one barrier per strip); MT waves add them, apply the epilogue
+//    and store bf16.  The barrier orders LDS only, so it does not drain the
+//    loads in flight.
 //
 // FP8: per K block, C += sa[m, kb] * sw[n / 128, kb] * MFMA(Wq, Aq) (one
 // v_mfma_f32_16x16x128_f8f6f4 per block, zero accumulator).  INT8: the
@@ -41,7 +42,7 @@
 namespace prr {
 
 constexpr int kDecodeWaves = 8;
-constexpr int kDecodeRing = 6;       // LDS slots per wave (5 tasks in flight)
+constexpr int kDecodeRing = 4;       // LDS slots per wave (3 tasks in flight)
 constexpr int kLdsBytes = 163840;    // LDS per workgroup on gfx950
 
 // One ring slot: a task's weight block (row r at bytes [128 r, 128 r + 128),
@@ -88,12 +89,13 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
     }
 
   // Dynamic LDS: the FP8 activation scales of all rows, transposed to
-  // [K block][row] (kept for the whole kernel), then the partial-sum
-  // exchange buffer.
+  // [K block][row] (kept for the whole kernel), then two partial-sum
+  // exchange buffers used by alternate strips.
   extern __shared__ float lds_dyn[];
   constexpr int kRows = MT * 16;
   float* lsa = lds_dyn;
   float* lred = lds_dyn + (kInt8 ? 0 : kRows * KB);
+  constexpr int kRedFloats = kDecodeWaves * MT * 4 * 64;
   if constexpr (!kInt8) {
     for (int e = threadIdx.x; e < kRows * KB; e += blockDim.x) {
       const int m = e / KB, kb = e - m * KB;
@@ -153,8 +155,12 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
 #pragma unroll
   for (int q = 0; q < R - 1; ++q) load_task(q);
 
-  auto red = reinterpret_cast<float (*)[MT][4][64]>(lred);      // [wave][mt][r][lane]
   for (int i = 0; i < my_n; ++i) {
+    // [wave][mt][r][lane], alternating between the two buffers: strip i's
+    // buffer is written again at strip i + 2, after every wave has passed
+    // strip i + 1's barrier (whose release fence completes the reads of
+    // strip i), so one barrier per strip suffices.
+    auto red = reinterpret_cast<float (*)[MT][4][64]>(lred + (i & 1) * kRedFloats);
     const int n0 = strip_n0(i);
     float accf[MT][4];
     v4i acci[MT];
@@ -244,7 +250,6 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
       }
       store4(C, M, N, m, n, v);
     }
-    lds_barrier();
   }
   // The trailing (out-of-range) loads land before the LDS is released.
   wait_vmcnt<0>();
@@ -278,7 +283,7 @@ static bool launch_decode_mt(const uint8_t* A, const float* sa, const uint8_t* W
   const int nstrips = (int)((N + 15) / 16);
   const int cus = compute_units();
   const int grid = nstrips < cus ? nstrips : cus;
-  const size_t lds = ((size_t)kDecodeWaves * MT * 4 * 64 + (kInt8 ? 0 : (size_t)MT * 16 * KB)) *
+  const size_t lds = ((size_t)2 * kDecodeWaves * MT * 4 * 64 + (kInt8 ? 0 : (size_t)MT * 16 * KB)) *
                      sizeof(float);
   if (lds + sizeof(DecodeSlot) * kDecodeWaves * kDecodeRing > (size_t)kLdsBytes) return false;
 #define PRR_DECODE_P(PV)                                                                  \
