@@ -26,6 +26,9 @@ What it computes, with the passage each part follows:
   recalibrated every step, and quantize-on-write of token rows into cache
   slots (FP8-RL abstract, item (ii): FP8 KV cache with per-step QKV scale
   recalibration; granularity and write rule are readings, listed there).
+* ``oracle.gemm`` -- also the mixture-of-experts grouping of the FP8 layer:
+  token rows sorted by expert, each group multiplied by its expert's weight
+  (FP8-RL abstract: dense and MoE models).
 * ``oracle.gemm`` -- the W8A8 linear layer: fp64 accumulation over the
   exactly decoded 8-bit operands with the per-K-block (FP8) or per-row and
   per-channel (INT8) scales, rounded once to bf16.

@@ -118,3 +118,24 @@ def rel_frobenius(c_bits, ref_bits) -> float:
     den = np.linalg.norm(r)
     num = np.linalg.norm(c - r)
     return float(num / den) if den > 0 else float(num)
+
+
+def w8a8_block_gemm_grouped(aq, sa, wq, sw, offsets) -> np.ndarray:
+    """Mixture-of-experts form of the FP8 linear layer (FP8-RL, abstract:
+    the FP8 stack covers dense and MoE models).  The rows of ``Aq [M, K]``
+    (and ``sa [M, K/128]``) are grouped by expert: rows
+    ``offsets[e] .. offsets[e+1] - 1`` go to expert ``e``, whose weight is
+    ``Wq[e] [N, K]`` with scales ``sw[e] [N/128, K/128]``.  Each group is the
+    dense layer above with its own expert's weight; bf16 bits [M, N].  Rows
+    outside every group (before offsets[0] or from offsets[E] on) are not
+    written (zero here)."""
+    offs = np.asarray(offsets, dtype=np.int64)
+    E = len(offs) - 1
+    M = np.asarray(aq).shape[0]
+    N = np.asarray(wq).shape[1]
+    out = np.zeros((M, N), dtype=np.uint16)
+    for e in range(E):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        if r1 > r0:
+            out[r0:r1] = round_bf16(w8a8_block_gemm(aq[r0:r1], sa[r0:r1], wq[e], sw[e]))
+    return out
