@@ -76,6 +76,7 @@ KERNEL_SOURCES = {
     # M <= 64 runs the persistent decode kernel.
     "w8a8_block_gemm@decode7b_upgate": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
     "w8a8_int8_channel_gemm@decode7b_upgate": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
+    "w8a8_block_gemm_grouped": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
     # M = 8192 runs the many-token kernel.
     "w8a8_block_gemm@prefill32b": ["gemm_prefill.hip", "mfma.h", "prr_device.h"],
     "w8a8_int8_channel_gemm@prefill32b": ["gemm_prefill.hip", "mfma.h", "prr_device.h"],
@@ -430,6 +431,101 @@ def run_kv32b(args, torch, B, W):
     return line
 
 
+def grouped_bytes(counts, N, K):
+    """Rows and their scales, the weights and scales of every expert that
+    has rows, the bf16 output and the row offsets."""
+    counts = np.asarray(counts)
+    M, E, KB = int(counts.sum()), len(counts), K // 128
+    active = int(np.count_nonzero(counts))
+    return (M * K + 4 * M * KB + active * (N * K + 4 * cdiv(N, 128) * KB) + 2 * M * N
+            + 8 * (E + 1))
+
+
+def run_moe_decode(args, torch, B, W):
+    """One decode step of a mixture-of-experts layer (128 experts, top-8
+    routing of 128 tokens, expert N = 1536, K = 2048): FP8 block quant of
+    every expert's weight, FP8 group quant of the routed rows, and the
+    grouped W8A8 GEMM over all experts in one launch."""
+    cfg = W.MOE_DECODE
+    E, N, K = cfg["E"], cfg["N"], cfg["K"]
+    counts = W.moe_routing(cfg["tokens"], E, cfg["topk"], seed=0)
+    p = W.moe_problem(counts, N, K, seed=0)
+    M, KB, NB = p["M"], K // 128, cdiv(N, 128)
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(p["A"].view(np.int16)).to(dev)
+    Wt = torch.from_numpy(p["Wt"].reshape(E * N, K).view(np.int16)).to(dev)
+    offsets = torch.from_numpy(p["offsets"]).to(dev)
+    hint = int(counts.max())
+    wq = torch.empty((E * N, K), dtype=torch.uint8, device=dev)
+    sw = torch.empty((E * NB, KB), dtype=torch.float32, device=dev)
+    aq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, KB), dtype=torch.float32, device=dev)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    work = {
+        "fp8_weight_block_quant": quant_bytes(E * N, K, E * NB * KB),
+        "fp8_act_token_quant": quant_bytes(M, K, M * KB),
+        "w8a8_block_gemm_grouped": grouped_bytes(counts, N, K),
+    }
+    step_bytes = sum(work.values())
+
+    def step(timer=None):
+        t = timer.run if timer else (lambda _n, f: f())
+        t("fp8_weight_block_quant", lambda: B.fp8_weight_block_quant(Wt, out=wq, scale=sw))
+        t("fp8_act_token_quant", lambda: B.fp8_act_token_quant(A, out=aq, scale=sa))
+        t("w8a8_block_gemm_grouped", lambda: B.w8a8_block_gemm_grouped(
+            aq, sa, wq.view(E, N, K), sw.view(E, NB, KB), offsets, hint, out=c))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    us = timer.avg_us()
+    kernels = {k: {"us": round(us[k], 2), "algorithmic_bytes": work[k],
+                   "GB/s": round(work[k] / us[k] / 1e3, 1)} for k in work}
+    dom = max(us, key=us.get)
+    achieved = work[dom] / us[dom] / 1e3
+    line = {
+        "metric": METRIC, "value": round(step_bytes / dt / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
+        "config": {"workload": "moe_decode", "experts": E, "topk": cfg["topk"],
+                   "tokens": cfg["tokens"], "rows": M, "N": N, "K": K,
+                   "rows_per_expert": [int(counts.min()), int(counts.max())],
+                   "step": "fp8 W block quant (all experts) + fp8 A group quant + grouped "
+                           "fp8 W8A8 GEMM",
+                   "step_algorithmic_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(dom, "moe_decode")},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import gemm, quant
+        ns = E                                  # the whole step (about 10 s on 16 cores)
+        sub = counts[:ns]
+        r1 = int(sub.sum())
+        t0 = time.perf_counter()
+        wqs = [quant.fp8_weight_block_quant(p["Wt"][e]) for e in range(ns)]
+        aqs, sas = quant.fp8_act_token_quant(p["A"][:r1])
+        gemm.w8a8_block_gemm_grouped(aqs, sas, np.stack([w for w, _ in wqs]),
+                                     np.stack([x for _, x in wqs]), p["offsets"][:ns + 1])
+        ct = time.perf_counter() - t0
+        sample = (quant_bytes(ns * N, K, ns * NB * KB) + quant_bytes(r1, K, r1 * KB)
+                  + grouped_bytes(sub, N, K))
+        line["cpu_baseline"] = {"value": round(sample / ct / 1e9, 4), "unit": "GB/s",
+                                "cores": cpu_threads(), "kind": "oracle", "seconds": round(ct, 2),
+                                "sample": f"one whole step: weight quant of all {ns} experts, "
+                                          f"quant of the {r1} routed rows, the grouped GEMM"}
+    return line
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -437,7 +533,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode7b_upgate",
                     choices=["decode7b_upgate", "decode32b_sweep", "prefill32b", "stack32b_requant",
-                             "kv32b_prefill"])
+                             "kv32b_prefill", "moe_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (outside the "
@@ -465,7 +561,7 @@ def main(argv=None):
         del src, dst
     run = {"decode7b_upgate": run_decode7b, "decode32b_sweep": run_decode32b,
            "prefill32b": run_prefill32b, "stack32b_requant": run_stack32b,
-           "kv32b_prefill": run_kv32b}[args.workload]
+           "kv32b_prefill": run_kv32b, "moe_decode": run_moe_decode}[args.workload]
     line = run(args, torch, B, W)
     print(json.dumps(line), flush=True)
     return 0

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PRR_ABI_VERSION 2
+#define PRR_ABI_VERSION 3
 
 typedef enum prr_status {
   PRR_OK = 0,
@@ -170,6 +170,35 @@ prr_status w8a8_int8_channel_gemm(const int8_t* a_i8, const float* a_scale,
                                   const int8_t* w_i8, const float* w_scale,
                                   int64_t M, int64_t N, int64_t K,
                                   uint16_t* c_bf16, hipStream_t stream);
+
+/*
+ * w8a8_block_gemm_grouped -- the FP8 W8A8 linear layer of a mixture of
+ * experts (FP8-RL, abstract: the FP8 rollout stack covers dense and MoE
+ * models), for decode-sized groups: one launch for every expert.
+ *   a_fp8 [M, K], a_scale [M, K/128]  token rows sorted by expert, as
+ *                       written by fp8_act_token_quant.
+ *   w_fp8 [E, N, K], w_scale [E, ceil(N/128), K/128]  each expert's weight
+ *                       as written by fp8_weight_block_quant.
+ *   expert_offsets [E + 1] int64, device memory: rows offsets[e] ..
+ *                       offsets[e+1] - 1 go to expert e (non-decreasing;
+ *                       values are clamped into [0, M], so rows before
+ *                       offsets[0] or from offsets[E] on are not written).
+ *   max_rows_per_expert a bound on the rows of any expert, used only to
+ *                       choose the register tiling (<= 16, <= 32, else 64
+ *                       rows); groups above 64 rows are processed in 64-row
+ *                       chunks, each of which reads the expert's weight.
+ *   c_bf16 out [M, N]   each group's rows are w8a8_block_gemm of the group
+ *                       with its expert's weight (same definition and
+ *                       tolerance).
+ *   E, M, N >= 0; K > 0 with K % 128 == 0 and K <= 6144 (PRR_ERR_
+ *   UNSUPPORTED_SHAPE beyond: the activations of a 64-row chunk must fit
+ *   in registers; 8192 when max_rows_per_expert <= 32).
+ */
+prr_status w8a8_block_gemm_grouped(const uint8_t* a_fp8, const float* a_scale,
+                                   const uint8_t* w_fp8, const float* w_scale,
+                                   const int64_t* expert_offsets, int64_t E, int64_t M,
+                                   int64_t N, int64_t K, int64_t max_rows_per_expert,
+                                   uint16_t* c_bf16, hipStream_t stream);
 
 /*
  * fp8_kv_scale_recalibrate -- per-step recalibration of one FP8 KV-cache

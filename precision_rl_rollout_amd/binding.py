@@ -32,11 +32,16 @@ _SIGNATURES = {
     "int8_weight_channel_quant": [_P, _I64, _I64, _P, _P, _P],
     "int8_act_token_quant": [_P, _I64, _I64, _P, _P, _P],
     "w8a8_int8_channel_gemm": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P],
+    "w8a8_block_gemm_grouped": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P],
     "fp8_kv_scale_recalibrate": [_P, _I64, _I64, _P, _P],
     "fp8_kv_cache_write": [_P, _P, _I64, _I64, _P, _P, _I64, _P],
 }
 
 _lib = None
+
+# PRR_ABI_VERSION of the signatures below; a library of another version is
+# refused at load time.
+ABI_VERSION = 3
 
 
 class PrrError(RuntimeError):
@@ -62,6 +67,9 @@ def load() -> ctypes.CDLL:
         lib.prr_status_string.restype = ctypes.c_char_p
         lib.prr_abi_version.argtypes = []
         lib.prr_abi_version.restype = ctypes.c_int
+        if lib.prr_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {lib.prr_abi_version()}, the "
+                               f"binding expects {ABI_VERSION}; rebuild it")
         _lib = lib
     return _lib
 
@@ -219,3 +227,24 @@ def fp8_kv_cache_write(kv: torch.Tensor, slot_mapping: torch.Tensor, scale: torc
            load().fp8_kv_cache_write(_ptr(kv), _ptr(slot_mapping), T, C, scale.data_ptr(),
                                      _ptr(cache), cache.shape[0], _stream(kv)))
     return cache
+
+
+def w8a8_block_gemm_grouped(aq: torch.Tensor, sa: torch.Tensor, wq: torch.Tensor,
+                            sw: torch.Tensor, offsets: torch.Tensor, max_rows_per_expert: int,
+                            out=None):
+    """Rows of aq [M, K] (uint8, sorted by expert) x experts' wq [E, N, K]
+    (uint8) with sa [M, K/128], sw [E, ceil(N/128), K/128] and
+    offsets int64 [E + 1] (device) -> C bf16 [M, N]."""
+    M, K = aq.shape
+    E, N = wq.shape[0], wq.shape[1]
+    _operand(aq, torch.uint8, (M, K), "aq")
+    _operand(sa, torch.float32, (M, _cdiv(K, 128)), "sa")
+    _operand(wq, torch.uint8, (E, N, K), "wq")
+    _operand(sw, torch.float32, (E, _cdiv(N, 128), _cdiv(K, 128)), "sw")
+    _operand(offsets, torch.int64, (E + 1,), "offsets")
+    c = _out(out, torch.bfloat16, (M, N), aq, "out")
+    _check("w8a8_block_gemm_grouped",
+           load().w8a8_block_gemm_grouped(_ptr(aq), _ptr(sa), _ptr(wq), _ptr(sw), _ptr(offsets),
+                                          E, M, N, K, int(max_rows_per_expert), _ptr(c),
+                                          _stream(aq)))
+    return c

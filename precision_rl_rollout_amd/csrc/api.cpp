@@ -159,6 +159,24 @@ prr_status w8a8_int8_channel_gemm(const int8_t* a_i8, const float* a_scale, cons
       prr::launch_w8a8_int8_channel_gemm(a_i8, a_scale, w_i8, w_scale, M, N, K, c_bf16, stream));
 }
 
+prr_status w8a8_block_gemm_grouped(const uint8_t* a_fp8, const float* a_scale,
+                                   const uint8_t* w_fp8, const float* w_scale,
+                                   const int64_t* expert_offsets, int64_t E, int64_t M, int64_t N,
+                                   int64_t K, int64_t max_rows_per_expert, uint16_t* c_bf16,
+                                   hipStream_t stream) {
+  PRR_TRY(check_dims(E, M, N));
+  PRR_TRY(check_dims(K, max_rows_per_expert));
+  if (K % 128 != 0 || K == 0) return PRR_ERR_UNSUPPORTED_SHAPE;
+  if (E == 0 || M == 0 || N == 0) return PRR_OK;
+  PRR_TRY(check_ptrs({a_fp8, a_scale, w_fp8, w_scale, expert_offsets, c_bf16}));
+  PRR_TRY(check_device());
+  hipError_t err = hipSuccess;
+  if (!prr::launch_gemm_grouped(a_fp8, a_scale, w_fp8, w_scale, expert_offsets, E, M, N, K,
+                                max_rows_per_expert, c_bf16, stream, &err))
+    return PRR_ERR_UNSUPPORTED_SHAPE;
+  return from_hip(err);
+}
+
 prr_status fp8_kv_scale_recalibrate(const uint16_t* x_bf16, int64_t T, int64_t C, float* scale,
                                     hipStream_t stream) {
   PRR_TRY(check_dims(T, C));

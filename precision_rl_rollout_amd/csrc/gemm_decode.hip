@@ -60,13 +60,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(n) : "memory");
 }
 
-// P: K blocks of the wave's piece held in registers (>= ceil(K/128 / 8)).
+typedef DecodeSlot DecodeRing[kDecodeWaves][kDecodeRing];
+
+// One segment: the M (<= MT * 16) activation rows at A against the strips
+// first, first + step, ... (n_strips of them) of the weight W [N, K]; the
+// output rows go to C [M, N].  P: K blocks of the wave's piece held in
+// registers (>= ceil(K/128 / 8)).  Every wave of the workgroup calls it with
+// the same arguments; it starts with a barrier (a previous segment's waves
+// may still read the LDS it rewrites) and ends with its loads drained.
 template <int MT, int P, bool kInt8>
-__global__ __launch_bounds__(512) void gemm_decode_kernel(
+__device__ __forceinline__ void decode_segment(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
-    const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int nstrips) {
+    const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int first,
+    int step, int n_strips, DecodeRing& ring, float* lds_dyn) {
   constexpr int R = kDecodeRing;
-  __shared__ __align__(16) DecodeSlot ring[kDecodeWaves][R];
+  lds_barrier();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -89,9 +97,8 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
     }
 
   // Dynamic LDS: the FP8 activation scales of all rows, transposed to
-  // [K block][row] (kept for the whole kernel), then two partial-sum
+  // [K block][row] (kept for the whole segment), then two partial-sum
   // exchange buffers used by alternate strips.
-  extern __shared__ float lds_dyn[];
   constexpr int kRows = MT * 16;
   float* lsa = lds_dyn;
   float* lred = lds_dyn + (kInt8 ? 0 : kRows * KB);
@@ -109,14 +116,11 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
     for (int mt = 0; mt < MT; ++mt) sa_row[mt] = (mt * 16 + r16 < M) ? sa[mt * 16 + r16] : 0.f;
   }
 
-  const int G = gridDim.x;
-  // Strips of this workgroup (uniform; the integer division runs on the
-  // vector unit, so the compiler needs telling).
-  const int my_n = __builtin_amdgcn_readfirstlane((nstrips - (int)blockIdx.x + G - 1) / G);
+  const int my_n = __builtin_amdgcn_readfirstlane(n_strips);
   // Strip index math is made provably uniform (readfirstlane) so that the
   // descriptors and LDS addresses live in scalar registers.
   auto strip_n0 = [&](int i) -> int {
-    return __builtin_amdgcn_readfirstlane((int)blockIdx.x + i * G) * 16;
+    return __builtin_amdgcn_readfirstlane(first + i * step) * 16;
   };
 
   // Task loads.  Lane l fills bytes [16 l, 16 l + 16) of each half of a
@@ -251,8 +255,75 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
       store4(C, M, N, m, n, v);
     }
   }
-  // The trailing (out-of-range) loads land before the LDS is released.
+  // The trailing (out-of-range) loads land before the LDS is reused.
   wait_vmcnt<0>();
+}
+
+// Dense layer: strips blockIdx.x, blockIdx.x + G, ... of one weight.
+template <int MT, int P, bool kInt8>
+__global__ __launch_bounds__(512) void gemm_decode_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int nstrips) {
+  __shared__ __align__(16) DecodeRing ring;
+  extern __shared__ float lds_dyn[];
+  const int G = gridDim.x;
+  // Strips of this workgroup (uniform; the integer division runs on the
+  // vector unit, so the compiler needs telling).
+  const int my_n = __builtin_amdgcn_readfirstlane((nstrips - (int)blockIdx.x + G - 1) / G);
+  decode_segment<MT, P, kInt8>(A, sa, W, sw, M, N, K, C, (int)blockIdx.x, G, my_n, ring, lds_dyn);
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Mixture of experts, FP8 (FP8-RL abstract: the FP8 stack covers MoE
+// models).  Rows offsets[e] .. offsets[e+1] - 1 of A go to expert e, whose
+// weight is W + e N K with scales sw + e ceil(N/128) K/128.  The work is
+// the list of (expert, 64-row chunk, 16-channel strip) items of the experts
+// that have rows; workgroup b takes a contiguous share of it, so an active
+// expert's strips are spread over the workgroups however few experts are
+// active, and a workgroup mostly stays on one expert (its activations load
+// once per segment).  Offsets are clamped into [0, M]: no access leaves the
+// arrays whatever they hold.
+template <int MT, int P>
+__global__ __launch_bounds__(512) void gemm_grouped_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, const int64_t* __restrict__ offsets, int E, int M, int N, int K,
+    uint16_t* __restrict__ C) {
+  __shared__ __align__(16) DecodeRing ring;
+  extern __shared__ float lds_dyn[];
+  constexpr int kChunk = MT * 16;
+  const int S = (N + 15) / 16;
+  const int KB = K / kBlock, NB = (N + kBlock - 1) / kBlock;
+  auto rows_of = [&](int e, int64_t& r0, int64_t& r1) {
+    r0 = min<int64_t>(max<int64_t>(uniform64(offsets[e]), 0), M);
+    r1 = min<int64_t>(max<int64_t>(uniform64(offsets[e + 1]), r0), M);
+  };
+  int64_t total = 0;
+  for (int e = 0; e < E; ++e) {
+    int64_t r0, r1;
+    rows_of(e, r0, r1);
+    total += (int64_t)S * ((r1 - r0 + kChunk - 1) / kChunk);
+  }
+  const int64_t G = gridDim.x;
+  const int64_t per = (total + G - 1) / G;
+  const int64_t lo = (int64_t)blockIdx.x * per, hi = min(lo + per, total);
+  int64_t base = 0;
+  for (int e = 0; e < E && base < hi; ++e) {
+    int64_t r0, r1;
+    rows_of(e, r0, r1);
+    for (int64_t row0 = r0; row0 < r1 && base < hi; row0 += kChunk, base += S) {
+      const int64_t a = max(lo, base), b = min(hi, base + S);
+      if (a >= b) continue;
+      const int rows = (int)min<int64_t>(kChunk, r1 - row0);
+      decode_segment<MT, P, false>(A + row0 * K, sa + row0 * KB, W + (int64_t)e * N * K,
+                                   sw + (int64_t)e * NB * KB, rows, N, K, C + row0 * N,
+                                   (int)(a - base), 1, (int)(b - a), ring, lds_dyn);
+    }
+  }
 }
 
 // Compute units of the current device (cached per device ordinal).
@@ -322,6 +393,47 @@ bool launch_gemm_decode(const uint8_t* A, const float* sa, const uint8_t* W, con
     case 4: return launch_decode_mt<4, kInt8>(A, sa, W, sw, M, N, K, C, stream, err);
     default: return false;
   }
+}
+
+template <int MT>
+static bool launch_grouped_mt(const uint8_t* A, const float* sa, const uint8_t* W,
+                              const float* sw, const int64_t* offsets, int64_t E, int64_t M,
+                              int64_t N, int64_t K, uint16_t* C, hipStream_t stream,
+                              hipError_t* err) {
+  const int KB = (int)(K / kBlock);
+  const int pw = (KB + kDecodeWaves - 1) / kDecodeWaves;
+  const size_t lds = ((size_t)2 * kDecodeWaves * MT * 4 * 64 + (size_t)MT * 16 * KB) * sizeof(float);
+  if (lds + sizeof(DecodeSlot) * kDecodeWaves * kDecodeRing > (size_t)kLdsBytes) return false;
+  const int grid = compute_units();
+#define PRR_GROUPED_P(PV)                                                                  \
+  if (pw <= PV) {                                                                          \
+    hipLaunchKernelGGL((gemm_grouped_kernel<MT, PV>), dim3(grid), dim3(512), lds, stream, A, \
+                       sa, W, sw, offsets, (int)E, (int)M, (int)N, (int)K, C);             \
+    *err = hipGetLastError();                                                              \
+    return true;                                                                           \
+  }
+  PRR_GROUPED_P(2)
+  PRR_GROUPED_P(3)
+  PRR_GROUPED_P(4)
+  PRR_GROUPED_P(5)
+  PRR_GROUPED_P(6)
+  if constexpr (MT <= 2) {
+    PRR_GROUPED_P(8)
+  }
+#undef PRR_GROUPED_P
+  return false;
+}
+
+bool launch_gemm_grouped(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
+                         const int64_t* offsets, int64_t E, int64_t M, int64_t N, int64_t K,
+                         int64_t rows_hint, uint16_t* C, hipStream_t stream, hipError_t* err) {
+  // Same 32-bit offset limits as the dense kernel (per expert weight).
+  if (K < kBlock || 128 * K >= 0x7FFFFF00LL || N > 0x1FFFFFF0LL) return false;
+  if (4 * ((N + kBlock - 1) / kBlock) * (K / kBlock) >= 0x7FFFFF00LL) return false;
+  if (64 * K >= 0x7FFFFF00LL) return false;
+  if (rows_hint <= 16) return launch_grouped_mt<1>(A, sa, W, sw, offsets, E, M, N, K, C, stream, err);
+  if (rows_hint <= 32) return launch_grouped_mt<2>(A, sa, W, sw, offsets, E, M, N, K, C, stream, err);
+  return launch_grouped_mt<4>(A, sa, W, sw, offsets, E, M, N, K, C, stream, err);
 }
 
 template bool launch_gemm_decode<false>(const uint8_t*, const float*, const uint8_t*, const float*,

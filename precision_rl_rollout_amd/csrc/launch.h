@@ -40,6 +40,13 @@ bool launch_gemm_decode(const uint8_t* A, const float* sa, const uint8_t* W, con
                         int64_t M, int64_t N, int64_t K, uint16_t* C, hipStream_t stream,
                         hipError_t* err);
 
+// Grouped (mixture-of-experts) FP8 GEMM on the decode machinery; rows_hint
+// bounds the rows per expert for the register tiling (larger groups run in
+// 64-row chunks).  Returns false, launching nothing, when K is too large.
+bool launch_gemm_grouped(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
+                         const int64_t* offsets, int64_t E, int64_t M, int64_t N, int64_t K,
+                         int64_t rows_hint, uint16_t* C, hipStream_t stream, hipError_t* err);
+
 // Many-token W8A8 GEMM (256 x 256 tiles, LDS ring fed by direct-to-LDS
 // loads).  Returns false, launching nothing, outside the shapes it handles.
 template <bool kInt8>

@@ -33,7 +33,12 @@ _STREAMS = {
     "q": 11, "k": 12, "v": 13, "o": 14, "gate": 15, "up": 16, "down": 17,
     "special": 21,
     "kv_K": 31, "kv_V": 32, "kv_K_cols": 33, "kv_V_cols": 34, "kv_slots": 35,
+    "moe_A": 41, "moe_A_cols": 42, "moe_route": 43, "moe_W": 100,
 }
+
+# Mixture-of-experts decode layer (a 30B-A3B-class model: 128 experts, top-8
+# routing, expert up/gate N = 2 x 768, hidden K = 2048), 128 decoding tokens.
+MOE_DECODE = dict(E=128, topk=8, tokens=128, N=1536, K=2048)
 
 # FP8 KV cache of a 32B-class layer: 8 KV heads of 128 (C = 1024 per token),
 # a prefill batch of 16,384 tokens written into a cache of 65,536 slots in
@@ -62,11 +67,16 @@ CONFIGS = {
     "prefill32b": dict(gemms=[(8192, 27648, 5120, True), (8192, 5120, 27648, True)]),
     "stack32b_requant": dict(layers=STACK_32B, gemm_m=64),
     "kv32b_prefill": dict(kv=KV_32B),
+    "moe_decode": dict(moe=MOE_DECODE),
 }
 
 
 def _rng(seed: int, stream: str) -> np.random.Generator:
     return np.random.default_rng([int(seed), _STREAMS[stream]])
+
+
+def _rng_expert(seed: int, e: int) -> np.random.Generator:
+    return np.random.default_rng([int(seed), _STREAMS["moe_W"], int(e)])
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -160,3 +170,26 @@ def kv_slot_mapping(T: int, num_slots: int, page: int = 16, seed: int = 0,
     if pad_every > 0:
         slots[::pad_every] = -1
     return slots
+
+
+def moe_routing(tokens: int, E: int, topk: int, seed: int = 0) -> np.ndarray:
+    """Expert counts [E] of a batch: each token picks topk distinct experts
+    uniformly at random (a synthetic router), so the counts vary around
+    tokens * topk / E and some experts may get none."""
+    rng = _rng(seed, "moe_route")
+    picks = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(tokens)])
+    return np.bincount(picks.ravel(), minlength=E).astype(np.int64)
+
+
+def moe_problem(counts, N: int, K: int, seed: int = 0) -> dict:
+    """bf16 inputs of a grouped layer: A [sum(counts), K] (rows sorted by
+    expert, activation recipe), one weight Wt_e [N, K] per expert, and the
+    row offsets [E + 1]."""
+    counts = np.asarray(counts, dtype=np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    M = int(offsets[-1])
+    cols = outlier_columns(K, seed, "moe_A_cols")
+    A = bf16_normal((M, K), 1.0, seed, "moe_A", cols)
+    Wt = np.stack([f32_to_bf16_bits(_rng_expert(seed, e).standard_normal((N, K), dtype=np.float32)
+                                    * np.float32(0.02)) for e in range(len(counts))])
+    return dict(A=A, Wt=Wt, offsets=offsets, M=M, N=N, K=K)

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     names = set(_declared())
     assert names == {"fp8_weight_block_quant", "fp8_act_token_quant", "w8a8_block_gemm",
                      "int8_weight_channel_quant", "int8_act_token_quant",
-                     "w8a8_int8_channel_gemm", "fp8_kv_scale_recalibrate",
+                     "w8a8_int8_channel_gemm", "w8a8_block_gemm_grouped",
+                     "fp8_kv_scale_recalibrate",
                      "fp8_kv_cache_write", "prr_status_string", "prr_abi_version"}
 
 
@@ -50,7 +51,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.abi_version() == 2
+    header = open(HEADER).read()
+    declared = int(re.search(r"#define PRR_ABI_VERSION (\d+)", header).group(1))
+    assert binding.abi_version() == declared == binding.ABI_VERSION
     names = [binding.status_string(s) for s in range(7)]
     assert names == ["PRR_OK", "PRR_ERR_INVALID_ARG", "PRR_ERR_UNSUPPORTED_SHAPE",
                      "PRR_ERR_MISALIGNED", "PRR_ERR_NO_DEVICE", "PRR_ERR_UNSUPPORTED_DEVICE",
