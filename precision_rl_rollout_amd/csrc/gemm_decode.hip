@@ -282,47 +282,113 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 // Mixture of experts, FP8 (FP8-RL abstract: the FP8 stack covers MoE
 // models).  Rows offsets[e] .. offsets[e+1] - 1 of A go to expert e, whose
 // weight is W + e N K with scales sw + e ceil(N/128) K/128.  The work is
-// the list of (expert, 64-row chunk, 16-channel strip) items of the experts
-// that have rows; workgroup b takes a contiguous share of it, so an active
-// expert's strips are spread over the workgroups however few experts are
-// active, and a workgroup mostly stays on one expert (its activations load
-// once per segment).  Offsets are clamped into [0, M]: no access leaves the
-// arrays whatever they hold.
+// the list of (expert, MT*16-row chunk, 16-channel strip) items of the
+// experts that have rows; workgroup b takes a contiguous share of it, so an
+// active expert's strips are spread over the workgroups however few experts
+// are active, and a workgroup mostly stays on one expert (its activations
+// load once per segment).  Offsets are clamped into [0, M]: no access leaves
+// the arrays whatever they hold.
+//
+// Finding the share: the 512 threads read the offsets of 512 experts at a
+// time (one load each, all in flight together), and a workgroup prefix sum
+// gives each expert's first item in LDS; a binary search there finds the
+// first expert of the share.  (Walking the offsets one expert after another
+// costs a dependent global load per expert, for every workgroup.)
+constexpr int kScanExperts = 512;                 // experts per scan round (= threads)
+
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
 template <int MT, int P>
 __global__ __launch_bounds__(512) void gemm_grouped_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, const int64_t* __restrict__ offsets, int E, int M, int N, int K,
     uint16_t* __restrict__ C) {
   __shared__ __align__(16) DecodeRing ring;
+  __shared__ int64_t first_item[kScanExperts + 1];   // of each expert of the round; [512] = end
+  __shared__ int row_lo[kScanExperts], row_hi[kScanExperts];
+  __shared__ int64_t wave_part[kDecodeWaves];
   extern __shared__ float lds_dyn[];
   constexpr int kChunk = MT * 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = (N + 15) / 16;
   const int KB = K / kBlock, NB = (N + kBlock - 1) / kBlock;
   auto rows_of = [&](int e, int64_t& r0, int64_t& r1) {
-    r0 = min<int64_t>(max<int64_t>(uniform64(offsets[e]), 0), M);
-    r1 = min<int64_t>(max<int64_t>(uniform64(offsets[e + 1]), r0), M);
+    r0 = min<int64_t>(max<int64_t>(offsets[e], 0), M);
+    r1 = min<int64_t>(max<int64_t>(offsets[e + 1], r0), M);
   };
-  int64_t total = 0;
-  for (int e = 0; e < E; ++e) {
+  auto items_of = [&](int64_t r0, int64_t r1) {
+    return (int64_t)S * ((r1 - r0 + kChunk - 1) / kChunk);
+  };
+  // Total items.
+  int64_t mine = 0;
+  for (int e = tid; e < E; e += kScanExperts) {
     int64_t r0, r1;
     rows_of(e, r0, r1);
-    total += (int64_t)S * ((r1 - r0 + kChunk - 1) / kChunk);
+    mine += items_of(r0, r1);
   }
+  mine = wave_sum_i64(mine);
+  if (lane == 0) wave_part[wave] = mine;
+  lds_barrier();
+  int64_t total = 0;
+#pragma unroll
+  for (int w = 0; w < kDecodeWaves; ++w) total += wave_part[w];
+  total = uniform64(total);
   const int64_t G = gridDim.x;
   const int64_t per = (total + G - 1) / G;
   const int64_t lo = (int64_t)blockIdx.x * per, hi = min(lo + per, total);
-  int64_t base = 0;
-  for (int e = 0; e < E && base < hi; ++e) {
-    int64_t r0, r1;
-    rows_of(e, r0, r1);
-    for (int64_t row0 = r0; row0 < r1 && base < hi; row0 += kChunk, base += S) {
-      const int64_t a = max(lo, base), b = min(hi, base + S);
-      if (a >= b) continue;
-      const int rows = (int)min<int64_t>(kChunk, r1 - row0);
-      decode_segment<MT, P, false>(A + row0 * K, sa + row0 * KB, W + (int64_t)e * N * K,
-                                   sw + (int64_t)e * NB * KB, rows, N, K, C + row0 * N,
-                                   (int)(a - base), 1, (int)(b - a), ring, lds_dyn);
+  int64_t carry = 0;                                 // items of earlier rounds
+  for (int e0 = 0; e0 < E && carry < hi; e0 += kScanExperts) {
+    lds_barrier();                                   // wave_part / tables of the last round
+    const int cnt = min(kScanExperts, E - e0);
+    int64_t r0 = 0, r1 = 0;
+    if (tid < cnt) rows_of(e0 + tid, r0, r1);
+    const int64_t own = items_of(r0, r1);
+    int64_t incl = own;                              // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
     }
+    if (lane == 63) wave_part[wave] = incl;
+    lds_barrier();
+    int64_t before = carry;
+    for (int w = 0; w < wave; ++w) before += wave_part[w];
+    first_item[tid] = before + incl - own;
+    row_lo[tid] = (int)r0;
+    row_hi[tid] = (int)r1;
+    if (tid == kScanExperts - 1) first_item[kScanExperts] = before + incl;
+    lds_barrier();
+    const int64_t round_end = uniform64(first_item[kScanExperts]);
+    if (round_end > lo) {
+      // First expert of the round whose items end after lo.
+      int a = 0, b = cnt - 1;
+      while (a < b) {
+        const int mid = (a + b) >> 1;
+        if (first_item[mid + 1] > lo) b = mid; else a = mid + 1;
+      }
+      for (int i = __builtin_amdgcn_readfirstlane(a); i < cnt; ++i) {
+        int64_t base = uniform64(first_item[i]);
+        if (base >= hi) break;
+        const int64_t e_end = uniform64(first_item[i + 1]);
+        if (e_end == base) continue;                 // no rows
+        const int e = e0 + i;
+        const int64_t er0 = __builtin_amdgcn_readfirstlane(row_lo[i]);
+        const int64_t er1 = __builtin_amdgcn_readfirstlane(row_hi[i]);
+        for (int64_t row0 = er0; row0 < er1 && base < hi; row0 += kChunk, base += S) {
+          const int64_t x = max(lo, base), y = min(hi, base + S);
+          if (x >= y) continue;
+          const int rows = (int)min<int64_t>(kChunk, er1 - row0);
+          decode_segment<MT, P, false>(A + row0 * K, sa + row0 * KB, W + (int64_t)e * N * K,
+                                       sw + (int64_t)e * NB * KB, rows, N, K, C + row0 * N,
+                                       (int)(x - base), 1, (int)(y - x), ring, lds_dyn);
+        }
+      }
+    }
+    carry = round_end;
   }
 }
 
@@ -403,7 +469,9 @@ static bool launch_grouped_mt(const uint8_t* A, const float* sa, const uint8_t* 
   const int KB = (int)(K / kBlock);
   const int pw = (KB + kDecodeWaves - 1) / kDecodeWaves;
   const size_t lds = ((size_t)2 * kDecodeWaves * MT * 4 * 64 + (size_t)MT * 16 * KB) * sizeof(float);
-  if (lds + sizeof(DecodeSlot) * kDecodeWaves * kDecodeRing > (size_t)kLdsBytes) return false;
+  const size_t tables = (kScanExperts + 1) * 8 + kScanExperts * 8 + kDecodeWaves * 8;
+  if (lds + tables + sizeof(DecodeSlot) * kDecodeWaves * kDecodeRing > (size_t)kLdsBytes)
+    return false;
   const int grid = compute_units();
 #define PRR_GROUPED_P(PV)                                                                  \
   if (pw <= PV) {                                                                          \
