@@ -27,8 +27,16 @@
 //    end load at out-of-range offsets: no traffic, zeros, no branch.
 //  * The 8 partial sums of a strip meet in LDS (two buffers, alternate
 //    strips, one barrier per strip); MT waves add them, apply the epilogue
-//    and store bf16.  The barrier orders LDS only, so it does not drain the
-//    loads in flight.
+//    and store bf16 while the next strip's first task is in flight.  The
+//    barrier orders LDS only, so it does not drain the loads in flight.
+//  * Start-up: the ring's first loads, the resident activations and their
+//    scales are all issued before the first wait (one memory latency).
+//  * Output: a strip writes 32 bytes of each of its M rows.  Strips are
+//    mapped to workgroups so that the 4 strips sharing 128-byte output
+//    lines run on one XCD, whose L2 merges their writes.  Measured on a
+//    64-row problem, the writes still cost about a fifth of the strip time
+//    (with no stores at all a strip streams as fast as for one row); staging
+//    4 strips in LDS and writing whole lines measured the same.
 //
 // FP8: per K block, C += sa[m, kb] * sw[n / 128, kb] * MFMA(Wq, Aq) (one
 // v_mfma_f32_16x16x128_f8f6f4 per block, zero accumulator).  INT8: the
@@ -42,6 +50,7 @@
 namespace prr {
 
 constexpr int kDecodeWaves = 8;
+constexpr int kDecodeThreads = kDecodeWaves * 64;
 constexpr int kDecodeRing = 4;       // LDS slots per wave (3 tasks in flight)
 constexpr int kLdsBytes = 163840;    // LDS per workgroup on gfx950
 
@@ -84,38 +93,6 @@ __device__ __forceinline__ void decode_segment(
   const int pw = kbase + (wave < kextra ? 1 : 0);
   const int kb0 = wave * kbase + min(wave, kextra);
 
-  // Resident activation fragments of all m-tiles for this wave's K piece.
-  const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(A, (int64_t)M * K);
-  v8i afr[MT][P];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int m = mt * 16 + r16;
-      const int off = (j < pw) ? m * K + (kb0 + j) * kBlock + g * 16 : kOutOfRange;
-      afr[mt][j] = buffer_load32(ares, off, 0);
-    }
-
-  // Dynamic LDS: the FP8 activation scales of all rows, transposed to
-  // [K block][row] (kept for the whole segment), then two partial-sum
-  // exchange buffers used by alternate strips.
-  constexpr int kRows = MT * 16;
-  float* lsa = lds_dyn;
-  float* lred = lds_dyn + (kInt8 ? 0 : kRows * KB);
-  constexpr int kRedFloats = kDecodeWaves * MT * 4 * 64;
-  if constexpr (!kInt8) {
-    for (int e = threadIdx.x; e < kRows * KB; e += blockDim.x) {
-      const int m = e / KB, kb = e - m * KB;
-      lsa[kb * kRows + m] = (m < M) ? sa[(int64_t)m * KB + kb] : 0.f;
-    }
-    lds_barrier();
-  }
-  float sa_row[MT];
-  if constexpr (kInt8) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sa_row[mt] = (mt * 16 + r16 < M) ? sa[mt * 16 + r16] : 0.f;
-  }
-
   const int my_n = __builtin_amdgcn_readfirstlane(n_strips);
   // Strip index math is made provably uniform (readfirstlane) so that the
   // descriptors and LDS addresses live in scalar registers.
@@ -151,21 +128,119 @@ __device__ __forceinline__ void decode_segment(
   };
   constexpr int kLoadsPerTask = 3;
 
+  // The ring's first R - 1 tasks go out first, then the activations and
+  // their scales, so that all of the segment's start-up loads are in
+  // flight together (one memory latency, not two).
+#pragma unroll
+  for (int q = 0; q < R - 1; ++q) load_task(q);
+
+  // Resident activation fragments of all m-tiles for this wave's K piece.
+  const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(A, (int64_t)M * K);
+  v8i afr[MT][P];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int m = mt * 16 + r16;
+      const int off = (j < pw) ? m * K + (kb0 + j) * kBlock + g * 16 : kOutOfRange;
+      afr[mt][j] = buffer_load32(ares, off, 0);
+    }
+
+  // Dynamic LDS: the FP8 activation scales of all rows, transposed to
+  // [K block][row] (kept for the whole segment), then two partial-sum
+  // exchange buffers used by alternate strips.
+  constexpr int kRows = MT * 16;
+  float* lsa = lds_dyn;
+  float* lred = lds_dyn + (kInt8 ? 0 : kRows * KB);
+  constexpr int kRedFloats = kDecodeWaves * MT * 4 * 64;
+  float sa_row[MT];
+  if constexpr (!kInt8) {
+    // kRows x KB <= kRows x 8 P scales: every load is issued before the
+    // first store.
+    constexpr int kPer = (kRows * 8 * P + kDecodeThreads - 1) / kDecodeThreads;
+    float v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = threadIdx.x + u * kDecodeThreads;
+      v[u] = (e < kRows * KB && e / KB < M) ? sa[e] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = threadIdx.x + u * kDecodeThreads;
+      const int m = e / KB, kb = e - m * KB;
+      if (e < kRows * KB) lsa[kb * kRows + m] = v[u];
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sa_row[mt] = (mt * 16 + r16 < M) ? sa[mt * 16 + r16] : 0.f;
+  }
+  // Wait for the activations here, with nothing queued behind them: an
+  // empty asm that consumes the registers makes the compiler place its own
+  // wait here rather than at their first use, where it would also wait for
+  // the ring loads issued by then.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) asm volatile("" : : "v"(__int_as_float(afr[mt][j][q])));
+    if constexpr (kInt8) asm volatile("" : : "v"(sa_row[mt]));
+  }
+  if constexpr (!kInt8) lds_barrier();
+
   // Fragment read offsets of this lane within a slot (chunks g and g + 4).
   const int rbase = r16 * kBlock;
   const int roff_lo = rbase + ((g ^ ((r16 >> 1) & 7)) << 4);
   const int roff_hi = rbase + (((g + 4) ^ ((r16 >> 1) & 7)) << 4);
 
+  // Partial sums of a strip: [wave][mt][lane] x 4 floats, in one of two
+  // buffers (strip i uses buffer i & 1).  Waves 0 .. MT-1 add the 8 partial
+  // sums of strip i during strip i + 1, right after issuing its first
+  // task's loads, so the reduction overlaps that task's memory wait instead
+  // of delaying the next load issue.  Buffer i & 1 is written again at the
+  // end of strip i + 2, after every wave (the reducers included, having
+  // finished) has passed strip i + 1's barrier: one barrier per strip.
+  auto red_buf = [&](int i) {
+    return reinterpret_cast<float4 (*)[MT][64]>(lred + (i & 1) * kRedFloats);
+  };
+  float swprev[4] = {0.f, 0.f, 0.f, 0.f};       // INT8: channel scales of the strip being reduced
+  auto reduce_strip = [&](int i) {
+    if (wave >= MT) return;
+    auto red = red_buf(i);
+    const int mt = wave;
+    const int64_t m = mt * 16 + r16;
+    const int64_t n = strip_n0(i) + 4 * g;
+    float4 q[kDecodeWaves];
 #pragma unroll
-  for (int q = 0; q < R - 1; ++q) load_task(q);
+    for (int w = 0; w < kDecodeWaves; ++w) q[w] = red[w][mt][lane];
+    float v[4];
+    if constexpr (kInt8) {
+      int32_t t[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        t[0] += __float_as_int(q[w].x);
+        t[1] += __float_as_int(q[w].y);
+        t[2] += __float_as_int(q[w].z);
+        t[3] += __float_as_int(q[w].w);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (float)t[r] * (sa_row[mt] * swprev[r]);
+    } else {
+      float f[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        f[0] += q[w].x;
+        f[1] += q[w].y;
+        f[2] += q[w].z;
+        f[3] += q[w].w;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = f[r];
+    }
+    store4(C, M, N, m, n, v);
+  };
 
   for (int i = 0; i < my_n; ++i) {
-    // [wave][mt][r][lane], alternating between the two buffers: strip i's
-    // buffer is written again at strip i + 2, after every wave has passed
-    // strip i + 1's barrier (whose release fence completes the reads of
-    // strip i), so one barrier per strip suffices.
-    auto red = reinterpret_cast<float (*)[MT][4][64]>(lred + (i & 1) * kRedFloats);
-    const int n0 = strip_n0(i);
     float accf[MT][4];
     v4i acci[MT];
 #pragma unroll
@@ -183,6 +258,7 @@ __device__ __forceinline__ void decode_segment(
     for (int j = 0; j < P; ++j) {
       const int t = i * P + j;
       load_task(t + R - 1);
+      if (j == 0 && i > 0) reduce_strip(i - 1);
       wait_vmcnt<kLoadsPerTask * (R - 1)>();   // task t has landed
       const DecodeSlot& sl = ring[wave][t % R];
       const uint4 lo = *reinterpret_cast<const uint4*>(sl.w + roff_lo);
@@ -191,8 +267,9 @@ __device__ __forceinline__ void decode_segment(
                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       if constexpr (kInt8) {
         if (j == 0) {
-          // Read now (the slot is reloaded before the epilogue needs them):
-          // the asm consumes the registers, so the read completes here.
+          // Read now (the slot is reloaded before the reduction needs
+          // them): the asm consumes the registers, so the read completes
+          // here.
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             swcur[r] = sl.s[4 * g + r];
@@ -226,51 +303,44 @@ __device__ __forceinline__ void decode_segment(
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Add the 8 partial sums of the strip through LDS.
+    auto red = red_buf(i);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        red[wave][mt][r][lane] = kInt8 ? __int_as_float(acci[mt][r]) : accf[mt][r];
-    lds_barrier();
-    if (wave < MT) {
-      const int mt = wave;
-      const int64_t m = mt * 16 + r16;
-      const int64_t n = n0 + 4 * g;
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (kInt8) {
-          int32_t tsum = 0;
-#pragma unroll
-          for (int w = 0; w < kDecodeWaves; ++w) tsum += __float_as_int(red[w][mt][r][lane]);
-          v[r] = (float)tsum * (sa_row[mt] * swcur[r]);
-        } else {
-          float fsum = 0.f;
-#pragma unroll
-          for (int w = 0; w < kDecodeWaves; ++w) fsum += red[w][mt][r][lane];
-          v[r] = fsum;
-        }
-      }
-      store4(C, M, N, m, n, v);
+    for (int mt = 0; mt < MT; ++mt) {
+      if constexpr (kInt8)
+        red[wave][mt][lane] = make_float4(__int_as_float(acci[mt][0]), __int_as_float(acci[mt][1]),
+                                          __int_as_float(acci[mt][2]), __int_as_float(acci[mt][3]));
+      else
+        red[wave][mt][lane] = make_float4(accf[mt][0], accf[mt][1], accf[mt][2], accf[mt][3]);
     }
+    if constexpr (kInt8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) swprev[r] = swcur[r];
+    }
+    lds_barrier();
   }
+  if (my_n > 0) reduce_strip(my_n - 1);
   // The trailing (out-of-range) loads land before the LDS is reused.
   wait_vmcnt<0>();
 }
 
-// Dense layer: strips blockIdx.x, blockIdx.x + G, ... of one weight.
+// Dense layer: strips l, l + G, l + 2G, ... of one weight (l below).
 template <int MT, int P, bool kInt8>
 __global__ __launch_bounds__(512) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int nstrips) {
   __shared__ __align__(16) DecodeRing ring;
-  extern __shared__ float lds_dyn[];
-  const int G = gridDim.x;
-  // Strips of this workgroup (uniform; the integer division runs on the
-  // vector unit, so the compiler needs telling).
-  const int my_n = __builtin_amdgcn_readfirstlane((nstrips - (int)blockIdx.x + G - 1) / G);
-  decode_segment<MT, P, kInt8>(A, sa, W, sw, M, N, K, C, (int)blockIdx.x, G, my_n, ring, lds_dyn);
+  extern __shared__ __align__(16) float lds_dyn[];
+  const int G = gridDim.x, b = blockIdx.x;
+  // A strip writes 32 bytes of each output row, a quarter of a 128-byte
+  // line.  The strips of a round are mapped so that the 4 strips of each
+  // 64-channel line group run on one XCD (workgroup b runs on XCD b % 8),
+  // whose L2 then merges the partial line writes: strip l(b) + i G with
+  // l = 32 (b / 32) + 4 (b % 8) + (b / 8) % 4, a permutation of [0, G) when
+  // G is a multiple of 32.  Counts are uniform; the integer division runs on
+  // the vector unit, so the compiler needs telling.
+  const int l = (G & 31) == 0 ? (((b >> 5) << 5) | ((b & 7) << 2) | ((b >> 3) & 3)) : b;
+  const int my_n = __builtin_amdgcn_readfirstlane((nstrips - l + G - 1) / G);
+  decode_segment<MT, P, kInt8>(A, sa, W, sw, M, N, K, C, l, G, my_n, ring, lds_dyn);
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
@@ -311,7 +381,7 @@ __global__ __launch_bounds__(512) void gemm_grouped_kernel(
   __shared__ int64_t first_item[kScanExperts + 1];   // of each expert of the round; [512] = end
   __shared__ int row_lo[kScanExperts], row_hi[kScanExperts];
   __shared__ int64_t wave_part[kDecodeWaves];
-  extern __shared__ float lds_dyn[];
+  extern __shared__ __align__(16) float lds_dyn[];
   constexpr int kChunk = MT * 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = (N + 15) / 16;

@@ -73,6 +73,13 @@ def _check(c_gpu, ref, label):
     print(f"  {label}: rel_fro vs bf16(oracle) = {err:.3e}; vs unrounded fp64 = {raw:.3e}",
           flush=True)
     assert err <= TOL, f"{label}: relative Frobenius error {err:.3e} > {TOL}"
+    # Element by element: one bf16 rounding (<= 2^-8 relative) plus fp32
+    # accumulation error far below 1e-3 of the output's rms.  A value written
+    # to the wrong place, or not written, is off by about the rms.
+    g = gemm.bf16_bits_to_f64(c_gpu)
+    rms = np.sqrt(np.mean(c64 * c64)) if c64.size else 0.0
+    bad = np.abs(g - c64) > 2.0 ** -8 * np.abs(c64) + 1e-3 * rms
+    assert not bad.any(), f"{label}: {int(bad.sum())} elements off, first at {np.argwhere(bad)[0]}"
 
 
 GEMM_SHAPES = [(16, 256, 256), (5, 200, 384), (1, 16, 128), (17, 129, 256), (33, 1000, 640),
@@ -81,6 +88,10 @@ GEMM_SHAPES = [(16, 256, 256), (5, 200, 384), (1, 16, 128), (17, 129, 256), (33,
                # decode kernel: 5, 6 and 8 K blocks per wave; 601 strips, so a
                # workgroup streams several strips through its LDS ring
                (64, 640, 5120), (48, 500, 6144), (24, 300, 8192), (40, 9607, 1024),
+               # decode kernel with whole rounds of 4-strip quads (staged output):
+               # a ragged strip inside the last quad, N not a multiple of 8
+               # (element-wise row segments), quads followed by single strips
+               (33, 16376, 256), (64, 16379, 384), (17, 20000, 512),
                # many-token kernel (256 x 256 tiles): odd K-block count over a
                # 3 x 4 tile grid, a single K block over 9 x 2 tiles, 4 x 4 tiles
                (513, 777, 1152), (2304, 512, 128), (1024, 1024, 256)]

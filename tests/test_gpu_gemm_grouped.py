@@ -50,6 +50,14 @@ def _run_and_check(counts, N, K, hint, seed=0, lead=0, tail=0):
     assert np.all(got[:r0] == CANARY16) and np.all(got[r1:] == CANARY16), "rows outside groups"
     err = gemm.rel_frobenius(got[r0:r1], ref[r0:r1])
     assert err <= TOL, f"relative Frobenius error {err:.3e}"
+    # Element by element: the two bf16 roundings (<= 2^-8 relative each) and
+    # an fp32 accumulation error far below 1e-3 of the rms; a value written to
+    # the wrong row or channel is off by about the rms.
+    g = gemm.bf16_bits_to_f64(got[r0:r1])
+    r = gemm.bf16_bits_to_f64(ref[r0:r1])
+    rms = np.sqrt(np.mean(r * r)) if r.size else 0.0
+    bad = np.abs(g - r) > 2.0 ** -7 * np.abs(r) + 1e-3 * rms
+    assert not bad.any(), f"{int(bad.sum())} elements off, first at {np.argwhere(bad)[0]}"
 
 
 @pytest.mark.parametrize("counts,N,K,hint", [
