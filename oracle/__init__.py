@@ -29,6 +29,12 @@ What it computes, with the passage each part follows:
 * ``oracle.gemm`` -- also the mixture-of-experts grouping of the FP8 layer:
   token rows sorted by expert, each group multiplied by its expert's weight
   (FP8-RL abstract: dense and MoE models).
+* ``oracle.tis`` -- token-level importance weights for rollout correction:
+  the trainer-to-rollout probability ratio of each sampled token, truncated
+  (TIS) or masked (MIS) at a constant, with per-sequence statistics
+  (FP8-RL abstract, item (iii); FlashRL article, section on the
+  rollout-training mismatch; formula and constant are readings, listed
+  there).
 * ``oracle.gemm`` -- the W8A8 linear layer: fp64 accumulation over the
   exactly decoded 8-bit operands with the per-K-block (FP8) or per-row and
   per-channel (INT8) scales, rounded once to bf16.

@@ -34,11 +34,16 @@ _STREAMS = {
     "special": 21,
     "kv_K": 31, "kv_V": 32, "kv_K_cols": 33, "kv_V_cols": 34, "kv_slots": 35,
     "moe_A": 41, "moe_A_cols": 42, "moe_route": 43, "moe_W": 100,
+    "tis_len": 51, "tis_lr": 52, "tis_d": 53, "tis_tail": 54,
 }
 
 # Mixture-of-experts decode layer (a 30B-A3B-class model: 128 experts, top-8
 # routing, expert up/gate N = 2 x 768, hidden K = 2048), 128 decoding tokens.
 MOE_DECODE = dict(E=128, topk=8, tokens=128, N=1536, K=2048)
+
+# Rollout-correction batch: 1024 responses of up to 8192 tokens, truncation
+# constant 2.
+TIS_BATCH = dict(B=1024, T=8192, cap=2.0)
 
 # FP8 KV cache of a 32B-class layer: 8 KV heads of 128 (C = 1024 per token),
 # a prefill batch of 16,384 tokens written into a cache of 65,536 slots in
@@ -193,3 +198,25 @@ def moe_problem(counts, N: int, K: int, seed: int = 0) -> dict:
     Wt = np.stack([f32_to_bf16_bits(_rng_expert(seed, e).standard_normal((N, K), dtype=np.float32)
                                     * np.float32(0.02)) for e in range(len(counts))])
     return dict(A=A, Wt=Wt, offsets=offsets, M=M, N=N, K=K)
+
+
+def tis_batch(B: int, T: int, seed: int = 0) -> dict:
+    """Per-token log-probabilities of a batch of B responses padded to T:
+    response lengths uniform in [max(1, T/8), T]; the rollout policy's
+    log-probability of each sampled token is -Exp(0.3) (mostly confident
+    tokens, a tail of unlikely ones, floored at -30); the trainer's differs
+    by N(0, 0.02) on 99% of the tokens and by N(0, 1) on the other 1% (the
+    precision mismatch and its tail).  Padding holds zeros.  float32 [B, T]
+    x 2 and the uint8 response mask."""
+    lens = _rng(seed, "tis_len").integers(max(1, T // 8), T + 1, size=B)
+    mask = (np.arange(T)[None, :] < lens[:, None]).astype(np.uint8)
+    lr = -_rng(seed, "tis_lr").exponential(0.3, size=(B, T))
+    lr = np.maximum(lr, -30.0).astype(np.float32)
+    r = _rng(seed, "tis_d")
+    d = r.standard_normal((B, T), dtype=np.float32) * np.float32(0.02)
+    tail = _rng(seed, "tis_tail").random((B, T)) < 0.01
+    d = np.where(tail, r.standard_normal((B, T), dtype=np.float32), d).astype(np.float32)
+    lt = (lr + d).astype(np.float32)
+    lr = np.where(mask != 0, lr, np.float32(0)).astype(np.float32)
+    lt = np.where(mask != 0, lt, np.float32(0)).astype(np.float32)
+    return dict(lp_train=lt, lp_rollout=lr, mask=mask)
