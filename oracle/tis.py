@@ -20,10 +20,10 @@ the readings taken here:
 * tokens outside the response (mask 0, padding) get ``w = 0`` and count in
   no statistic;
 * "over the cap" is decided in binary32, in log space:
-  ``d = fl32(lp_train - lp_rollout) > fl32(ln C)``, with ``ln C`` taken in
-  fp64 and rounded once (both inputs are binary32 log-probabilities; a
-  decision that sets a weight to C or 0 must not depend on how an
-  implementation evaluates exp);
+  ``d = fl32(lp_train - lp_rollout) > fl32(ln C)``, with C itself a
+  binary32 value and ``ln C`` taken in fp64 and rounded once (both inputs
+  are binary32 log-probabilities; a decision that sets a weight to C or 0
+  must not depend on how an implementation evaluates exp);
 * per sequence: valid tokens, tokens over the cap, the sum of the weights,
   and the sum of ``lp_rollout - lp_train`` over valid tokens (divided by the
   valid count, the sample estimate of KL(rollout || trainer) for tokens drawn
@@ -44,8 +44,9 @@ MASK = 1          # MIS
 
 
 def log_cap(cap: float) -> np.float32:
-    """fl32(ln C) for C > 0 (+inf for C = +inf)."""
-    c = float(cap)
+    """fl32(ln C) for C > 0 (+inf for C = +inf).  C is a binary32 value (the
+    constant is passed as one), so the logarithm is taken of fl32(C)."""
+    c = float(np.float32(cap))
     if not c > 0:
         raise ValueError("oracle: the truncation constant must be positive")
     return np.float32(math.log(c)) if math.isfinite(c) else np.float32(np.inf)
