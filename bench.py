@@ -24,7 +24,8 @@ GEMMs, TFLOP/s), ``stack32b_requant`` (FP8 and INT8 re-quantization of a
 32B-class layer's seven weights), ``kv32b_prefill`` (FP8 KV-cache scale
 recalibration and quantize-on-write of a 16,384-token prefill),
 ``moe_decode`` (a 128-expert top-8 decode layer: weight re-quantization of
-every expert, activation quantization, the grouped GEMM).
+every expert, activation quantization, the grouped GEMM), ``tis_batch``
+(TIS and MIS token weights of 1024 responses padded to 8192 tokens).
 """
 
 from __future__ import annotations
@@ -82,6 +83,7 @@ KERNEL_SOURCES = {
     "w8a8_block_gemm@decode7b_upgate": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
     "w8a8_int8_channel_gemm@decode7b_upgate": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
     "w8a8_block_gemm_grouped": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
+    "tis_token_weights": ["tis.hip", "prr_device.h"],
     # M = 8192 runs the many-token kernel.
     "w8a8_block_gemm@prefill32b": ["gemm_prefill.hip", "mfma.h", "prr_device.h"],
     "w8a8_int8_channel_gemm@prefill32b": ["gemm_prefill.hip", "mfma.h", "prr_device.h"],
@@ -523,6 +525,56 @@ def run_moe_decode(args, torch, B, W):
     return line
 
 
+def run_tis(args, torch, B, W):
+    """Rollout correction of a batch of 1024 responses padded to 8192 tokens:
+    per step, the TIS and the MIS weights with per-sequence statistics and
+    batch totals (two calls)."""
+    cfg = W.TIS_BATCH
+    Bn, T, cap = cfg["B"], cfg["T"], cfg["cap"]
+    p = W.tis_batch(Bn, T, seed=0)
+    lt = torch.from_numpy(p["lp_train"]).cuda()
+    lr = torch.from_numpy(p["lp_rollout"]).cuda()
+    mk = torch.from_numpy(p["mask"]).cuda()
+    outs = {m: (torch.empty((Bn, T), dtype=torch.float32, device="cuda:0"),
+                torch.empty((Bn, 4), dtype=torch.float32, device="cuda:0"),
+                torch.empty((4,), dtype=torch.float64, device="cuda:0"))
+            for m in (B.IS_TRUNCATE, B.IS_MASK)}
+    names = {B.IS_TRUNCATE: "tis_token_weights(TIS)", B.IS_MASK: "tis_token_weights(MIS)"}
+
+    def step(_i, timer=None):
+        for m in (B.IS_TRUNCATE, B.IS_MASK):
+            w, rs, tt = outs[m]
+            f = lambda: B.tis_token_weights(lt, lr, mk, cap, m, out=w, row_stats=rs, totals=tt)
+            timer.run(names[m], f) if timer else f()
+
+    dt, us, dom = timed_steps(torch, step, args)
+    per_call = 13 * Bn * T + 16 * Bn * 2 + 32          # inputs, weights, row stats (write + read), totals
+    kernels = {k: {"us": round(v, 2), "algorithmic_bytes": per_call,
+                   "GB/s": round(per_call / v / 1e3, 1)} for k, v in us.items()}
+    line = {"metric": METRIC, "value": round(2 * per_call / dt / 1e9, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "tis_batch", "sequences": Bn, "tokens": T, "cap": cap,
+                       "valid_tokens": int(p["mask"].sum()),
+                       "step": "TIS and MIS token weights with per-sequence statistics and totals"},
+            "roofline": {"bound": "hbm", "kernel": dom,
+                         "achieved": round(per_call / us[dom] / 1e3, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(per_call / us[dom] / 1e3 / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("tis_token_weights", "tis_batch")},
+            "kernels": kernels}
+    if not args.no_cpu_baseline:
+        from oracle import tis as otis
+        t0 = time.perf_counter()
+        for m in (otis.TRUNCATE, otis.MASK):
+            otis.importance_weights(p["lp_train"], p["lp_rollout"], p["mask"], cap, m)
+        ct = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(2 * per_call / ct / 1e9, 4), "unit": "GB/s",
+                                "cores": cpu_threads(), "kind": "oracle", "seconds": round(ct, 2),
+                                "sample": "one whole step (TIS and MIS over the full batch)"}
+    return line
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -530,7 +582,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode7b_upgate",
                     choices=["decode7b_upgate", "decode32b_sweep", "prefill32b", "stack32b_requant",
-                             "kv32b_prefill", "moe_decode"])
+                             "kv32b_prefill", "moe_decode", "tis_batch"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (outside the "
@@ -558,7 +610,8 @@ def main(argv=None):
         del src, dst
     run = {"decode7b_upgate": run_decode7b, "decode32b_sweep": run_decode32b,
            "prefill32b": run_prefill32b, "stack32b_requant": run_stack32b,
-           "kv32b_prefill": run_kv32b, "moe_decode": run_moe_decode}[args.workload]
+           "kv32b_prefill": run_kv32b, "moe_decode": run_moe_decode,
+           "tis_batch": run_tis}[args.workload]
     line = run(args, torch, B, W)
     print(json.dumps(line), flush=True)
     return 0

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PRR_ABI_VERSION 3
+#define PRR_ABI_VERSION 4
 
 typedef enum prr_status {
   PRR_OK = 0,
@@ -237,6 +237,44 @@ prr_status fp8_kv_scale_recalibrate(const uint16_t* x_bf16, int64_t T, int64_t C
 prr_status fp8_kv_cache_write(const uint16_t* kv_bf16, const int64_t* slot_mapping,
                               int64_t T, int64_t C, const float* scale, uint8_t* cache,
                               int64_t num_slots, hipStream_t stream);
+
+/*
+ * tis_token_weights -- token-level importance weights for correcting the
+ * mismatch between the rollout policy (e.g. an FP8 rollout engine) and the
+ * trainer's policy (FP8-RL, abstract, item (iii): token-level TIS/MIS
+ * rollout correction; FlashRL article, section on the rollout-training
+ * mismatch: truncated importance sampling).  The pages print no formula;
+ * this library's reading, per response token t of sequence b:
+ *   d   = fl32(logp_train - logp_rollout)          (binary32 subtraction)
+ *   over = d > fl32(ln cap)                         (ln in fp64, rounded once)
+ *   PRR_IS_TRUNCATE (TIS): w = over ? cap : expf(d)     (= min(ratio, cap))
+ *   PRR_IS_MASK     (MIS): w = over ? 0   : expf(d)     (token left out)
+ *   padding (mask 0): w = 0, counted in no statistic; its log-probabilities
+ *   are never used (they may hold anything, NaN included).
+ *   logp_train, logp_rollout in [B, T] fp32: log-probability of each sampled
+ *                       token under the trainer's / the rollout engine's
+ *                       policy (finite on response tokens).
+ *   mask       in  [B, T] uint8: nonzero = response token.
+ *   cap        truncation constant C > 0 (+inf: plain importance ratios).
+ *   weights    out [B, T] fp32.  expf(d) is within 2 ulp of exp(d).
+ *   row_stats  out [B, 4] fp32 or NULL: per sequence (valid tokens, tokens
+ *                  over the cap, sum of w, sum of logp_rollout - logp_train);
+ *                  counts are exact (T <= 2^24), the sums are fp32 added in
+ *                  a fixed order (bitwise repeatable).  The last one divided
+ *                  by the first is the sample estimate of KL(rollout ||
+ *                  trainer).
+ *   totals     out [4] fp64 or NULL: the sums over all sequences of
+ *                  row_stats (fixed order); requires row_stats when B > 0.
+ *   B, T >= 0; T > 2^24 -> PRR_ERR_UNSUPPORTED_SHAPE; cap not > 0 (NaN
+ *   included), an unknown mode, or totals without row_stats ->
+ *   PRR_ERR_INVALID_ARG.  T % 4 == 0 takes the vector path.
+ */
+#define PRR_IS_TRUNCATE 0
+#define PRR_IS_MASK 1
+prr_status tis_token_weights(const float* logp_train, const float* logp_rollout,
+                             const uint8_t* mask, int64_t B, int64_t T, float cap, int mode,
+                             float* weights, float* row_stats, double* totals,
+                             hipStream_t stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* prr_status_string(prr_status status);

@@ -35,13 +35,17 @@ _SIGNATURES = {
     "w8a8_block_gemm_grouped": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P],
     "fp8_kv_scale_recalibrate": [_P, _I64, _I64, _P, _P],
     "fp8_kv_cache_write": [_P, _P, _I64, _I64, _P, _P, _I64, _P],
+    "tis_token_weights": [_P, _P, _P, _I64, _I64, ctypes.c_float, ctypes.c_int, _P, _P, _P, _P],
 }
+
+IS_TRUNCATE = 0     # TIS: min(ratio, cap)
+IS_MASK = 1         # MIS: ratio, or 0 above the cap
 
 _lib = None
 
 # PRR_ABI_VERSION of the signatures below; a library of another version is
 # refused at load time.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class PrrError(RuntimeError):
@@ -248,3 +252,27 @@ def w8a8_block_gemm_grouped(aq: torch.Tensor, sa: torch.Tensor, wq: torch.Tensor
                                           E, M, N, K, int(max_rows_per_expert), _ptr(c),
                                           _stream(aq)))
     return c
+
+
+def tis_token_weights(lp_train: torch.Tensor, lp_rollout: torch.Tensor, mask: torch.Tensor,
+                      cap: float, mode: int = IS_TRUNCATE, out=None, row_stats=None, totals=None,
+                      stats: bool = True):
+    """Token-level importance weights of a batch: lp_train, lp_rollout fp32
+    [B, T] (log-probabilities of the sampled tokens), mask uint8 [B, T]
+    (nonzero = response token), truncation constant cap, mode IS_TRUNCATE
+    (TIS) or IS_MASK (MIS).  Returns (weights fp32 [B, T], row_stats fp32
+    [B, 4] or None, totals fp64 [4] or None)."""
+    if lp_train.dim() != 2:
+        raise ValueError("lp_train: expected [B, T]")
+    B, T = lp_train.shape
+    _operand(lp_train, torch.float32, (B, T), "lp_train")
+    _operand(lp_rollout, torch.float32, (B, T), "lp_rollout")
+    _operand(mask, torch.uint8, (B, T), "mask")
+    w = _out(out, torch.float32, (B, T), lp_train, "out")
+    rs = _out(row_stats, torch.float32, (B, 4), lp_train, "row_stats") if stats else None
+    tt = _out(totals, torch.float64, (4,), lp_train, "totals") if stats else None
+    _check("tis_token_weights",
+           load().tis_token_weights(_ptr(lp_train), _ptr(lp_rollout), _ptr(mask), B, T,
+                                    float(cap), int(mode), _ptr(w), _ptr(rs), _ptr(tt),
+                                    _stream(lp_train)))
+    return w, rs, tt

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cmath>
 
 #include "launch.h"
 #include "prr.h"
@@ -199,6 +200,26 @@ prr_status fp8_kv_cache_write(const uint16_t* kv_bf16, const int64_t* slot_mappi
   PRR_TRY(check_device());
   return from_hip(
       prr::launch_fp8_kv_cache_write(kv_bf16, slot_mapping, T, C, scale, cache, num_slots, stream));
+}
+
+prr_status tis_token_weights(const float* logp_train, const float* logp_rollout,
+                             const uint8_t* mask, int64_t B, int64_t T, float cap, int mode,
+                             float* weights, float* row_stats, double* totals,
+                             hipStream_t stream) {
+  PRR_TRY(check_dims(B, T));
+  if (!(cap > 0.0f) || (mode != PRR_IS_TRUNCATE && mode != PRR_IS_MASK)) return PRR_ERR_INVALID_ARG;
+  if (totals != nullptr && row_stats == nullptr && B > 0) return PRR_ERR_INVALID_ARG;
+  if (T > (int64_t(1) << 24)) return PRR_ERR_UNSUPPORTED_SHAPE;   // counts kept exact in fp32
+  if (B > 0 && T > 0) PRR_TRY(check_ptrs({logp_train, logp_rollout, mask, weights}));
+  if (B > 0 && row_stats != nullptr) PRR_TRY(check_ptrs({row_stats}));
+  if (totals != nullptr) PRR_TRY(check_ptrs({totals}));
+  if (B == 0 && totals == nullptr) return PRR_OK;
+  if (T == 0 && row_stats == nullptr && totals == nullptr) return PRR_OK;
+  PRR_TRY(check_device());
+  // fl32(ln C), from the fp64 logarithm rounded once; +inf for C = +inf.
+  const float lncap = std::isinf(cap) ? cap : (float)std::log((double)cap);
+  return from_hip(prr::launch_tis_token_weights(logp_train, logp_rollout, mask, B, T, cap, lncap,
+                                                mode, weights, row_stats, totals, stream));
 }
 
 const char* prr_status_string(prr_status status) {

@@ -30,6 +30,11 @@ hipError_t launch_fp8_kv_cache_write(const uint16_t* kv, const int64_t* slots, i
                                      int64_t C, const float* scale, uint8_t* cache,
                                      int64_t num_slots, hipStream_t stream);
 
+hipError_t launch_tis_token_weights(const float* lp_train, const float* lp_rollout,
+                                    const uint8_t* mask, int64_t B, int64_t T, float cap,
+                                    float lncap, int mode, float* w, float* row_stats,
+                                    double* totals, hipStream_t stream);
+
 // Compute units of the current device (cached per device; 256 if unknown).
 int compute_units();
 

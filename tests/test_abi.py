@@ -41,7 +41,8 @@ def test_header_declares_the_boundary():
                      "int8_weight_channel_quant", "int8_act_token_quant",
                      "w8a8_int8_channel_gemm", "w8a8_block_gemm_grouped",
                      "fp8_kv_scale_recalibrate",
-                     "fp8_kv_cache_write", "prr_status_string", "prr_abi_version"}
+                     "fp8_kv_cache_write", "tis_token_weights", "prr_status_string",
+                     "prr_abi_version"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -160,3 +161,37 @@ def test_kv_cache_write_argument_checks():
 def test_kv_no_device_is_reported():
     assert binding.call("fp8_kv_scale_recalibrate", FAKE, 4, 8, FAKE, None) == NO_DEVICE
     assert binding.call("fp8_kv_cache_write", FAKE, FAKE, 4, 8, FAKE, FAKE, 16, None) == NO_DEVICE
+
+
+def test_tis_argument_checks():
+    c = lambda *a: binding.call("tis_token_weights", *a)
+    ok = [FAKE, FAKE, FAKE, 4, 8, 2.0, 0, FAKE, FAKE, FAKE, None]
+    bad = dict(B=(3, -1), T=(4, -8), cap0=(5, 0.0), capneg=(5, -1.0), capnan=(5, float("nan")),
+               mode=(6, 2))
+    for _, (i, v) in bad.items():
+        a = list(ok)
+        a[i] = v
+        assert c(*a) == INVALID
+    for i in (0, 1, 2, 7):
+        a = list(ok)
+        a[i] = None
+        assert c(*a) == INVALID
+        a[i] = ODD
+        assert c(*a) == MISALIGNED
+    a = list(ok)
+    a[8] = None                                  # totals need the row statistics
+    assert c(*a) == INVALID
+    a = list(ok)
+    a[4] = 2 ** 24 + 4                           # counts must stay exact in fp32
+    assert c(*a) == SHAPE
+    # nothing to compute and nothing to report: no pointer is needed
+    assert c(None, None, None, 0, 8, 2.0, 1, None, None, None, None) == OK
+    assert c(None, None, None, 4, 0, 2.0, 0, None, None, None, None) == OK
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="needs a process without a GPU")
+def test_tis_no_device_is_reported():
+    assert binding.call("tis_token_weights", FAKE, FAKE, FAKE, 4, 8, 2.0, 0, FAKE, FAKE, FAKE,
+                        None) == NO_DEVICE
+    assert binding.call("tis_token_weights", None, None, None, 0, 8, 2.0, 0, None, None, FAKE,
+                        None) == NO_DEVICE
