@@ -117,15 +117,30 @@ __global__ __launch_bounds__(kTisThreads) void tis_row_kernel(
 
 // Batch totals from the row statistics: one workgroup, fp64, fixed order
 // (thread i adds rows i, i + 256, ... in order, then a butterfly and the
-// 4 wave results in wave order).  B == 0 writes zeros.
+// 4 wave results in wave order).  A thread's rows are loaded kTotalRows at a
+// time (16 bytes each, all issued before the first add).  B == 0 writes
+// zeros.
+constexpr int kTotalRows = 8;
+
 __global__ __launch_bounds__(kTisThreads) void tis_total_kernel(const float* __restrict__ row_stats,
                                                                 int64_t B,
                                                                 double* __restrict__ totals) {
   const int tid = threadIdx.x;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int64_t b = tid; b < B; b += kTisThreads) {
+  for (int64_t b0 = tid; b0 < B; b0 += (int64_t)kTisThreads * kTotalRows) {
+    float4 v[kTotalRows];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] += (double)row_stats[b * 4 + j];
+    for (int u = 0; u < kTotalRows; ++u) {
+      const int64_t b = b0 + (int64_t)u * kTisThreads;
+      v[u] = b < B ? reinterpret_cast<const float4*>(row_stats)[b] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kTotalRows; ++u) {
+      s[0] += (double)v[u].x;
+      s[1] += (double)v[u].y;
+      s[2] += (double)v[u].z;
+      s[3] += (double)v[u].w;
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1)
