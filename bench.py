@@ -385,6 +385,57 @@ def run_stack32b(args, torch, B, W):
                         "int8_weight_channel_quant(stack)": {"us": round(peri, 1), "GB/s": round(bi / peri / 1e3, 1)}}}
 
 
+def run_stack_gemm(args, torch, B, W):
+    """The W8A8 GEMMs of one 32B-shaped layer stack at decode batch sizes:
+    for M in (1, 64), the FP8 block-scaled and the INT8 per-channel GEMM of
+    each of the seven weights (q, k, v, o, gate, up, down; 487 MB of 8-bit
+    weights per pass, so no GEMM finds its weight in the 256 MB last-level
+    cache).  value: algorithmic bytes of the whole pass / its time."""
+    layers = []
+    for name, N, K in W.STACK_32B:
+        w = torch.from_numpy(W.stack_layer(name, 0).view(np.int16)).cuda()
+        layers.append((name, N, K, B.fp8_weight_block_quant(w), B.int8_weight_channel_quant(w)))
+        del w
+    res, total_bytes, total_s = {}, 0, 0.0
+    for M in (1, 64):
+        acts = {}
+        for name, N, K, _, _ in layers:
+            if K not in acts:
+                a = torch.from_numpy(W.activation(M, K, 0).view(np.int16)).cuda()
+                acts[K] = (B.fp8_act_token_quant(a), B.int8_act_token_quant(a))
+        outs = {name: torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+                for name, N, K, _, _ in layers}
+        work = {}
+        for name, N, K, _, _ in layers:
+            work[f"w8a8_block_gemm/{name}/M{M}"] = gemm_bytes(M, N, K, M * (K // 128),
+                                                             cdiv(N, 128) * (K // 128))
+            work[f"w8a8_int8_channel_gemm/{name}/M{M}"] = gemm_bytes(M, N, K, M, N)
+
+        def step(_i, timer=None, M=M, acts=acts, outs=outs):
+            t = timer.run if timer else (lambda _n, f: f())
+            for name, N, K, (wq, sw), (wqi, swi) in layers:
+                (aq, sa), (aqi, sai) = acts[K]
+                c = outs[name]
+                t(f"w8a8_block_gemm/{name}/M{M}", lambda: B.w8a8_block_gemm(aq, sa, wq, sw, out=c))
+                t(f"w8a8_int8_channel_gemm/{name}/M{M}",
+                  lambda: B.w8a8_int8_channel_gemm(aqi, sai, wqi, swi, out=c))
+
+        dt, us, _ = timed_steps(torch, step, args)
+        for k, v in us.items():
+            res[k] = {"us": round(v, 2), "GB/s": round(work[k] / v / 1e3, 1),
+                      "hbm_frac": round(work[k] / v / 1e3 / HBM_PEAK_GBS, 4)}
+        total_bytes += sum(work.values())
+        total_s += dt
+    return {"metric": METRIC, "value": round(total_bytes / total_s / 1e9, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(total_s * 1e3, 3), "higher_is_better": True, "vs_baseline": None,
+            "dtype": "fp8e4m3+int8", "data": "synthetic",
+            "config": {"workload": "stack32b_gemm", "M": [1, 64],
+                       "layers": [list(x) for x in W.STACK_32B],
+                       "value_is": "algorithmic bytes of all 28 GEMM calls / their time"},
+            "kernels": res}
+
+
 def run_kv32b(args, torch, B, W):
     """FP8 KV cache of a 32B-class layer for a 16,384-token prefill: per
     step, recalibrate the K and V scales on the new rows and write both into
@@ -582,7 +633,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode7b_upgate",
                     choices=["decode7b_upgate", "decode32b_sweep", "prefill32b", "stack32b_requant",
-                             "kv32b_prefill", "moe_decode", "tis_batch"])
+                             "kv32b_prefill", "moe_decode", "tis_batch", "stack32b_gemm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (outside the "
@@ -611,7 +662,7 @@ def main(argv=None):
     run = {"decode7b_upgate": run_decode7b, "decode32b_sweep": run_decode32b,
            "prefill32b": run_prefill32b, "stack32b_requant": run_stack32b,
            "kv32b_prefill": run_kv32b, "moe_decode": run_moe_decode,
-           "tis_batch": run_tis}[args.workload]
+           "tis_batch": run_tis, "stack32b_gemm": run_stack_gemm}[args.workload]
     line = run(args, torch, B, W)
     print(json.dumps(line), flush=True)
     return 0

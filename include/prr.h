@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PRR_ABI_VERSION 4
+#define PRR_ABI_VERSION 5
 
 typedef enum prr_status {
   PRR_OK = 0,
@@ -170,6 +170,36 @@ prr_status w8a8_int8_channel_gemm(const int8_t* a_i8, const float* a_scale,
                                   const int8_t* w_i8, const float* w_scale,
                                   int64_t M, int64_t N, int64_t K,
                                   uint16_t* c_bf16, hipStream_t stream);
+
+/*
+ * w8a8_gemm_workspace_size / w8a8_block_gemm_ws / w8a8_int8_channel_gemm_ws
+ * -- the two GEMMs above with an optional caller-owned workspace, for
+ * decode-sized batches (M <= 64) of layers with few output channels or long
+ * K (e.g. a down projection, N 5120 x K 27648), where one workgroup per
+ * 16-channel strip over all of K leaves CUs idle or cannot hold the
+ * activations.  With the workspace the call splits K into S slices, writes
+ * fp32 partial sums (INT8: int32 accumulators) to it and adds the slices in
+ * a fixed order (bitwise repeatable; same definition and tolerance as the
+ * one-pass call).  Callers that cannot provide one use the calls above.
+ *   w8a8_gemm_workspace_size: *bytes = the workspace the _ws calls use for
+ *       this shape on the current device (S x M x N x 4; 0 = no split, the
+ *       _ws call runs the one-pass kernels).  Same for FP8 and INT8.
+ *   workspace: device memory, 16-byte aligned, not shared with a call in
+ *       flight on another stream; NULL or workspace_bytes below the size
+ *       -> the one-pass kernels (never an error).  The library does not
+ *       keep the pointer.
+ *   Other arguments and errors as w8a8_block_gemm / w8a8_int8_channel_gemm;
+ *   workspace_bytes < 0 -> PRR_ERR_INVALID_ARG.
+ */
+prr_status w8a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes);
+prr_status w8a8_block_gemm_ws(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                              const float* w_scale, int64_t M, int64_t N, int64_t K,
+                              uint16_t* c_bf16, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream);
+prr_status w8a8_int8_channel_gemm_ws(const int8_t* a_i8, const float* a_scale,
+                                     const int8_t* w_i8, const float* w_scale, int64_t M,
+                                     int64_t N, int64_t K, uint16_t* c_bf16, void* workspace,
+                                     int64_t workspace_bytes, hipStream_t stream);
 
 /*
  * w8a8_block_gemm_grouped -- the FP8 W8A8 linear layer of a mixture of

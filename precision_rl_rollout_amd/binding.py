@@ -36,6 +36,9 @@ _SIGNATURES = {
     "fp8_kv_scale_recalibrate": [_P, _I64, _I64, _P, _P],
     "fp8_kv_cache_write": [_P, _P, _I64, _I64, _P, _P, _I64, _P],
     "tis_token_weights": [_P, _P, _P, _I64, _I64, ctypes.c_float, ctypes.c_int, _P, _P, _P, _P],
+    "w8a8_gemm_workspace_size": [_I64, _I64, _I64, _P],
+    "w8a8_block_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
+    "w8a8_int8_channel_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
 }
 
 IS_TRUNCATE = 0     # TIS: min(ratio, cap)
@@ -45,7 +48,7 @@ _lib = None
 
 # PRR_ABI_VERSION of the signatures below; a library of another version is
 # refused at load time.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class PrrError(RuntimeError):
@@ -152,8 +155,41 @@ def fp8_act_token_quant(a: torch.Tensor, out=None, scale=None):
     return q, s
 
 
-def w8a8_block_gemm(a_fp8, a_scale, w_fp8, w_scale, out=None):
-    """FP8 codes + block scales -> C [M, N] bf16."""
+_ws_sizes: dict = {}
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace (bytes) the _ws GEMM calls use for this shape on the current
+    device; 0 when the one-pass kernels are used.  (Remembered per device
+    and shape: the answer depends only on them.)"""
+    key = (torch.cuda.current_device(), int(M), int(N), int(K))
+    if key not in _ws_sizes:
+        n = ctypes.c_int64(0)
+        _check("w8a8_gemm_workspace_size",
+               load().w8a8_gemm_workspace_size(int(M), int(N), int(K), ctypes.addressof(n)))
+        _ws_sizes[key] = int(n.value)
+    return _ws_sizes[key]
+
+
+def _workspace(workspace, M, N, K, like):
+    """workspace="auto": a buffer of the size the library asks for (none if
+    it asks for none); None: no workspace; a uint8 CUDA tensor: used as is."""
+    if workspace is None:
+        return None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace: 'auto', None or a uint8 CUDA tensor")
+        n = gemm_workspace_bytes(M, N, K) if M > 0 and N > 0 and K > 0 else 0
+        return torch.empty((n,), dtype=torch.uint8, device=like.device) if n else None
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace: expected a contiguous CUDA uint8 tensor")
+    return workspace
+
+
+def w8a8_block_gemm(a_fp8, a_scale, w_fp8, w_scale, out=None, workspace="auto"):
+    """FP8 codes + block scales -> C [M, N] bf16.  With a workspace (by
+    default one of the size the library asks for), decode-sized batches of
+    narrow or long-K layers are split over K (w8a8_block_gemm_ws)."""
     M, K = a_fp8.shape
     N = w_fp8.shape[0]
     _operand(a_fp8, torch.uint8, (M, K), "a_fp8")
@@ -161,9 +197,15 @@ def w8a8_block_gemm(a_fp8, a_scale, w_fp8, w_scale, out=None):
     _operand(a_scale, torch.float32, (M, _cdiv(K, 128)), "a_scale")
     _operand(w_scale, torch.float32, (_cdiv(N, 128), _cdiv(K, 128)), "w_scale")
     c = _out(out, torch.bfloat16, (M, N), a_fp8, "out")
-    _check("w8a8_block_gemm",
-           load().w8a8_block_gemm(_ptr(a_fp8), _ptr(a_scale), _ptr(w_fp8), _ptr(w_scale),
-                                  M, N, K, _ptr(c), _stream(a_fp8)))
+    ws = _workspace(workspace, M, N, K, a_fp8)
+    if ws is None:
+        _check("w8a8_block_gemm",
+               load().w8a8_block_gemm(_ptr(a_fp8), _ptr(a_scale), _ptr(w_fp8), _ptr(w_scale),
+                                      M, N, K, _ptr(c), _stream(a_fp8)))
+    else:
+        _check("w8a8_block_gemm_ws",
+               load().w8a8_block_gemm_ws(_ptr(a_fp8), _ptr(a_scale), _ptr(w_fp8), _ptr(w_scale),
+                                         M, N, K, _ptr(c), _ptr(ws), ws.numel(), _stream(a_fp8)))
     return c
 
 
@@ -189,8 +231,9 @@ def int8_act_token_quant(a: torch.Tensor, out=None, scale=None):
     return q, s
 
 
-def w8a8_int8_channel_gemm(a_i8, a_scale, w_i8, w_scale, out=None):
-    """INT8 codes + per-row / per-channel scales -> C [M, N] bf16."""
+def w8a8_int8_channel_gemm(a_i8, a_scale, w_i8, w_scale, out=None, workspace="auto"):
+    """INT8 codes + per-row / per-channel scales -> C [M, N] bf16 (workspace
+    as w8a8_block_gemm)."""
     M, K = a_i8.shape
     N = w_i8.shape[0]
     _operand(a_i8, torch.int8, (M, K), "a_i8")
@@ -198,9 +241,16 @@ def w8a8_int8_channel_gemm(a_i8, a_scale, w_i8, w_scale, out=None):
     _operand(a_scale, torch.float32, (M,), "a_scale")
     _operand(w_scale, torch.float32, (N,), "w_scale")
     c = _out(out, torch.bfloat16, (M, N), a_i8, "out")
-    _check("w8a8_int8_channel_gemm",
-           load().w8a8_int8_channel_gemm(_ptr(a_i8), _ptr(a_scale), _ptr(w_i8), _ptr(w_scale),
-                                         M, N, K, _ptr(c), _stream(a_i8)))
+    ws = _workspace(workspace, M, N, K, a_i8)
+    if ws is None:
+        _check("w8a8_int8_channel_gemm",
+               load().w8a8_int8_channel_gemm(_ptr(a_i8), _ptr(a_scale), _ptr(w_i8),
+                                             _ptr(w_scale), M, N, K, _ptr(c), _stream(a_i8)))
+    else:
+        _check("w8a8_int8_channel_gemm_ws",
+               load().w8a8_int8_channel_gemm_ws(_ptr(a_i8), _ptr(a_scale), _ptr(w_i8),
+                                                _ptr(w_scale), M, N, K, _ptr(c), _ptr(ws),
+                                                ws.numel(), _stream(a_i8)))
     return c
 
 

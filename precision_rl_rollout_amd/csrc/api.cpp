@@ -160,6 +160,55 @@ prr_status w8a8_int8_channel_gemm(const int8_t* a_i8, const float* a_scale, cons
       prr::launch_w8a8_int8_channel_gemm(a_i8, a_scale, w_i8, w_scale, M, N, K, c_bf16, stream));
 }
 
+prr_status w8a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* bytes) {
+  if (bytes == nullptr) return PRR_ERR_INVALID_ARG;
+  *bytes = 0;
+  PRR_TRY(check_dims(M, N, K));
+  if (K % 128 != 0) return PRR_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0 || N == 0 || K == 0) return PRR_OK;
+  PRR_TRY(check_device());
+  prr::SplitPlan plan;
+  if (prr::splitk_plan(M, N, K, &plan)) *bytes = plan.bytes;
+  return PRR_OK;
+}
+
+prr_status w8a8_block_gemm_ws(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                              const float* w_scale, int64_t M, int64_t N, int64_t K,
+                              uint16_t* c_bf16, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream) {
+  if (workspace_bytes < 0) return PRR_ERR_INVALID_ARG;
+  if (workspace != nullptr && workspace_bytes > 0 && M > 0 && N > 0)
+    PRR_TRY(check_ptrs({workspace}));
+  PRR_TRY(gemm_common(a_fp8, a_scale, w_fp8, w_scale, M, N, K, c_bf16, false));
+  if (M == 0 || N == 0) return PRR_OK;
+  hipError_t err = hipSuccess;
+  if (K > 0 && prr::launch_gemm_decode_splitk<false>(a_fp8, a_scale, w_fp8, w_scale, M, N, K,
+                                                      static_cast<float*>(workspace),
+                                                      workspace_bytes, c_bf16, stream, &err))
+    return from_hip(err);
+  return from_hip(
+      prr::launch_w8a8_block_gemm(a_fp8, a_scale, w_fp8, w_scale, M, N, K, c_bf16, stream));
+}
+
+prr_status w8a8_int8_channel_gemm_ws(const int8_t* a_i8, const float* a_scale,
+                                     const int8_t* w_i8, const float* w_scale, int64_t M,
+                                     int64_t N, int64_t K, uint16_t* c_bf16, void* workspace,
+                                     int64_t workspace_bytes, hipStream_t stream) {
+  if (workspace_bytes < 0) return PRR_ERR_INVALID_ARG;
+  if (workspace != nullptr && workspace_bytes > 0 && M > 0 && N > 0)
+    PRR_TRY(check_ptrs({workspace}));
+  PRR_TRY(gemm_common(a_i8, a_scale, w_i8, w_scale, M, N, K, c_bf16, true));
+  if (M == 0 || N == 0) return PRR_OK;
+  hipError_t err = hipSuccess;
+  if (K > 0 && prr::launch_gemm_decode_splitk<true>(
+                   reinterpret_cast<const uint8_t*>(a_i8), a_scale,
+                   reinterpret_cast<const uint8_t*>(w_i8), w_scale, M, N, K,
+                   static_cast<float*>(workspace), workspace_bytes, c_bf16, stream, &err))
+    return from_hip(err);
+  return from_hip(
+      prr::launch_w8a8_int8_channel_gemm(a_i8, a_scale, w_i8, w_scale, M, N, K, c_bf16, stream));
+}
+
 prr_status w8a8_block_gemm_grouped(const uint8_t* a_fp8, const float* a_scale,
                                    const uint8_t* w_fp8, const float* w_scale,
                                    const int64_t* expert_offsets, int64_t E, int64_t M, int64_t N,

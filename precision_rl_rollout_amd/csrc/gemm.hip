@@ -63,6 +63,14 @@ template <> struct SkinnyPick<2> { using type = SkinnyCfg<2, 4, 4, 2>; };
 template <> struct SkinnyPick<3> { using type = SkinnyCfg<3, 4, 4, 2>; };
 template <> struct SkinnyPick<4> { using type = SkinnyCfg<4, 4, 2, 2>; };
 
+// Narrow layers (few output channels, long K: e.g. a down projection, N 5120
+// x K 27648): the configurations above give a workgroup 32-128 channels,
+// which leaves most CUs idle when N is small (40 workgroups for 5120
+// channels at MT 4).  Here a workgroup takes one 16-channel strip with K
+// split over its 4 waves and a 4-deep ring, so there is one workgroup per
+// strip; each re-reads the activations (M x K from L2) once.
+template <int MT> struct SkinnyNarrow { using type = SkinnyCfg<MT, 1, 4, 4>; };
+
 template <class Cfg, bool kInt8>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
@@ -340,24 +348,17 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
     if (launch_gemm_decode<kInt8>(A, sa, W, sw, M, N, K, C, stream, &err)) return err;
   }
   // The skinny kernel addresses A and one 128-row weight slab with 32-bit
-  // buffer offsets.
+  // buffer offsets; its FP8 activation scales (MT x 16 rows x K/128) are
+  // staged in LDS.  Above 64 rows the many-token kernel (128-wide tiles when
+  // few) is faster.
   const int64_t mt16 = (M + 15) / 16 * 16;
-  // Above 64 rows the many-token kernel (128-wide tiles when few) is faster.
-  if (M <= 64 && 128 * K < kOutOfRange &&
-      (kInt8 || mt16 * (K / kBlock) <= kSkinnyLdsScales)) {
+  const size_t skinny_scales = kInt8 ? 0 : (size_t)mt16 * (K / kBlock) * sizeof(float);
+  if (M <= 64 && 128 * K < kOutOfRange && M * K < kOutOfRange &&
+      skinny_scales <= (size_t)kSkinnyLdsBytes) {
     const int mt = (int)((M + 15) / 16);
-#define PRR_SKINNY(X)                                                                        \
-  case X: {                                                                                  \
-    using Cfg = typename SkinnyPick<X>::type;                                                \
-    const unsigned grid = (unsigned)((N + Cfg::kCols - 1) / Cfg::kCols);                    \
-    const size_t lds_scales = kInt8 ? 0 : (size_t)(X * 16) * (K / kBlock) * sizeof(float);  \
-    const size_t lds_red =                                                                   \
-        Cfg::kKS > 1 ? (size_t)4 * Cfg::kS * X * 4 * 64 * sizeof(float) : 0;               \
-    const size_t lds = lds_scales > lds_red ? lds_scales : lds_red;                         \
-    hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, kInt8>), dim3(grid), dim3(256), lds, stream, \
-                       A, sa, W, sw, M, N, K, C);                                            \
-    break;                                                                                   \
-  }
+    const int cus = compute_units();
+#define PRR_SKINNY_LAUNCH(CFG, X)                                                              {                                                                                              using Cfg = CFG;                                                                             const unsigned grid = (unsigned)((N + Cfg::kCols - 1) / Cfg::kCols);                        const size_t lds_red =                                                                           Cfg::kKS > 1 ? (size_t)4 * Cfg::kS * X * 4 * 64 * sizeof(float) : 0;                   const size_t lds = skinny_scales > lds_red ? skinny_scales : lds_red;                       hipLaunchKernelGGL((gemm_skinny_kernel<Cfg, kInt8>), dim3(grid), dim3(256), lds, stream,                        A, sa, W, sw, M, N, K, C);                                              }
+#define PRR_SKINNY(X)                                                                          case X:                                                                                        if ((N + SkinnyPick<X>::type::kCols - 1) / SkinnyPick<X>::type::kCols < cus)                   PRR_SKINNY_LAUNCH(typename SkinnyNarrow<X>::type, X)                                       else                                                                                           PRR_SKINNY_LAUNCH(typename SkinnyPick<X>::type, X)                                         break;
     switch (mt) {
       PRR_SKINNY(1)
       PRR_SKINNY(2)
@@ -367,6 +368,7 @@ static hipError_t launch_gemm(const uint8_t* A, const float* sa, const uint8_t* 
         return hipErrorInvalidValue;
     }
 #undef PRR_SKINNY
+#undef PRR_SKINNY_LAUNCH
     return hipGetLastError();
   }
   {

@@ -41,6 +41,7 @@
 // FP8: per K block, C += sa[m, kb] * sw[n / 128, kb] * MFMA(Wq, Aq) (one
 // v_mfma_f32_16x16x128_f8f6f4 per block, zero accumulator).  INT8: the
 // int32 MFMA accumulates the wave's whole piece; scales in the epilogue.
+#include <algorithm>
 #include <atomic>
 
 #include "launch.h"
@@ -71,17 +72,42 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef DecodeSlot DecodeRing[kDecodeWaves][kDecodeRing];
 
+// Four fp32 values for P[m, n..n+3], bounds-checked.
+__device__ __forceinline__ void store_partial4(float* P, int64_t M, int64_t N, int64_t m,
+                                               int64_t n, const float v[4]) {
+  if (m >= M) return;
+  float* p = P + m * N + n;
+  if (n + 3 < N && (N & 3) == 0) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) p[r] = v[r];
+  }
+}
+
+// The K range of a segment: K/128 blocks starting at block kb_first of
+// activation and weight rows that are ld bytes long, whose scale rows hold
+// KBs blocks.  A whole layer is {K, 0, K/128}.
+struct KSlice {
+  int ld, kb_first, KBs;
+};
+
 // One segment: the M (<= MT * 16) activation rows at A against the strips
-// first, first + step, ... (n_strips of them) of the weight W [N, K]; the
-// output rows go to C [M, N].  P: K blocks of the wave's piece held in
-// registers (>= ceil(K/128 / 8)).  Every wave of the workgroup calls it with
-// the same arguments; it starts with a barrier (a previous segment's waves
-// may still read the LDS it rewrites) and ends with its loads drained.
-template <int MT, int P, bool kInt8>
+// first, first + step, ... (n_strips of them) of the weight W [N, ld], over
+// the K blocks of `ks` (K bytes of each row).  The output rows go to C
+// [M, N] as bf16, or, with kPartial, to Pout [M, N] as fp32 partial sums
+// (FP8: scaled; INT8: the raw int32 accumulators, bit-cast).  P: K blocks
+// of the wave's piece held in registers (>= ceil(K/128 / 8)).  Every wave
+// of the workgroup calls it with the same arguments; it starts with a
+// barrier (a previous segment's waves may still read the LDS it rewrites)
+// and ends with its loads drained.
+template <int MT, int P, bool kInt8, bool kPartial = false>
 __device__ __forceinline__ void decode_segment(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
-    const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int first,
-    int step, int n_strips, DecodeRing& ring, float* lds_dyn) {
+    const float* __restrict__ sw, int M, int N, int K, KSlice ks, uint16_t* __restrict__ C,
+    float* __restrict__ Pout, int first, int step, int n_strips, DecodeRing& ring,
+    float* lds_dyn) {
   constexpr int R = kDecodeRing;
   lds_barrier();
   const int lane = threadIdx.x & 63;
@@ -104,18 +130,19 @@ __device__ __forceinline__ void decode_segment(
   // slot: row 8 h + l / 8, slot position l % 8, i.e. global chunk
   // (l % 8) ^ ((row >> 1) & 7).
   const int NB = (N + kBlock - 1) / kBlock;
-  const v4i rsw = sgpr_rsrc(sw, kInt8 ? (int64_t)N * 4 : (int64_t)NB * KB * 4);
+  const int ld = ks.ld, kbf = ks.kb_first;
+  const v4i rsw = sgpr_rsrc(sw, kInt8 ? (int64_t)N * 4 : (int64_t)NB * ks.KBs * 4);
   const int lrow0 = lane >> 3, lrow1 = lrow0 + 8;
-  const int lofs0 = lrow0 * K + (((lane & 7) ^ ((lrow0 >> 1) & 7)) << 4);
-  const int lofs1 = lrow1 * K + (((lane & 7) ^ ((lrow1 >> 1) & 7)) << 4);
+  const int lofs0 = lrow0 * ld + (((lane & 7) ^ ((lrow0 >> 1) & 7)) << 4);
+  const int lofs1 = lrow1 * ld + (((lane & 7) ^ ((lrow1 >> 1) & 7)) << 4);
   auto load_task = [&](int t) {
     const int i = t / P, j = t - i * P;
     const bool live = i < my_n;
     const int n0 = strip_n0(live ? i : 0);
     const int rows = live ? min(16, N - n0) : 0;   // rows past N read zeros
-    const v4i rw = sgpr_rsrc(W + (int64_t)n0 * K, (int64_t)rows * K);
+    const v4i rw = sgpr_rsrc(W + (int64_t)n0 * ld, (int64_t)rows * ld);
     const bool jl = j < pw;
-    const int kofs = (kb0 + j) * kBlock;
+    const int kofs = (kbf + kb0 + j) * kBlock;
     DecodeSlot& sl = ring[wave][t % R];
     dma_b128(rw, lds_addr(sl.w), jl ? lofs0 + kofs : kOutOfRange, 0);
     dma_b128(rw, lds_addr(sl.w + 1024), jl ? lofs1 + kofs : kOutOfRange, 0);
@@ -123,7 +150,7 @@ __device__ __forceinline__ void decode_segment(
     if constexpr (kInt8)
       vs = (live && j == 0 && lane < 16 && n0 + lane < N) ? (n0 + lane) * 4 : kOutOfRange;
     else
-      vs = (live && jl && lane == 0) ? ((n0 >> 7) * KB + kb0 + j) * 4 : kOutOfRange;
+      vs = (live && jl && lane == 0) ? ((n0 >> 7) * ks.KBs + kbf + kb0 + j) * 4 : kOutOfRange;
     dma_b32(rsw, lds_addr(sl.s), vs);
   };
   constexpr int kLoadsPerTask = 3;
@@ -135,14 +162,14 @@ __device__ __forceinline__ void decode_segment(
   for (int q = 0; q < R - 1; ++q) load_task(q);
 
   // Resident activation fragments of all m-tiles for this wave's K piece.
-  const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(A, (int64_t)M * K);
+  const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(A, (int64_t)M * ld);
   v8i afr[MT][P];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int j = 0; j < P; ++j) {
       const int m = mt * 16 + r16;
-      const int off = (j < pw) ? m * K + (kb0 + j) * kBlock + g * 16 : kOutOfRange;
+      const int off = (j < pw) ? m * ld + (kbf + kb0 + j) * kBlock + g * 16 : kOutOfRange;
       afr[mt][j] = buffer_load32(ares, off, 0);
     }
 
@@ -162,7 +189,8 @@ __device__ __forceinline__ void decode_segment(
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int e = threadIdx.x + u * kDecodeThreads;
-      v[u] = (e < kRows * KB && e / KB < M) ? sa[e] : 0.f;
+      const int m = e / KB;
+      v[u] = (e < kRows * KB && m < M) ? sa[m * ks.KBs + kbf + (e - m * KB)] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -214,6 +242,33 @@ __device__ __forceinline__ void decode_segment(
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) q[w] = red[w][mt][lane];
     float v[4];
+    if constexpr (kPartial) {
+      if constexpr (kInt8) {
+        int32_t t[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < kDecodeWaves; ++w) {
+          t[0] += __float_as_int(q[w].x);
+          t[1] += __float_as_int(q[w].y);
+          t[2] += __float_as_int(q[w].z);
+          t[3] += __float_as_int(q[w].w);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = __int_as_float(t[r]);
+      } else {
+        float f[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kDecodeWaves; ++w) {
+          f[0] += q[w].x;
+          f[1] += q[w].y;
+          f[2] += q[w].z;
+          f[3] += q[w].w;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = f[r];
+      }
+      store_partial4(Pout, M, N, m, n, v);
+      return;
+    }
     if constexpr (kInt8) {
       int32_t t[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -340,7 +395,58 @@ __global__ __launch_bounds__(512) void gemm_decode_kernel(
   // the vector unit, so the compiler needs telling.
   const int l = (G & 31) == 0 ? (((b >> 5) << 5) | ((b & 7) << 2) | ((b >> 3) & 3)) : b;
   const int my_n = __builtin_amdgcn_readfirstlane((nstrips - l + G - 1) / G);
-  decode_segment<MT, P, kInt8>(A, sa, W, sw, M, N, K, C, l, G, my_n, ring, lds_dyn);
+  decode_segment<MT, P, kInt8>(A, sa, W, sw, M, N, K, KSlice{K, 0, K / kBlock}, C, nullptr, l, G,
+                               my_n, ring, lds_dyn);
+}
+
+// Split-K decode (a caller-provided workspace): the K blocks are cut into
+// S slices; workgroup b works on slice b % S, with its activations for that
+// slice resident, over the strips (b / S) + i (G / S), and writes fp32
+// partial sums (INT8: int32 accumulators) to workspace slice s [M, N].  A
+// second kernel adds the S slices in order and rounds to bf16.  Used where
+// one workgroup per strip over all of K would leave CUs idle (few output
+// channels) or cannot hold the activations (long K): every CU then reads
+// only its slice of the activations, and there are S times more work items.
+template <int MT, int P, bool kInt8>
+__global__ __launch_bounds__(512) void gemm_decode_splitk_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, int M, int N, int K, int S, int nstrips,
+    float* __restrict__ ws) {
+  __shared__ __align__(16) DecodeRing ring;
+  extern __shared__ __align__(16) float lds_dyn[];
+  const int b = blockIdx.x;
+  const int s = __builtin_amdgcn_readfirstlane(b % S);
+  const int q = __builtin_amdgcn_readfirstlane(b / S);
+  const int GQ = (int)gridDim.x / S;
+  const int KB = K / kBlock;
+  const int kb_first = __builtin_amdgcn_readfirstlane((int)((int64_t)s * KB / S));
+  const int kb_end = __builtin_amdgcn_readfirstlane((int)((int64_t)(s + 1) * KB / S));
+  const int my_n = __builtin_amdgcn_readfirstlane((nstrips - q + GQ - 1) / GQ);
+  decode_segment<MT, P, kInt8, true>(A, sa, W, sw, M, N, (kb_end - kb_first) * kBlock,
+                                     KSlice{K, kb_first, KB}, nullptr,
+                                     ws + (int64_t)s * M * N, q, GQ, my_n, ring, lds_dyn);
+}
+
+// C = bf16(sum over s of ws[s]) in slice order; INT8 adds the int32 slices
+// exactly and applies sa[m] sw[n] as the one-pass kernel does.
+template <bool kInt8>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(
+    const float* __restrict__ ws, int S, int64_t M, int64_t N, const float* __restrict__ sa,
+    const float* __restrict__ sw, uint16_t* __restrict__ C) {
+  const int64_t MN = M * N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= MN) return;
+  float v;
+  if constexpr (kInt8) {
+    int32_t t = 0;
+    for (int k = 0; k < S; ++k) t += __float_as_int(ws[k * MN + i]);
+    const int64_t m = i / N, n = i - m * N;
+    v = (float)t * (sa[m] * sw[n]);
+  } else {
+    v = 0.f;
+    for (int k = 0; k < S; ++k) v += ws[k * MN + i];
+  }
+  C[i] = (uint16_t)f32_to_bf16_rne(v);
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
@@ -453,8 +559,9 @@ __global__ __launch_bounds__(512) void gemm_grouped_kernel(
           if (x >= y) continue;
           const int rows = (int)min<int64_t>(kChunk, er1 - row0);
           decode_segment<MT, P, false>(A + row0 * K, sa + row0 * KB, W + (int64_t)e * N * K,
-                                       sw + (int64_t)e * NB * KB, rows, N, K, C + row0 * N,
-                                       (int)(x - base), 1, (int)(y - x), ring, lds_dyn);
+                                       sw + (int64_t)e * NB * KB, rows, N, K, KSlice{K, 0, KB},
+                                       C + row0 * N, nullptr, (int)(x - base), 1, (int)(y - x),
+                                       ring, lds_dyn);
         }
       }
     }
@@ -511,6 +618,94 @@ static bool launch_decode_mt(const uint8_t* A, const float* sa, const uint8_t* W
 #undef PRR_DECODE_P
   return false;
 }
+
+// Split-K plan (one rule for FP8 and INT8, so that the workspace size does
+// not depend on the type): for M <= 64, when one pass cannot hold the
+// activations (more than 8 Pmax K blocks), or when M > 16 and the layer has
+// fewer strips than twice the CUs, cut K into S slices: enough for the register budget, and about 4 work
+// items per CU, with at least 8 K blocks per slice.  G workgroups, a multiple
+// of S; the workspace is S x M x N fp32.
+bool splitk_plan(int64_t M, int64_t N, int64_t K, SplitPlan* plan) {
+  if (M < 1 || M > 64 || N < 1 || K < kBlock || K % kBlock != 0) return false;
+  if (128 * K >= 0x7FFFFF00LL || N > 0x1FFFFFF0LL || 64 * K >= 0x7FFFFF00LL) return false;
+  const int64_t KB = K / kBlock;
+  if (4 * ((N + kBlock - 1) / kBlock) * KB >= 0x7FFFFF00LL) return false;
+  const int mt = (int)((M + 15) / 16);
+  const int MT = mt <= 2 ? mt : 4;
+  const int64_t pmax = MT <= 2 ? 8 : 6;
+  const int64_t nstrips = (N + 15) / 16;
+  const int cus = compute_units();
+  const bool one_pass = (KB + kDecodeWaves - 1) / kDecodeWaves <= pmax;
+  // (At M <= 16 the one-pass kernel's start-up is short, and the second
+  // launch of the split costs more than the idle CUs on narrow layers.)
+  if (one_pass && (nstrips >= 2 * cus || M <= 16)) return false;
+  const int64_t s_regs = (KB + kDecodeWaves * pmax - 1) / (kDecodeWaves * pmax);
+  const int64_t s_bal = (4 * cus + nstrips - 1) / nstrips;
+  int64_t S = std::max(s_regs, s_bal);
+  S = std::min<int64_t>(S, std::min<int64_t>(KB / kDecodeWaves, 32));
+  if (S < 2 || S < s_regs) return false;
+  const int64_t kbs = (KB + S - 1) / S;                 // longest slice
+  const size_t lds = ((size_t)2 * kDecodeWaves * MT * 4 * 64 + (size_t)MT * 16 * kbs) * sizeof(float);
+  if (lds + sizeof(DecodeSlot) * kDecodeWaves * kDecodeRing > (size_t)kLdsBytes) return false;
+  if (M * N * S > (int64_t)1 << 40) return false;
+  plan->S = (int)S;
+  plan->G = std::max<int>((int)S, cus / (int)S * (int)S);
+  plan->MT = MT;
+  plan->pw = (int)((kbs + kDecodeWaves - 1) / kDecodeWaves);
+  plan->bytes = M * N * S * (int64_t)sizeof(float);
+  return true;
+}
+
+template <int MT, bool kInt8>
+static bool launch_splitk_mt(const uint8_t* A, const float* sa, const uint8_t* W,
+                             const float* sw, int64_t M, int64_t N, int64_t K, float* ws,
+                             const SplitPlan& pl, uint16_t* C, hipStream_t stream,
+                             hipError_t* err) {
+  const int KB = (int)(K / kBlock);
+  const int kbs = (KB + pl.S - 1) / pl.S;
+  const int nstrips = (int)((N + 15) / 16);
+  const size_t lds = ((size_t)2 * kDecodeWaves * MT * 4 * 64 + (kInt8 ? 0 : (size_t)MT * 16 * kbs)) *
+                     sizeof(float);
+  bool launched = false;
+#define PRR_SPLIT_P(PV)                                                                         if (!launched && pl.pw <= PV) {                                                                 hipLaunchKernelGGL((gemm_decode_splitk_kernel<MT, PV, kInt8>), dim3(pl.G), dim3(512), lds,                        stream, A, sa, W, sw, (int)M, (int)N, (int)K, pl.S, nstrips, ws);           launched = true;                                                                            }
+  PRR_SPLIT_P(2)
+  PRR_SPLIT_P(3)
+  PRR_SPLIT_P(4)
+  PRR_SPLIT_P(5)
+  PRR_SPLIT_P(6)
+  if constexpr (MT <= 2) {
+    PRR_SPLIT_P(8)
+  }
+#undef PRR_SPLIT_P
+  if (!launched) return false;
+  const int64_t MN = M * N;
+  hipLaunchKernelGGL((gemm_splitk_reduce_kernel<kInt8>), dim3((unsigned)((MN + 255) / 256)),
+                     dim3(256), 0, stream, ws, pl.S, M, N, sa, sw, C);
+  *err = hipGetLastError();
+  return true;
+}
+
+template <bool kInt8>
+bool launch_gemm_decode_splitk(const uint8_t* A, const float* sa, const uint8_t* W,
+                               const float* sw, int64_t M, int64_t N, int64_t K, float* ws,
+                               int64_t ws_bytes, uint16_t* C, hipStream_t stream,
+                               hipError_t* err) {
+  SplitPlan pl;
+  if (ws == nullptr || !splitk_plan(M, N, K, &pl) || ws_bytes < pl.bytes) return false;
+  switch (pl.MT) {
+    case 1: return launch_splitk_mt<1, kInt8>(A, sa, W, sw, M, N, K, ws, pl, C, stream, err);
+    case 2: return launch_splitk_mt<2, kInt8>(A, sa, W, sw, M, N, K, ws, pl, C, stream, err);
+    case 4: return launch_splitk_mt<4, kInt8>(A, sa, W, sw, M, N, K, ws, pl, C, stream, err);
+    default: return false;
+  }
+}
+
+template bool launch_gemm_decode_splitk<false>(const uint8_t*, const float*, const uint8_t*,
+                                               const float*, int64_t, int64_t, int64_t, float*,
+                                               int64_t, uint16_t*, hipStream_t, hipError_t*);
+template bool launch_gemm_decode_splitk<true>(const uint8_t*, const float*, const uint8_t*,
+                                              const float*, int64_t, int64_t, int64_t, float*,
+                                              int64_t, uint16_t*, hipStream_t, hipError_t*);
 
 template <bool kInt8>
 bool launch_gemm_decode(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,

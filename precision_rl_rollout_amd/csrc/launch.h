@@ -35,6 +35,23 @@ hipError_t launch_tis_token_weights(const float* lp_train, const float* lp_rollo
                                     float lncap, int mode, float* w, float* row_stats,
                                     double* totals, hipStream_t stream);
 
+// Split-K decode GEMM plan: S K-slices, G workgroups, MT m-tiles, pw K
+// blocks per wave, `bytes` of fp32 workspace.  False: no split for this
+// shape (the one-pass kernels handle it).
+struct SplitPlan {
+  int S, G, MT, pw;
+  int64_t bytes;
+};
+bool splitk_plan(int64_t M, int64_t N, int64_t K, SplitPlan* plan);
+
+// Split-K decode GEMM into the caller's workspace; false if the shape has no
+// split plan or the workspace is missing or too small (nothing launched).
+template <bool kInt8>
+bool launch_gemm_decode_splitk(const uint8_t* A, const float* sa, const uint8_t* W,
+                               const float* sw, int64_t M, int64_t N, int64_t K, float* ws,
+                               int64_t ws_bytes, uint16_t* C, hipStream_t stream,
+                               hipError_t* err);
+
 // Compute units of the current device (cached per device; 256 if unknown).
 int compute_units();
 

@@ -84,9 +84,9 @@ __device__ __forceinline__ v8i buffer_load32(__amdgpu_buffer_rsrc_t r, int voff,
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Activation scales of a skinny problem staged in LDS (floats): M <= 128
-// tokens by up to 64 K blocks (K <= 8192), or fewer tokens by more blocks.
-constexpr int kSkinnyLdsScales = 128 * 64;
+// LDS the skinny kernel may use for its staged FP8 activation scales
+// (64 rows x K/128 floats: K up to 81,920 at 64 rows).
+constexpr int kSkinnyLdsBytes = 160 * 1024;
 
 __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int voff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));

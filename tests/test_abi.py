@@ -10,6 +10,7 @@ Pointers passed here are never dereferenced: every call fails (or is empty)
 before the library reaches a launch.
 """
 
+import ctypes
 import os
 import re
 
@@ -41,7 +42,8 @@ def test_header_declares_the_boundary():
                      "int8_weight_channel_quant", "int8_act_token_quant",
                      "w8a8_int8_channel_gemm", "w8a8_block_gemm_grouped",
                      "fp8_kv_scale_recalibrate",
-                     "fp8_kv_cache_write", "tis_token_weights", "prr_status_string",
+                     "fp8_kv_cache_write", "tis_token_weights", "w8a8_gemm_workspace_size",
+                     "w8a8_block_gemm_ws", "w8a8_int8_channel_gemm_ws", "prr_status_string",
                      "prr_abi_version"}
 
 
@@ -195,3 +197,35 @@ def test_tis_no_device_is_reported():
                         None) == NO_DEVICE
     assert binding.call("tis_token_weights", None, None, None, 0, 8, 2.0, 0, None, None, FAKE,
                         None) == NO_DEVICE
+
+
+@pytest.mark.parametrize("fn", ["w8a8_block_gemm_ws", "w8a8_int8_channel_gemm_ws"])
+def test_gemm_ws_argument_checks(fn):
+    c = lambda *a: binding.call(fn, *a)
+    ok = [FAKE, FAKE, FAKE, FAKE, 16, 256, 256, FAKE, FAKE, 1024, None]
+    for i, v in ((4, -1), (5, -2), (6, -128), (9, -1)):
+        a = list(ok)
+        a[i] = v
+        assert c(*a) == INVALID
+    a = list(ok)
+    a[6] = 200
+    assert c(*a) == SHAPE
+    for i in (0, 1, 2, 3, 7):
+        a = list(ok)
+        a[i] = None
+        assert c(*a) == INVALID
+        a[i] = ODD
+        assert c(*a) == MISALIGNED
+    a = list(ok)
+    a[8] = ODD                                   # a workspace must be aligned too
+    assert c(*a) == MISALIGNED
+    assert c(None, None, None, None, 0, 256, 256, None, None, 0, None) == OK
+
+
+def test_workspace_size_argument_checks():
+    n = ctypes.c_int64(-1)
+    c = lambda *a: binding.call("w8a8_gemm_workspace_size", *a)
+    assert c(4, 8, 256, None) == INVALID
+    assert c(-1, 8, 256, ctypes.addressof(n)) == INVALID
+    assert c(4, 8, 200, ctypes.addressof(n)) == SHAPE
+    assert c(0, 8, 256, ctypes.addressof(n)) == OK and n.value == 0

@@ -92,6 +92,9 @@ GEMM_SHAPES = [(16, 256, 256), (5, 200, 384), (1, 16, 128), (17, 129, 256), (33,
                # a ragged strip inside the last quad, N not a multiple of 8
                # (element-wise row segments), quads followed by single strips
                (33, 16376, 256), (64, 16379, 384), (17, 20000, 512),
+               # long K, few channels (one strip per workgroup, K over 4 waves):
+               # every m-tile count, ragged N
+               (5, 300, 16384), (33, 1000, 20480), (64, 2000, 12800), (20, 777, 10240),
                # many-token kernel (256 x 256 tiles): odd K-block count over a
                # 3 x 4 tile grid, a single K block over 9 x 2 tiles, 4 x 4 tiles
                (513, 777, 1152), (2304, 512, 128), (1024, 1024, 256)]
@@ -155,6 +158,45 @@ def test_full_7b_decode_upgate():
     _check(_gpu_fp8(p["A"], p["Wt"]), _ref_fp8(p["A"], p["Wt"]), "7B up/gate fp8")
     announce("w8a8_int8_channel_gemm full 7B decode up/gate")
     _check(_gpu_int8(p["A"], p["Wt"]), _ref_int8(p["A"], p["Wt"]), "7B up/gate int8")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 640, 5120), (5, 300, 16384), (24, 300, 8192),
+                                   (64, 5120, 5120), (1, 5120, 27648), (40, 2000, 12800)])
+def test_split_k_and_one_pass_agree(M, N, K):
+    """Shapes the library splits over K when given a workspace: the split
+    and the one-pass result both meet the oracle; a workspace below the
+    size asked for gives the one-pass result bit for bit; the split is
+    repeatable bit for bit."""
+    assert binding.gemm_workspace_bytes(M, N, K) > 0
+    p = workloads.gemm_problem(M, N, K, outliers=True, seed=M + N)
+    a_dev, w_dev = bits_to_dev(p["A"]), bits_to_dev(p["Wt"])
+    for kind in ("fp8", "int8"):
+        if kind == "fp8":
+            aq, sa = binding.fp8_act_token_quant(a_dev)
+            wq, sw = binding.fp8_weight_block_quant(w_dev)
+            fn, ref = binding.w8a8_block_gemm, _ref_fp8(p["A"], p["Wt"])
+        else:
+            aq, sa = binding.int8_act_token_quant(a_dev)
+            wq, sw = binding.int8_weight_channel_quant(w_dev)
+            fn, ref = binding.w8a8_int8_channel_gemm, _ref_int8(p["A"], p["Wt"])
+        announce(f"{kind} GEMM split-K vs one pass M{M} N{N} K{K}")
+        split = host(fn(aq, sa, wq, sw))
+        again = host(fn(aq, sa, wq, sw))
+        plain = host(fn(aq, sa, wq, sw, workspace=None))
+        small = host(fn(aq, sa, wq, sw, workspace=torch.empty(16, dtype=torch.uint8, device="cuda:0")))
+        _check(split, ref, f"split {kind} M{M} N{N} K{K}")
+        _check(plain, ref, f"one pass {kind} M{M} N{N} K{K}")
+        assert np.array_equal(split, again)
+        assert np.array_equal(small, plain)
+
+
+@pytest.mark.parametrize("M", [1, 64])
+def test_full_32b_down_projection_decode(M):
+    p = workloads.gemm_problem(M, 5120, 27648, True, seed=0, down=True)
+    announce(f"w8a8_block_gemm full 32B down projection M{M} N5120 K27648")
+    _check(_gpu_fp8(p["A"], p["Wt"]), _ref_fp8(p["A"], p["Wt"]), f"32B down M{M} fp8")
+    announce(f"w8a8_int8_channel_gemm full 32B down projection M{M}")
+    _check(_gpu_int8(p["A"], p["Wt"]), _ref_int8(p["A"], p["Wt"]), f"32B down M{M} int8")
 
 
 def test_full_32b_decode_sweep():
