@@ -428,25 +428,63 @@ __global__ __launch_bounds__(512) void gemm_decode_splitk_kernel(
 }
 
 // C = bf16(sum over s of ws[s]) in slice order; INT8 adds the int32 slices
-// exactly and applies sa[m] sw[n] as the one-pass kernel does.
+// exactly and applies sa[m] sw[n] as the one-pass kernel does.  A thread
+// takes 4 consecutive outputs (16-byte reads of every slice when N % 4 ==
+// 0, all issued before the adds; element by element otherwise).
+constexpr int kReduceSlices = 8;   // slice loads in flight per pass
+
 template <bool kInt8>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(
     const float* __restrict__ ws, int S, int64_t M, int64_t N, const float* __restrict__ sa,
     const float* __restrict__ sw, uint16_t* __restrict__ C) {
   const int64_t MN = M * N;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= MN) return;
-  float v;
-  if constexpr (kInt8) {
-    int32_t t = 0;
-    for (int k = 0; k < S; ++k) t += __float_as_int(ws[k * MN + i]);
-    const int64_t m = i / N, n = i - m * N;
-    v = (float)t * (sa[m] * sw[n]);
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i0 >= MN) return;
+  float f[4] = {0.f, 0.f, 0.f, 0.f};
+  int32_t t[4] = {0, 0, 0, 0};
+  if ((N & 3) == 0) {
+    for (int k0 = 0; k0 < S; k0 += kReduceSlices) {
+      float4 v[kReduceSlices];
+#pragma unroll
+      for (int u = 0; u < kReduceSlices; ++u)
+        v[u] = k0 + u < S ? *reinterpret_cast<const float4*>(ws + (k0 + u) * MN + i0)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < kReduceSlices; ++u) {
+        if (k0 + u >= S) break;
+        if constexpr (kInt8) {
+          t[0] += __float_as_int(v[u].x);
+          t[1] += __float_as_int(v[u].y);
+          t[2] += __float_as_int(v[u].z);
+          t[3] += __float_as_int(v[u].w);
+        } else {
+          f[0] += v[u].x;
+          f[1] += v[u].y;
+          f[2] += v[u].z;
+          f[3] += v[u].w;
+        }
+      }
+    }
   } else {
-    v = 0.f;
-    for (int k = 0; k < S; ++k) v += ws[k * MN + i];
+    for (int k = 0; k < S; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (i0 + r >= MN) break;
+        const float x = ws[k * MN + i0 + r];
+        if constexpr (kInt8) t[r] += __float_as_int(x); else f[r] += x;
+      }
   }
-  C[i] = (uint16_t)f32_to_bf16_rne(v);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t i = i0 + r;
+    if (i >= MN) break;
+    float v = f[r];
+    if constexpr (kInt8) {
+      const int64_t m = i / N, n = i - m * N;
+      v = (float)t[r] * (sa[m] * sw[n]);
+    }
+    C[i] = (uint16_t)f32_to_bf16_rne(v);
+  }
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
@@ -679,7 +717,7 @@ static bool launch_splitk_mt(const uint8_t* A, const float* sa, const uint8_t* W
 #undef PRR_SPLIT_P
   if (!launched) return false;
   const int64_t MN = M * N;
-  hipLaunchKernelGGL((gemm_splitk_reduce_kernel<kInt8>), dim3((unsigned)((MN + 255) / 256)),
+  hipLaunchKernelGGL((gemm_splitk_reduce_kernel<kInt8>), dim3((unsigned)((MN + 1023) / 1024)),
                      dim3(256), 0, stream, ws, pl.S, M, N, sa, sw, C);
   *err = hipGetLastError();
   return true;
