@@ -26,6 +26,11 @@ What it computes, with the passage each part follows:
   recalibrated every step, and quantize-on-write of token rows into cache
   slots (FP8-RL abstract, item (ii): FP8 KV cache with per-step QKV scale
   recalibration; granularity and write rule are readings, listed there).
+* ``oracle.attention`` -- decode attention over the FP8 KV cache: the
+  query quantized with its own per-tensor scale, scores and softmax in fp64
+  over the paged cache's codes, the output rounded once to bf16 (FP8-RL
+  abstract, item (ii): FP8 KV cache with per-step Q/K/V scales; the
+  attention details are readings, listed there).
 * ``oracle.gemm`` -- also the mixture-of-experts grouping of the FP8 layer:
   token rows sorted by expert, each group multiplied by its expert's weight
   (FP8-RL abstract: dense and MoE models).

@@ -35,11 +35,16 @@ _STREAMS = {
     "kv_K": 31, "kv_V": 32, "kv_K_cols": 33, "kv_V_cols": 34, "kv_slots": 35,
     "moe_A": 41, "moe_A_cols": 42, "moe_route": 43, "moe_W": 100,
     "tis_len": 51, "tis_lr": 52, "tis_d": 53, "tis_tail": 54,
+    "att_q": 61, "att_len": 62, "att_pages": 63, "att_codes": 64,
 }
 
 # Mixture-of-experts decode layer (a 30B-A3B-class model: 128 experts, top-8
 # routing, expert up/gate N = 2 x 768, hidden K = 2048), 128 decoding tokens.
 MOE_DECODE = dict(E=128, topk=8, tokens=128, N=1536, K=2048)
+
+# Decode attention over an FP8 KV cache of a 32B-class layer (40 query heads,
+# 8 KV heads of 128), 64 sequences of 1024-8192 cached tokens, 16-slot pages.
+ATT_32B = dict(B=64, Hq=40, Hkv=8, D=128, page=16, min_len=1024, max_len=8192)
 
 # Rollout-correction batch: 1024 responses of up to 8192 tokens, truncation
 # constant 2.
@@ -220,3 +225,39 @@ def tis_batch(B: int, T: int, seed: int = 0) -> dict:
     lr = np.where(mask != 0, lr, np.float32(0)).astype(np.float32)
     lt = np.where(mask != 0, lt, np.float32(0)).astype(np.float32)
     return dict(lp_train=lt, lp_rollout=lr, mask=mask)
+
+
+def att_lengths(B: int, lo: int, hi: int, seed: int = 0) -> np.ndarray:
+    """Cached tokens per sequence, uniform in [lo, hi] (the length mix of
+    long outputs)."""
+    return _rng(seed, "att_len").integers(lo, hi + 1, size=B).astype(np.int32)
+
+
+def att_block_table(seq_lens, page: int, seed: int = 0) -> tuple[np.ndarray, int]:
+    """A block table [B, max_blocks] int32 that gives every sequence its own
+    pages, taken from one seeded random permutation of the whole pool;
+    returns (table, num_slots).  Unused entries hold -1."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    need = (lens + page - 1) // page
+    total = int(need.sum())
+    perm = _rng(seed, "att_pages").permutation(max(total, 1)).astype(np.int32)
+    mb = int(max(1, need.max() if len(need) else 1))
+    table = np.full((len(lens), mb), -1, dtype=np.int32)
+    pos = 0
+    for b, k in enumerate(need):
+        table[b, :k] = perm[pos:pos + k]
+        pos += int(k)
+    return table, max(total, 1) * page
+
+
+def att_query(B: int, Hq: int, D: int, seed: int = 0) -> np.ndarray:
+    """The new token's queries, bf16 [B, Hq, D] (activation recipe, no
+    outlier channels)."""
+    return bf16_normal((B, Hq * D), 1.0, seed, "att_q").reshape(B, Hq, D)
+
+
+def att_random_codes(num_slots: int, C: int, seed: int = 0) -> np.ndarray:
+    """Cache contents for timing: uniform random finite e4m3 codes (every
+    byte but the two NaN codes), uint8 [num_slots, C]."""
+    r = _rng(seed, "att_codes").integers(0, 254, size=(num_slots, C), dtype=np.uint8)
+    return np.where(r >= 0x7F, r + 1, r).astype(np.uint8)    # skip 0x7F; 0xFF is never drawn
