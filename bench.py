@@ -25,7 +25,10 @@ GEMMs, TFLOP/s), ``stack32b_requant`` (FP8 and INT8 re-quantization of a
 recalibration and quantize-on-write of a 16,384-token prefill),
 ``moe_decode`` (a 128-expert top-8 decode layer: weight re-quantization of
 every expert, activation quantization, the grouped GEMM), ``tis_batch``
-(TIS and MIS token weights of 1024 responses padded to 8192 tokens).
+(TIS and MIS token weights of 1024 responses padded to 8192 tokens),
+``stack32b_gemm`` (the decode GEMMs of a 32B layer stack at M = 1 and 64),
+``att32b_decode`` (decode attention over an FP8 KV cache: 64 sequences of
+1024-8192 tokens, 40 query heads over 8 KV heads).
 """
 
 from __future__ import annotations
@@ -84,6 +87,7 @@ KERNEL_SOURCES = {
     "w8a8_int8_channel_gemm@decode7b_upgate": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
     "w8a8_block_gemm_grouped": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
     "tis_token_weights": ["tis.hip", "prr_device.h"],
+    "fp8_kv_decode_attention": ["attention.hip", "prr_device.h"],
     # M = 8192 runs the many-token kernel.
     "w8a8_block_gemm@prefill32b": ["gemm_prefill.hip", "mfma.h", "prr_device.h"],
     "w8a8_int8_channel_gemm@prefill32b": ["gemm_prefill.hip", "mfma.h", "prr_device.h"],
@@ -576,6 +580,64 @@ def run_moe_decode(args, torch, B, W):
     return line
 
 
+def run_att(args, torch, B, W):
+    """Decode attention over the FP8 KV cache of a 32B-class layer (40 query
+    heads over 8 KV heads of 128): 64 sequences of 1024-8192 cached tokens
+    in 16-slot pages taken in random order (604 MB of K and V codes, so no
+    step finds them in the 256 MB last-level cache)."""
+    cfg = W.ATT_32B
+    Bn, Hq, Hkv, D, page = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["page"]
+    lens = W.att_lengths(Bn, cfg["min_len"], cfg["max_len"], 0)
+    table, num_slots = W.att_block_table(lens, page, 0)
+    q_np = W.att_query(Bn, Hq, D, 0)
+    kc_np = W.att_random_codes(num_slots, Hkv * D, 0)
+    vc_np = W.att_random_codes(num_slots, Hkv * D, 1)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(q_np.reshape(Bn, -1).view(np.int16)).to(dev).view(Bn, Hq, D)
+    kc, vc = torch.from_numpy(kc_np).to(dev), torch.from_numpy(vc_np).to(dev)
+    tb, sl = torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev)
+    sq = B.fp8_kv_scale_recalibrate(q.view(Bn, -1))
+    sk = torch.tensor([2.0 ** -12], dtype=torch.float32, device=dev)
+    sv = torch.tensor([2.0 ** -8], dtype=torch.float32, device=dev)
+    out = torch.empty((Bn, Hq, D), dtype=torch.bfloat16, device=dev)
+    tokens = int(lens.sum())
+    work = (2 * tokens * Hkv * D + 4 * Bn * Hq * D + 4 * int(((lens + page - 1) // page).sum())
+            + 4 * Bn)
+
+    def step(_i, timer=None):
+        f = lambda: B.fp8_kv_decode_attention(q, sq, kc, vc, sk, sv, tb, sl, Hkv, page, out=out)
+        timer.run("fp8_kv_decode_attention", f) if timer else f()
+
+    dt, us, dom = timed_steps(torch, step, args)
+    line = {"metric": METRIC, "value": round(work / dt / 1e9, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
+            "config": {"workload": "att32b_decode", "sequences": Bn, "q_heads": Hq,
+                       "kv_heads": Hkv, "head_dim": D, "page": page, "cached_tokens": tokens,
+                       "step_algorithmic_bytes": work},
+            "roofline": {"bound": "hbm", "kernel": dom,
+                         "achieved": round(work / us[dom] / 1e3, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(work / us[dom] / 1e3 / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(dom, "att32b_decode")},
+            "kernels": {k: {"us": round(v, 2), "algorithmic_bytes": work,
+                            "GB/s": round(work / v / 1e3, 1)} for k, v in us.items()}}
+    if not args.no_cpu_baseline:
+        from oracle import attention as oatt
+        from oracle import kv as okv
+        rows = list(range(0, Bn, 8))                     # 8 of the 64 sequences
+        t0 = time.perf_counter()
+        oatt.decode_attention(q_np, okv.kv_scale(q_np), kc_np, vc_np, np.float32(2.0 ** -12),
+                              np.float32(2.0 ** -8), table, lens, Hkv, page, batch_rows=rows)
+        ct = time.perf_counter() - t0
+        sample = 2 * int(lens[rows].sum()) * Hkv * D + 4 * len(rows) * Hq * D
+        line["cpu_baseline"] = {"value": round(sample / ct / 1e9, 4), "unit": "GB/s",
+                                "cores": cpu_threads(), "kind": "oracle", "seconds": round(ct, 2),
+                                "sample": f"sequences {rows[0]}, {rows[1]}, ... {rows[-1]} "
+                                          f"({len(rows)} of {Bn}) of the same batch"}
+    return line
+
+
 def run_tis(args, torch, B, W):
     """Rollout correction of a batch of 1024 responses padded to 8192 tokens:
     per step, the TIS and the MIS weights with per-sequence statistics and
@@ -633,7 +695,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode7b_upgate",
                     choices=["decode7b_upgate", "decode32b_sweep", "prefill32b", "stack32b_requant",
-                             "kv32b_prefill", "moe_decode", "tis_batch", "stack32b_gemm"])
+                             "kv32b_prefill", "moe_decode", "tis_batch", "stack32b_gemm",
+                             "att32b_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (outside the "
@@ -662,7 +725,8 @@ def main(argv=None):
     run = {"decode7b_upgate": run_decode7b, "decode32b_sweep": run_decode32b,
            "prefill32b": run_prefill32b, "stack32b_requant": run_stack32b,
            "kv32b_prefill": run_kv32b, "moe_decode": run_moe_decode,
-           "tis_batch": run_tis, "stack32b_gemm": run_stack_gemm}[args.workload]
+           "tis_batch": run_tis, "stack32b_gemm": run_stack_gemm,
+           "att32b_decode": run_att}[args.workload]
     line = run(args, torch, B, W)
     print(json.dumps(line), flush=True)
     return 0

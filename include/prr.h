@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PRR_ABI_VERSION 5
+#define PRR_ABI_VERSION 6
 
 typedef enum prr_status {
   PRR_OK = 0,
@@ -267,6 +267,41 @@ prr_status fp8_kv_scale_recalibrate(const uint16_t* x_bf16, int64_t T, int64_t C
 prr_status fp8_kv_cache_write(const uint16_t* kv_bf16, const int64_t* slot_mapping,
                               int64_t T, int64_t C, const float* scale, uint8_t* cache,
                               int64_t num_slots, hipStream_t stream);
+
+/*
+ * fp8_kv_decode_attention -- the read side of the FP8 KV cache (FP8-RL,
+ * abstract, item (ii): FP8 KV cache with per-step Q/K/V scales): attention
+ * of one new token per sequence over its cached tokens.  The pages give no
+ * kernel; this library's reading: the query is quantized per tensor with
+ * q_scale (the cache's e4m3 encode); score of cached token t for query head
+ * h: s_q s_k softmax_scale (q^_h . k^_t) against cache head h / (Hq / Hkv);
+ * softmax over the sequence's seq_lens[b] tokens; output s_v sum_t p_t v^_t
+ * rounded to bf16.  fp32 arithmetic; the output is judged like a GEMM
+ * (relative Frobenius error <= 1e-3 against the fp64 definition).
+ *   q_bf16      in  [B, Hq, D] bf16 bits: the new token's queries.
+ *   q_scale, k_scale, v_scale  in  one fp32 each, device memory (e.g. from
+ *                   fp8_kv_scale_recalibrate of Q, K and V).
+ *   k_cache, v_cache  in  [num_slots, Hkv * D] e4m3 codes (e.g. written by
+ *                   fp8_kv_cache_write); the new token's K and V are
+ *                   expected in the cache already.
+ *   block_table in  [B, max_blocks] int32: token t of sequence b is in slot
+ *                   block_table[b][t / page] * page + t % page.  A token
+ *                   whose slot is negative or >= num_slots is skipped.
+ *   seq_lens    in  [B] int32: cached tokens per sequence (clamped to
+ *                   [0, max_blocks * page]); 0 writes zeros.
+ *   softmax_scale   finite (typically 1 / sqrt(D)).
+ *   out_bf16    out [B, Hq, D].
+ *   D must be 128 and Hq / Hkv (a whole number) at most 8
+ *   (PRR_ERR_UNSUPPORTED_SHAPE otherwise); Hkv, page and max_blocks >= 1
+ *   when B x Hq > 0.
+ */
+prr_status fp8_kv_decode_attention(const uint16_t* q_bf16, const float* q_scale,
+                                   const uint8_t* k_cache, const uint8_t* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page,
+                                   int64_t max_blocks, int64_t num_slots, float softmax_scale,
+                                   uint16_t* out_bf16, hipStream_t stream);
 
 /*
  * tis_token_weights -- token-level importance weights for correcting the

@@ -37,6 +37,8 @@ _SIGNATURES = {
     "fp8_kv_cache_write": [_P, _P, _I64, _I64, _P, _P, _I64, _P],
     "tis_token_weights": [_P, _P, _P, _I64, _I64, ctypes.c_float, ctypes.c_int, _P, _P, _P, _P],
     "w8a8_gemm_workspace_size": [_I64, _I64, _I64, _P],
+    "fp8_kv_decode_attention": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                _I64, _I64, ctypes.c_float, _P, _P],
     "w8a8_block_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
     "w8a8_int8_channel_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
 }
@@ -48,7 +50,7 @@ _lib = None
 
 # PRR_ABI_VERSION of the signatures below; a library of another version is
 # refused at load time.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class PrrError(RuntimeError):
@@ -326,3 +328,35 @@ def tis_token_weights(lp_train: torch.Tensor, lp_rollout: torch.Tensor, mask: to
                                     float(cap), int(mode), _ptr(w), _ptr(rs), _ptr(tt),
                                     _stream(lp_train)))
     return w, rs, tt
+
+
+def fp8_kv_decode_attention(q: torch.Tensor, q_scale: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                            block_table: torch.Tensor, seq_lens: torch.Tensor, Hkv: int,
+                            page: int, softmax_scale: float | None = None, out=None):
+    """Decode attention over the FP8 KV cache: q bf16 [B, Hq, D]; scales fp32
+    [1] on the device; caches uint8 [num_slots, Hkv * D]; block_table int32
+    [B, max_blocks]; seq_lens int32 [B].  Returns bf16 [B, Hq, D]."""
+    if q.dim() != 3:
+        raise ValueError("q: expected [B, Hq, D]")
+    B, Hq, D = q.shape
+    if q.dtype not in (torch.bfloat16, torch.int16) or not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q: expected a contiguous CUDA bf16 tensor")
+    for t, name in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _operand(t, torch.float32, (1,), name)
+    num_slots = k_cache.shape[0]
+    _operand(k_cache, torch.uint8, (num_slots, Hkv * D), "k_cache")
+    _operand(v_cache, torch.uint8, (num_slots, Hkv * D), "v_cache")
+    if block_table.dim() != 2:
+        raise ValueError("block_table: expected [B, max_blocks]")
+    _operand(block_table, torch.int32, (B, block_table.shape[1]), "block_table")
+    _operand(seq_lens, torch.int32, (B,), "seq_lens")
+    o = _out(out, torch.bfloat16, (B, Hq, D), q, "out")
+    c = float(1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
+    _check("fp8_kv_decode_attention",
+           load().fp8_kv_decode_attention(_ptr(q), q_scale.data_ptr(), _ptr(k_cache),
+                                          _ptr(v_cache), k_scale.data_ptr(), v_scale.data_ptr(),
+                                          _ptr(block_table), _ptr(seq_lens), B, Hq, Hkv, D,
+                                          page, block_table.shape[1], num_slots, c, _ptr(o),
+                                          _stream(q)))
+    return o

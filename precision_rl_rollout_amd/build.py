@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libprr.so")
 
 SOURCES = ["api.cpp", "quant_fp8.hip", "quant_int8.hip", "gemm.hip", "gemm_decode.hip", "gemm_prefill.hip", "kv_fp8.hip",
-           "tis.hip"]
+           "tis.hip", "attention.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 # No fast-math or denormal-flush flags: the quantizers rely on IEEE fp32

@@ -271,6 +271,30 @@ prr_status tis_token_weights(const float* logp_train, const float* logp_rollout,
                                                 mode, weights, row_stats, totals, stream));
 }
 
+prr_status fp8_kv_decode_attention(const uint16_t* q_bf16, const float* q_scale,
+                                   const uint8_t* k_cache, const uint8_t* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page,
+                                   int64_t max_blocks, int64_t num_slots, float softmax_scale,
+                                   uint16_t* out_bf16, hipStream_t stream) {
+  PRR_TRY(check_dims(B, Hq, Hkv));
+  PRR_TRY(check_dims(D, page, max_blocks));
+  PRR_TRY(check_dims(num_slots, 0));
+  if (!std::isfinite(softmax_scale)) return PRR_ERR_INVALID_ARG;
+  if (B == 0 || Hq == 0) return PRR_OK;
+  if (Hkv == 0 || page == 0 || max_blocks == 0) return PRR_ERR_INVALID_ARG;
+  if (D != 128 || Hq % Hkv != 0 || Hq / Hkv > 8) return PRR_ERR_UNSUPPORTED_SHAPE;
+  if (B * Hkv > kMaxGrid || max_blocks * page > (int64_t(1) << 40)) return PRR_ERR_UNSUPPORTED_SHAPE;
+  PRR_TRY(check_ptrs({q_bf16, q_scale, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens,
+                      out_bf16}));
+  PRR_TRY(check_device());
+  return from_hip(prr::launch_fp8_decode_attention(q_bf16, q_scale, k_cache, v_cache, k_scale,
+                                                   v_scale, block_table, seq_lens, B, Hq, Hkv,
+                                                   page, max_blocks, num_slots, softmax_scale,
+                                                   out_bf16, stream));
+}
+
 const char* prr_status_string(prr_status status) {
   switch (status) {
     case PRR_OK: return "PRR_OK";

@@ -35,6 +35,14 @@ hipError_t launch_tis_token_weights(const float* lp_train, const float* lp_rollo
                                     float lncap, int mode, float* w, float* row_stats,
                                     double* totals, hipStream_t stream);
 
+hipError_t launch_fp8_decode_attention(const uint16_t* q, const float* q_scale,
+                                       const uint8_t* k_cache, const uint8_t* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       int64_t B, int64_t Hq, int64_t Hkv, int64_t page,
+                                       int64_t max_blocks, int64_t num_slots,
+                                       float softmax_scale, uint16_t* out, hipStream_t stream);
+
 // Split-K decode GEMM plan: S K-slices, G workgroups, MT m-tiles, pw K
 // blocks per wave, `bytes` of fp32 workspace.  False: no split for this
 // shape (the one-pass kernels handle it).

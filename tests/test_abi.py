@@ -42,7 +42,7 @@ def test_header_declares_the_boundary():
                      "int8_weight_channel_quant", "int8_act_token_quant",
                      "w8a8_int8_channel_gemm", "w8a8_block_gemm_grouped",
                      "fp8_kv_scale_recalibrate",
-                     "fp8_kv_cache_write", "tis_token_weights", "w8a8_gemm_workspace_size",
+                     "fp8_kv_cache_write", "tis_token_weights", "w8a8_gemm_workspace_size", "fp8_kv_decode_attention",
                      "w8a8_block_gemm_ws", "w8a8_int8_channel_gemm_ws", "prr_status_string",
                      "prr_abi_version"}
 
@@ -229,3 +229,28 @@ def test_workspace_size_argument_checks():
     assert c(-1, 8, 256, ctypes.addressof(n)) == INVALID
     assert c(4, 8, 200, ctypes.addressof(n)) == SHAPE
     assert c(0, 8, 256, ctypes.addressof(n)) == OK and n.value == 0
+
+
+def test_attention_argument_checks():
+    c = lambda *a: binding.call("fp8_kv_decode_attention", *a)
+    ok = [FAKE] * 8 + [4, 40, 8, 128, 16, 64, 4096, 0.088, FAKE, None]
+    for i, v in ((8, -1), (9, -1), (10, -1), (12, -16), (13, -1), (14, -1),
+                 (15, float("nan")), (15, float("inf"))):
+        a = list(ok)
+        a[i] = v
+        assert c(*a) == INVALID, (i, v)
+    for i, v in ((11, 64), (9, 41), (9, 80), (10, 3)):
+        a = list(ok)
+        a[i] = v
+        assert c(*a) == SHAPE, (i, v)
+    for i in (0, 1, 2, 3, 4, 5, 6, 7, 16):
+        a = list(ok)
+        a[i] = None
+        assert c(*a) == INVALID
+        a[i] = ODD
+        assert c(*a) == MISALIGNED
+    a = list(ok)
+    a[12] = 0                                    # a page of zero tokens
+    assert c(*a) == INVALID
+    # nothing to compute: no pointer is needed
+    assert c(*([None] * 8 + [0, 40, 8, 128, 16, 64, 4096, 0.088, None, None])) == OK
