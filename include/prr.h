@@ -291,9 +291,9 @@ prr_status fp8_kv_cache_write(const uint16_t* kv_bf16, const int64_t* slot_mappi
  *                   [0, max_blocks * page]); 0 writes zeros.
  *   softmax_scale   finite (typically 1 / sqrt(D)).
  *   out_bf16    out [B, Hq, D].
- *   D must be 128 and Hq / Hkv (a whole number) at most 8
- *   (PRR_ERR_UNSUPPORTED_SHAPE otherwise); Hkv, page and max_blocks >= 1
- *   when B x Hq > 0.
+ *   D must be 128, Hq / Hkv (a whole number) at most 8 and page at most
+ *   2^20 (PRR_ERR_UNSUPPORTED_SHAPE otherwise); Hkv, page and max_blocks
+ *   >= 1 when B x Hq > 0.
  */
 prr_status fp8_kv_decode_attention(const uint16_t* q_bf16, const float* q_scale,
                                    const uint8_t* k_cache, const uint8_t* v_cache,

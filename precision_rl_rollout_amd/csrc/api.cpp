@@ -285,7 +285,8 @@ prr_status fp8_kv_decode_attention(const uint16_t* q_bf16, const float* q_scale,
   if (B == 0 || Hq == 0) return PRR_OK;
   if (Hkv == 0 || page == 0 || max_blocks == 0) return PRR_ERR_INVALID_ARG;
   if (D != 128 || Hq % Hkv != 0 || Hq / Hkv > 8) return PRR_ERR_UNSUPPORTED_SHAPE;
-  if (B * Hkv > kMaxGrid || max_blocks * page > (int64_t(1) << 40)) return PRR_ERR_UNSUPPORTED_SHAPE;
+  if (B * Hkv > kMaxGrid || page > (int64_t(1) << 20) || max_blocks * page > (int64_t(1) << 40))
+    return PRR_ERR_UNSUPPORTED_SHAPE;
   PRR_TRY(check_ptrs({q_bf16, q_scale, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens,
                       out_bf16}));
   PRR_TRY(check_device());

@@ -52,6 +52,41 @@ __device__ __forceinline__ void decode8(uint2 c, float f[8]) {
   }
 }
 
+// Sum over the 16 lanes of a row, left in every lane of the row: DPP
+// exchanges within quads, then half-rows, then rows (ALU only; a shuffle
+// through LDS costs a round trip per step).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+// Values that are uniform within each 16-lane row: combine the 4 rows
+// through scalar reads of lanes 0, 16, 32, 48.
+__device__ __forceinline__ float rows_max4(float v) {
+  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ float rows_sum4(float v) {
+  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);   // row_half_mirror
+  v += dpp_mov<0x140>(v);   // row_mirror
+  return v;
+}
+
 template <int G>
 __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ q_scale,
@@ -119,8 +154,12 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
         const int64_t t = t0 + 4 * u + tg;
         int64_t slot = -1;
         if (t < c1) {
-          const int pg = tbl[(int)(t / page) - p0];
-          slot = (int64_t)pg * page + t % page;
+          // 32-bit offset within the staged chunk (c0 is a whole number of
+          // pages): a 64-bit division here costs ~100 instructions a token
+          const uint32_t rel = (uint32_t)(t - c0);
+          const uint32_t pi = rel / (uint32_t)page;
+          const int pg = tbl[pi];
+          slot = (int64_t)pg * page + (rel - pi * (uint32_t)page);
         }
         ok[u] = slot >= 0 && slot < num_slots;
         kc[u] = make_uint2(0, 0);
@@ -142,8 +181,7 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
           float dot = 0.f;
 #pragma unroll
           for (int d = 0; d < 8; ++d) dot = __builtin_fmaf(qv[g][d], kf[d], dot);
-#pragma unroll
-          for (int off = 8; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+          dot = row_sum16(dot);
           s[u][g] = ok[u] ? dot * cs : -__builtin_inff();
         }
       }
@@ -154,8 +192,7 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
         float mi = s[0][g];
 #pragma unroll
         for (int u = 1; u < kAttSteps; ++u) mi = fmaxf(mi, s[u][g]);
-        mi = fmaxf(mi, __shfl_xor(mi, 16, 64));
-        mi = fmaxf(mi, __shfl_xor(mi, 32, 64));
+        mi = rows_max4(mi);
         const float mn = fmaxf(m[g], mi);
         // (every token so far skipped: mn = -inf; subtract 0 so that the
         // weights and alpha come out 0 rather than NaN)
@@ -168,8 +205,7 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
           s[u][g] = __builtin_amdgcn_exp2f(s[u][g] - mref);
           ps += s[u][g];
         }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
+        ps = rows_sum4(ps);
         l[g] = l[g] * alpha + ps;
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc[g][d] *= alpha;
