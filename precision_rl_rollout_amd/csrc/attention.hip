@@ -7,21 +7,22 @@
 // s_v sum_t p_t v^_t, rounded once to bf16.
 //
 // Bound by HBM: every cached token costs 2 x 128 bytes per KV head (its K
-// and V codes) against ~5 flops per byte for a group of 5 query heads, so
-// the arithmetic runs on the vector ALUs (fp32), not on MFMA.
+// and V codes) against ~5 flops per byte for a group of 5 query heads.
 //
-//  * One 512-thread workgroup per (sequence, KV head).  16 lanes take one
-//    token (8 of its 128 dimensions each: one 8-byte load of K and one of
-//    V), a wave takes 4 tokens per step and 8 steps (32 tokens) per
-//    iteration, with all 16 loads of an iteration issued before any math.
-//    Wave w takes iterations w, w + 8, ... of the sequence.
-//  * The decoded query of every head of the group stays in registers
-//    (8 G floats per lane).  Dot products are reduced over the 16 lanes of
-//    a token by butterflies.
+//  * One 512-thread workgroup per (sequence, KV head); wave w takes
+//    iterations w, w + 8, ... of the sequence, 32 tokens (two tiles of 16)
+//    an iteration, with every load of an iteration issued before any math.
+//  * Q K^T on the matrix cores in bf16: e4m3 -> bf16 is exact, and the bf16
+//    16x16x32 instruction sums its products to fp32 accuracy, while the
+//    e4m3 instructions of gfx950 keep only ~13 bits inside a dot product
+//    (measured: errors up to 2e-4 of the sum of |products|), which the
+//    softmax would turn into output errors well above a bf16 rounding.  One
+//    tile of 16 tokens against the group's query heads (rows past G zero) is
+//    four instructions, with no cross-lane reduction.
 //  * Online softmax in the base-2 domain (scores carry log2 e), updated once
-//    per iteration: a wave keeps the running maximum and sum per head and a
-//    partial output per lane (its own tokens), rescaled when the maximum
-//    grows; the 8 waves are combined through LDS at the end.
+//    per iteration per head; P V on the vector ALUs in fp32 with the
+//    probabilities passed through a per-wave LDS tile; the 8 waves are
+//    combined through LDS at the end.
 //  * The sequence's block-table row is staged in LDS (2048 pages at a time).
 //    A token whose page entry is negative or points past the cache is
 //    skipped; the loads of skipped and padding tokens are not issued.
@@ -33,8 +34,7 @@ namespace prr {
 constexpr int kAttThreads = 512;
 constexpr int kAttWaves = kAttThreads / 64;
 constexpr int kAttD = 128;            // head dimension
-constexpr int kAttSteps = 8;          // 4-token steps per iteration
-constexpr int kAttIter = 4 * kAttSteps;
+constexpr int kAttIter = 32;          // tokens of a wave iteration (two tiles of 16)
 constexpr int kAttTablePages = 2048;  // block-table entries staged at a time
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -52,39 +52,29 @@ __device__ __forceinline__ void decode8(uint2 c, float f[8]) {
   }
 }
 
-// Sum over the 16 lanes of a row, left in every lane of the row: DPP
-// exchanges within quads, then half-rows, then rows (ALU only; a shuffle
-// through LDS costs a round trip per step).
-template <int kCtrl>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Eight e4m3 codes -> eight bf16 values (exact: every e4m3 value, subnormals
+// included, is a bf16 value), in code order.
+__device__ __forceinline__ v8bf e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const uint4 r = make_uint4(
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true)));
+  return __builtin_bit_cast(v8bf, r);
 }
 
-// Values that are uniform within each 16-lane row: combine the 4 rows
-// through scalar reads of lanes 0, 16, 32, 48.
-__device__ __forceinline__ float rows_max4(float v) {
-  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
-__device__ __forceinline__ float rows_sum4(float v) {
-  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return (r0 + r1) + (r2 + r3);
-}
-
-__device__ __forceinline__ float row_sum16(float v) {
-  v += dpp_mov<0xB1>(v);    // quad_perm [1, 0, 3, 2]
-  v += dpp_mov<0x4E>(v);    // quad_perm [2, 3, 0, 1]
-  v += dpp_mov<0x141>(v);   // row_half_mirror
-  v += dpp_mov<0x140>(v);   // row_mirror
-  return v;
+// x / d for x < 2^24 and a quotient below 2^6 (x at most 32 past a
+// multiple of d): one float product, corrected by one step either way.
+__device__ __forceinline__ uint32_t small_div(uint32_t x, uint32_t d, float inv_d) {
+  uint32_t qt = (uint32_t)((float)x * inv_d);
+  const int32_t rem = (int32_t)(x - qt * d);
+  if (rem < 0) --qt;
+  else if (rem >= (int32_t)d) ++qt;
+  return qt;
 }
 
 template <int G>
@@ -95,13 +85,22 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hq,
     int Hkv, int page, int max_blocks, int64_t num_slots, float softmax_scale,
     uint16_t* __restrict__ out) {
+  constexpr int kPS = G <= 4 ? 4 : 8;               // pbuf row stride (heads)
   __shared__ int32_t tbl[kAttTablePages];
   __shared__ float part[kAttWaves][G][kAttD + 2];
+  __shared__ float4 pbuf[kAttWaves][kAttIter][kPS / 4];  // [token of the iteration][head]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.x / Hkv, kvh = blockIdx.x - b * Hkv;
-  const int tg = lane >> 4, l16 = lane & 15;       // token in the step, dims 8 l16 ..
+  // MFMA layout: lane (g, r) = row r (token r of a 16-token tile, or query
+  // head r), dimensions [32 g, 32 g + 32) as 4 slices of 8 (one per
+  // 16x16x32 instruction); its results are tokens 4 g .. 4 g + 3 of head r.  V layout: lane (tg, dg) =
+  // tokens 4 tg .. 4 tg + 3 of a tile, dimensions [8 dg, 8 dg + 8).
+  const int g = lane >> 4, r = lane & 15;
+  const int tg = g, dg = r;
   const int64_t row_bytes = (int64_t)Hkv * kAttD;
+  const uint8_t* kbase = k_cache + (int64_t)kvh * kAttD;
+  const uint8_t* vbase = v_cache + (int64_t)kvh * kAttD + 8 * dg;
   uint16_t* ob = out + ((int64_t)b * Hq + (int64_t)kvh * G) * kAttD;
 
   int64_t n = seq_lens[b];
@@ -112,28 +111,33 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     return;
   }
 
-  // The group's query heads: quantized with s_q, decoded (exact).
+  // The group's query heads, quantized with s_q and decoded to bf16 (exact):
+  // second MFMA operand, row r = head r (zero past the group).  Slice j of
+  // lane (g, r) holds dimensions [32 g + 8 j, 32 g + 8 j + 8).
   const float sq = *q_scale;
   const BlockDiv dq = block_div(sq);
-  float qv[G][8];
+  v8bf qf[4];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)kvh * G + g) * kAttD + 8 * l16;
-    const uint4 w = *reinterpret_cast<const uint4*>(qh);
-    decode8(e4m3_chunk_any<true>(w, sq, dq), qv[g]);
+  for (int j = 0; j < 4; ++j) qf[j] = __builtin_bit_cast(v8bf, make_uint4(0, 0, 0, 0));
+  if (r < G) {
+    const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)kvh * G + r) * kAttD + 32 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 c = e4m3_chunk_any<true>(*reinterpret_cast<const uint4*>(qh + 8 * j), sq, dq);
+      qf[j] = e4m3x8_to_bf16(c.x, c.y);
+    }
   }
   // Score scale in the base-2 domain.
   const float cs = sq * (*k_scale) * softmax_scale * kLog2e;
   const float sv = *v_scale;
+  const float inv_page = 1.0f / (float)page;
 
-  float m[G], l[G], acc[G][8];
+  float m = -__builtin_inff(), l = 0.f;              // head r (equal in the 4 lanes of r)
+  float acc[G][8];                                  // this lane's tokens and dimensions
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -__builtin_inff();
-    l[g] = 0.f;
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) acc[g][d] = 0.f;
-  }
+    for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
 
   const int32_t* trow = block_table + (int64_t)b * max_blocks;
   const int64_t chunk_tokens = (int64_t)kAttTablePages * page;
@@ -144,116 +148,150 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     __syncthreads();                                   // previous chunk's readers are done
     for (int e = tid; e < np; e += kAttThreads) tbl[e] = trow[p0 + e];
     __syncthreads();
-    const int64_t iters = (c1 - c0 + kAttIter - 1) / kAttIter;
-    for (int64_t it = wave; it < iters; it += kAttWaves) {
-      const int64_t t0 = c0 + it * kAttIter;
-      uint2 kc[kAttSteps], vc[kAttSteps];
-      bool ok[kAttSteps];
+    const int iters = (int)((c1 - c0 + kAttIter - 1) / kAttIter);
+    const int ntok = (int)(c1 - c0);
+    for (int it = wave; it < iters; it += kAttWaves) {
+      // Token k of the iteration is token it * 32 + k of the chunk: page
+      // pi0 + (off0 + k) / page of the staged table, all in 32 bits (a
+      // chunk holds at most 2^31 tokens).
+      const uint32_t rel0 = (uint32_t)it * kAttIter;
+      const uint32_t pi0 = rel0 / (uint32_t)page, off0 = rel0 - pi0 * (uint32_t)page;
+      auto slot_of = [&](int k) -> int64_t {
+        if ((int)rel0 + k >= ntok) return -1;
+        const uint32_t off = off0 + (uint32_t)k;
+        const uint32_t qp = small_div(off, (uint32_t)page, inv_page);
+        return (int64_t)tbl[pi0 + qp] * page + (off - qp * (uint32_t)page);
+      };
+      uint4 kl[2], kh[2];                               // bytes [32 g, 32 g + 32) of token r
+      uint2 vc[2][4];
+      uint64_t okm[2];
 #pragma unroll
-      for (int u = 0; u < kAttSteps; ++u) {
-        const int64_t t = t0 + 4 * u + tg;
-        int64_t slot = -1;
-        if (t < c1) {
-          // 32-bit offset within the staged chunk (c0 is a whole number of
-          // pages): a 64-bit division here costs ~100 instructions a token
-          const uint32_t rel = (uint32_t)(t - c0);
-          const uint32_t pi = rel / (uint32_t)page;
-          const int pg = tbl[pi];
-          slot = (int64_t)pg * page + (rel - pi * (uint32_t)page);
+      for (int tile = 0; tile < 2; ++tile) {
+        const int64_t sk = slot_of(16 * tile + r);
+        const bool ok = sk >= 0 && sk < num_slots;
+        okm[tile] = __ballot(ok) & 0xFFFF;               // bit j: token 16 tile + j
+        kl[tile] = kh[tile] = make_uint4(0, 0, 0, 0);
+        if (ok) {
+          const uint8_t* kp = kbase + sk * row_bytes + 32 * g;
+          kl[tile] = *reinterpret_cast<const uint4*>(kp);
+          kh[tile] = *reinterpret_cast<const uint4*>(kp + 16);
         }
-        ok[u] = slot >= 0 && slot < num_slots;
-        kc[u] = make_uint2(0, 0);
-        vc[u] = make_uint2(0, 0);
-        if (ok[u]) {
-          const int64_t off = slot * row_bytes + (int64_t)kvh * kAttD + 8 * l16;
-          kc[u] = *reinterpret_cast<const uint2*>(k_cache + off);
-          vc[u] = *reinterpret_cast<const uint2*>(v_cache + off);
-        }
-      }
-      // Scores (base 2) of this lane's tokens, for every head.
-      float s[kAttSteps][G];
 #pragma unroll
-      for (int u = 0; u < kAttSteps; ++u) {
-        float kf[8];
-        decode8(kc[u], kf);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float dot = 0.f;
-#pragma unroll
-          for (int d = 0; d < 8; ++d) dot = __builtin_fmaf(qv[g][d], kf[d], dot);
-          dot = row_sum16(dot);
-          s[u][g] = ok[u] ? dot * cs : -__builtin_inff();
+        for (int i = 0; i < 4; ++i) {
+          const int k = 16 * tile + 4 * tg + i;
+          vc[tile][i] = make_uint2(0, 0);
+          if ((okm[tile] >> (4 * tg + i)) & 1) {
+            const int64_t svl = slot_of(k);
+            vc[tile][i] = *reinterpret_cast<const uint2*>(vbase + svl * row_bytes);
+          }
         }
       }
-      // Softmax update per head (s becomes p in place), then one decode of
-      // each token's V for all heads.
+      // Scores (base 2): lane (g, r) gets tokens 16 tile + 4 g + i of head r.
+      float sc[2][4];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float mi = s[0][g];
+      for (int tile = 0; tile < 2; ++tile) {
+        v4f d = {0.f, 0.f, 0.f, 0.f};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kl[tile].x, kl[tile].y), qf[0], d,
+                                                    0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kl[tile].z, kl[tile].w), qf[1], d,
+                                                    0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kh[tile].x, kh[tile].y), qf[2], d,
+                                                    0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kh[tile].z, kh[tile].w), qf[3], d,
+                                                    0, 0, 0);
 #pragma unroll
-        for (int u = 1; u < kAttSteps; ++u) mi = fmaxf(mi, s[u][g]);
-        mi = rows_max4(mi);
-        const float mn = fmaxf(m[g], mi);
-        // (every token so far skipped: mn = -inf; subtract 0 so that the
-        // weights and alpha come out 0 rather than NaN)
-        const float mref = mn == -__builtin_inff() ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m[g] - mref);
-        m[g] = mn;
-        float ps = 0.f;
+        for (int i = 0; i < 4; ++i)
+          sc[tile][i] = ((okm[tile] >> (4 * g + i)) & 1) ? d[i] * cs : -__builtin_inff();
+      }
+      float mi = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      mi = fmaxf(mi, __shfl_xor(mi, 16, 64));
+      mi = fmaxf(mi, __shfl_xor(mi, 32, 64));
+      const float mn = fmaxf(m, mi);
+      // (every token so far skipped: mn = -inf; subtract 0 so that the
+      // weights and alpha come out 0 rather than NaN)
+      const float mref = mn == -__builtin_inff() ? 0.f : mn;
+      const float alpha = __builtin_amdgcn_exp2f(m - mref);
+      m = mn;
+      float ps = 0.f;
+      float* prow = reinterpret_cast<float*>(&pbuf[wave][0][0]);
 #pragma unroll
-        for (int u = 0; u < kAttSteps; ++u) {
-          s[u][g] = __builtin_amdgcn_exp2f(s[u][g] - mref);
-          ps += s[u][g];
+      for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(sc[tile][i] - mref);
+          ps += pv;
+          if (r < G) prow[(16 * tile + 4 * g + i) * kPS + r] = pv;
         }
-        ps = rows_sum4(ps);
-        l[g] = l[g] * alpha + ps;
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l = l * alpha + ps;
+      // Rescale, then P V in the V layout.  The probabilities were written
+      // by this wave; its LDS operations complete in order.
+      asm volatile("" ::: "memory");
 #pragma unroll
-        for (int d = 0; d < 8; ++d) acc[g][d] *= alpha;
+      for (int h = 0; h < G; ++h) {
+        const float ah = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[h][d] *= ah;
       }
 #pragma unroll
-      for (int u = 0; u < kAttSteps; ++u) {
-        float vf[8];
-        decode8(vc[u], vf);
+      for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int i = 0; i < 4; ++i) {
+          const int k = 16 * tile + 4 * tg + i;
+          float pt[kPS];
 #pragma unroll
-          for (int d = 0; d < 8; ++d) acc[g][d] = __builtin_fmaf(s[u][g], vf[d], acc[g][d]);
-      }
+          for (int c = 0; c < kPS / 4; ++c) {
+            const float4 p4 = pbuf[wave][k][c];
+            pt[4 * c + 0] = p4.x;
+            pt[4 * c + 1] = p4.y;
+            pt[4 * c + 2] = p4.z;
+            pt[4 * c + 3] = p4.w;
+          }
+          float vf[8];
+          decode8(vc[tile][i], vf);
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(pt[h], vf[d], acc[h][d]);
+        }
+      asm volatile("" ::: "memory");
     }
   }
 
   // The 4 token groups of a wave, then the 8 waves.
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      acc[g][d] += __shfl_xor(acc[g][d], 16, 64);
-      acc[g][d] += __shfl_xor(acc[g][d], 32, 64);
+      acc[h][d] += __shfl_xor(acc[h][d], 16, 64);
+      acc[h][d] += __shfl_xor(acc[h][d], 32, 64);
     }
-  if (lane < 16) {
+  if (tg == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int d = 0; d < 8; ++d) part[wave][g][8 * lane + d] = acc[g][d];
-      if (lane == 0) {
-        part[wave][g][kAttD] = m[g];
-        part[wave][g][kAttD + 1] = l[g];
-      }
+      for (int d = 0; d < 8; ++d) part[wave][h][8 * dg + d] = acc[h][d];
+    if (r < G) {
+      part[wave][r][kAttD] = m;
+      part[wave][r][kAttD + 1] = l;
     }
   }
   __syncthreads();
   for (int e = tid; e < G * kAttD; e += kAttThreads) {
-    const int g = e / kAttD, d = e - g * kAttD;
+    const int h = e / kAttD, d = e - h * kAttD;
     float M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, part[w][g][kAttD]);
+    for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, part[w][h][kAttD]);
     float L = 0.f, O = 0.f;
     if (M != -__builtin_inff()) {
 #pragma unroll
       for (int w = 0; w < kAttWaves; ++w) {
-        const float f = __builtin_amdgcn_exp2f(part[w][g][kAttD] - M);
-        L += part[w][g][kAttD + 1] * f;
-        O += part[w][g][d] * f;
+        const float f = __builtin_amdgcn_exp2f(part[w][h][kAttD] - M);
+        L += part[w][h][kAttD + 1] * f;
+        O += part[w][h][d] * f;
       }
     }
     const float v = L > 0.f ? sv * (O / L) : 0.f;
