@@ -36,6 +36,7 @@ constexpr int kAttWaves = kAttThreads / 64;
 constexpr int kAttD = 128;            // head dimension
 constexpr int kAttIter = 32;          // tokens of a wave iteration (two tiles of 16)
 constexpr int kAttTablePages = 2048;  // block-table entries staged at a time
+constexpr int kAttOrderMax = 256;     // sequences ordered by length in-kernel (at most)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Eight e4m3 codes -> eight floats (exact).
@@ -86,26 +87,52 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     int Hkv, int page, int max_blocks, int64_t num_slots, float softmax_scale,
     uint16_t* __restrict__ out) {
   constexpr int kPS = G <= 4 ? 4 : 8;               // pbuf row stride (heads)
-  __shared__ int32_t tbl[kAttTablePages];
+  __shared__ int64_t tbase[kAttTablePages];        // byte offset of a staged page's first row
+  __shared__ int32_t tlim[kAttTablePages];         // its slots inside the cache (0: skipped)
   __shared__ float part[kAttWaves][G][kAttD + 2];
   __shared__ float4 pbuf[kAttWaves][kAttIter][kPS / 4];  // [token of the iteration][head]
+  __shared__ int32_t pick;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.x / Hkv, kvh = blockIdx.x - b * Hkv;
+  const int B = (int)(gridDim.x / Hkv);
+  const int kvh = blockIdx.x % Hkv;
+  const int64_t n_cap = (int64_t)max_blocks * page;
+  auto length = [&](int bb) -> int64_t {
+    const int64_t v = seq_lens[bb];
+    return min(v < 0 ? (int64_t)0 : v, n_cap);
+  };
+  // Longest sequences first: workgroup i serves the sequence of rank i / Hkv
+  // in order of decreasing length (ties by index), so that the work left
+  // for the last workgroups to start is the shortest.  The ranks are a
+  // permutation, so exactly one thread finds the target.
+  int b = (int)(blockIdx.x / Hkv);
+  if (B <= kAttOrderMax) {
+    const int64_t* lens = tbase;                   // staging space until the table is loaded
+    for (int e = tid; e < B; e += kAttThreads) tbase[e] = length(e);
+    __syncthreads();
+    for (int j = tid; j < B; j += kAttThreads) {
+      const int64_t lj = lens[j];
+      int rank = 0;
+      for (int i = 0; i < B; ++i) rank += (lens[i] > lj) || (lens[i] == lj && i < j);
+      if (rank == b) pick = j;
+    }
+    __syncthreads();
+    b = pick;
+  }
   // MFMA layout: lane (g, r) = row r (token r of a 16-token tile, or query
   // head r), dimensions [32 g, 32 g + 32) as 4 slices of 8 (one per
-  // 16x16x32 instruction); its results are tokens 4 g .. 4 g + 3 of head r.  V layout: lane (tg, dg) =
-  // tokens 4 tg .. 4 tg + 3 of a tile, dimensions [8 dg, 8 dg + 8).
+  // 16x16x32 instruction); its results are tokens 4 g .. 4 g + 3 of head r.
+  // V layout: lane (tg, dg) = tokens 4 tg .. 4 tg + 3 of a tile, dimensions
+  // [8 dg, 8 dg + 8).
   const int g = lane >> 4, r = lane & 15;
   const int tg = g, dg = r;
-  const int64_t row_bytes = (int64_t)Hkv * kAttD;
+  const uint32_t row_bytes = (uint32_t)Hkv * kAttD;
   const uint8_t* kbase = k_cache + (int64_t)kvh * kAttD;
   const uint8_t* vbase = v_cache + (int64_t)kvh * kAttD + 8 * dg;
   uint16_t* ob = out + ((int64_t)b * Hq + (int64_t)kvh * G) * kAttD;
 
-  int64_t n = seq_lens[b];
-  n = n < 0 ? 0 : n;
-  n = min(n, (int64_t)max_blocks * page);
+  // (no cache slots: every token is skipped)
+  const int64_t n = num_slots > 0 ? length(b) : 0;
   if (n == 0) {
     for (int e = tid; e < G * kAttD; e += kAttThreads) ob[e] = 0;
     return;
@@ -145,45 +172,56 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     const int64_t c1 = min(n, c0 + chunk_tokens);
     const int p0 = (int)(c0 / page);
     const int np = (int)((c1 - c0 + page - 1) / page);
-    __syncthreads();                                   // previous chunk's readers are done
-    for (int e = tid; e < np; e += kAttThreads) tbl[e] = trow[p0 + e];
+    __syncthreads();                                   // previous readers of the table are done
+    for (int e = tid; e < np; e += kAttThreads) {
+      const int64_t pid = trow[p0 + e];
+      const int64_t first = pid * page;
+      const int64_t lim = pid < 0 ? 0 : min((int64_t)page, max((int64_t)0, num_slots - first));
+      tlim[e] = (int32_t)lim;
+      tbase[e] = lim > 0 ? first * row_bytes : 0;
+    }
     __syncthreads();
     const int iters = (int)((c1 - c0 + kAttIter - 1) / kAttIter);
     const int ntok = (int)(c1 - c0);
     for (int it = wave; it < iters; it += kAttWaves) {
-      // Token k of the iteration is token it * 32 + k of the chunk: page
+      // Token k of the iteration is token 32 it + k of the chunk: page
       // pi0 + (off0 + k) / page of the staged table, all in 32 bits (a
-      // chunk holds at most 2^31 tokens).
+      // chunk holds at most 2^31 tokens).  A token that is absent (past the
+      // length, or its slot outside the cache) reads row 0 of the cache
+      // (there is one) and is masked.
       const uint32_t rel0 = (uint32_t)it * kAttIter;
       const uint32_t pi0 = rel0 / (uint32_t)page, off0 = rel0 - pi0 * (uint32_t)page;
-      auto slot_of = [&](int k) -> int64_t {
-        if ((int)rel0 + k >= ntok) return -1;
+      auto locate = [&](int k, uint64_t& at) -> bool {
+        const bool in = (int)rel0 + k < ntok;
         const uint32_t off = off0 + (uint32_t)k;
         const uint32_t qp = small_div(off, (uint32_t)page, inv_page);
-        return (int64_t)tbl[pi0 + qp] * page + (off - qp * (uint32_t)page);
+        const uint32_t pi = in ? pi0 + qp : 0;
+        const uint32_t o = off - qp * (uint32_t)page;
+        // (pi is in range either way; the empty asm keeps the compiler from
+        // moving the reads under a branch on ok)
+        int32_t lim = tlim[pi];
+        int64_t base = tbase[pi];
+        asm volatile("" : "+v"(lim), "+v"(base));
+        const bool ok = in & ((int32_t)o < lim);
+        at = ok ? (uint64_t)base + (uint64_t)o * row_bytes : 0;
+        return ok;
       };
       uint4 kl[2], kh[2];                               // bytes [32 g, 32 g + 32) of token r
       uint2 vc[2][4];
       uint64_t okm[2];
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile) {
-        const int64_t sk = slot_of(16 * tile + r);
-        const bool ok = sk >= 0 && sk < num_slots;
+        uint64_t at;
+        const bool ok = locate(16 * tile + r, at);
         okm[tile] = __ballot(ok) & 0xFFFF;               // bit j: token 16 tile + j
-        kl[tile] = kh[tile] = make_uint4(0, 0, 0, 0);
-        if (ok) {
-          const uint8_t* kp = kbase + sk * row_bytes + 32 * g;
-          kl[tile] = *reinterpret_cast<const uint4*>(kp);
-          kh[tile] = *reinterpret_cast<const uint4*>(kp + 16);
-        }
+        const uint8_t* kp = kbase + at + 32 * g;
+        kl[tile] = *reinterpret_cast<const uint4*>(kp);
+        kh[tile] = *reinterpret_cast<const uint4*>(kp + 16);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int k = 16 * tile + 4 * tg + i;
-          vc[tile][i] = make_uint2(0, 0);
-          if ((okm[tile] >> (4 * tg + i)) & 1) {
-            const int64_t svl = slot_of(k);
-            vc[tile][i] = *reinterpret_cast<const uint2*>(vbase + svl * row_bytes);
-          }
+          const bool okv = locate(16 * tile + 4 * tg + i, at);
+          const uint2 v = *reinterpret_cast<const uint2*>(vbase + at);
+          vc[tile][i] = make_uint2(okv ? v.x : 0u, okv ? v.y : 0u);
         }
       }
       // Scores (base 2): lane (g, r) gets tokens 16 tile + 4 g + i of head r.
