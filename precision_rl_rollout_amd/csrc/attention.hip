@@ -37,25 +37,16 @@ constexpr int kAttD = 128;            // head dimension
 constexpr int kAttIter = 32;          // tokens of a wave iteration (two tiles of 16)
 constexpr int kAttTablePages = 2048;  // block-table entries staged at a time
 constexpr int kAttOrderMax = 256;     // sequences ordered by length in-kernel (at most)
+constexpr int kAttVRow = 144;         // LDS bytes a token of the V tile (128 + bank skew)
+constexpr int kAttVTile = kAttIter * kAttVRow;
+constexpr float kAttWeightExp = 14.f; // weights scaled by 2^14 (fp16 range)
 constexpr float kLog2e = 1.4426950408889634f;
-
-// Eight e4m3 codes -> eight floats (exact).
-__device__ __forceinline__ void decode8(uint2 c, float f[8]) {
-  const uint32_t w[2] = {c.x, c.y};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);
-    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);
-    f[4 * h + 0] = lo[0];
-    f[4 * h + 1] = lo[1];
-    f[4 * h + 2] = hi[0];
-    f[4 * h + 3] = hi[1];
-  }
-}
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 // Eight e4m3 codes -> eight bf16 values (exact: every e4m3 value, subnormals
 // included, is a bf16 value), in code order.
@@ -78,6 +69,17 @@ __device__ __forceinline__ uint32_t small_div(uint32_t x, uint32_t d, float inv_
   return qt;
 }
 
+// Eight e4m3 codes (a 64-bit pair) -> eight fp16 values (exact: every e4m3
+// value, subnormals included, is an fp16 value), in code order.
+__device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t lo, uint32_t hi) {
+  const uint4 r = make_uint4(
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true)));
+  return __builtin_bit_cast(v8h, r);
+}
+
 template <int G>
 __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ q_scale,
@@ -86,11 +88,13 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hq,
     int Hkv, int page, int max_blocks, int64_t num_slots, float softmax_scale,
     uint16_t* __restrict__ out) {
-  constexpr int kPS = G <= 4 ? 4 : 8;               // pbuf row stride (heads)
+  typedef float Part[G][kAttD + 2];
+  static_assert(sizeof(Part) * kAttWaves <= kAttWaves * kAttVTile, "partials fit the V tiles");
   __shared__ int64_t tbase[kAttTablePages];        // byte offset of a staged page's first row
   __shared__ int32_t tlim[kAttTablePages];         // its slots inside the cache (0: skipped)
-  __shared__ float part[kAttWaves][G][kAttD + 2];
-  __shared__ float4 pbuf[kAttWaves][kAttIter][kPS / 4];  // [token of the iteration][head]
+  // Per-wave V tile of an iteration, token-major (kAttVRow bytes a token);
+  // after the token loop the same space holds the waves' partial results.
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[kAttWaves * kAttVTile];
   __shared__ int32_t pick;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -119,16 +123,28 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     __syncthreads();
     b = pick;
   }
-  // MFMA layout: lane (g, r) = row r (token r of a 16-token tile, or query
-  // head r), dimensions [32 g, 32 g + 32) as 4 slices of 8 (one per
-  // 16x16x32 instruction); its results are tokens 4 g .. 4 g + 3 of head r.
-  // V layout: lane (tg, dg) = tokens 4 tg .. 4 tg + 3 of a tile, dimensions
-  // [8 dg, 8 dg + 8).
+  // Lane (g, r), in the layout of the 16x16x32 instructions:
+  //  * Q K^T (bf16): row r = token r of a 16-token tile (first operand) or
+  //    query head r (second operand, zero past the group), dimensions
+  //    [32 g, 32 g + 32) as 4 slices of 8; results: tokens 4 g .. 4 g + 3
+  //    of head r.  K and V of token r are loaded by the same lanes.
+  //  * P V (fp16), summed over the iteration's 32 tokens: k-slot e of lane
+  //    (g, .) is token 16 (e / 4) + 4 g + e % 4, so the probabilities stay
+  //    where Q K^T left them (second operand, row r = head r); the first
+  //    operand, row r = dimension 16 j + r, is read from the V tile by a
+  //    transposing LDS load; results: dimensions 16 j + 4 g .. 16 j + 4 g + 3
+  //    of head r.
   const int g = lane >> 4, r = lane & 15;
-  const int tg = g, dg = r;
   const uint32_t row_bytes = (uint32_t)Hkv * kAttD;
-  const uint8_t* kbase = k_cache + (int64_t)kvh * kAttD;
-  const uint8_t* vbase = v_cache + (int64_t)kvh * kAttD + 8 * dg;
+  const uint8_t* kbase = k_cache + (int64_t)kvh * kAttD + 32 * g;
+  const uint8_t* vbase = v_cache + (int64_t)kvh * kAttD + 32 * g;
+  uint8_t* vt = vtile + wave * kAttVTile;
+  // The transposing load: lane (g, s) names 8 bytes, and lane (g, r) gets
+  // byte r % 8 of the bytes named by lanes (g, 2 e + r / 8), e = 0 .. 7.  So
+  // lane (g, s) names dimensions 16 j + 8 (s % 2) .. + 8 of token-slot
+  // e = s / 2.
+  const int tr_tok = 16 * (r >> 3) + 4 * g + ((r >> 1) & 3);
+  const uint8_t* tr_src = vt + tr_tok * kAttVRow + 8 * (r & 1);
   uint16_t* ob = out + ((int64_t)b * Hq + (int64_t)kvh * G) * kAttD;
 
   // (no cache slots: every token is skipped)
@@ -138,9 +154,7 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     return;
   }
 
-  // The group's query heads, quantized with s_q and decoded to bf16 (exact):
-  // second MFMA operand, row r = head r (zero past the group).  Slice j of
-  // lane (g, r) holds dimensions [32 g + 8 j, 32 g + 8 j + 8).
+  // The group's query heads, quantized with s_q and decoded to bf16 (exact).
   const float sq = *q_scale;
   const BlockDiv dq = block_div(sq);
   v8bf qf[4];
@@ -154,17 +168,17 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
       qf[j] = e4m3x8_to_bf16(c.x, c.y);
     }
   }
-  // Score scale in the base-2 domain.
+  // Score scale in the base-2 domain.  Weights are 2^(s - m + 14), in
+  // [0, 2^14], so that their fp16 halves stay clear of the subnormals; the
+  // factor cancels in O / L.
   const float cs = sq * (*k_scale) * softmax_scale * kLog2e;
   const float sv = *v_scale;
   const float inv_page = 1.0f / (float)page;
 
   float m = -__builtin_inff(), l = 0.f;              // head r (equal in the 4 lanes of r)
-  float acc[G][8];                                  // this lane's tokens and dimensions
+  v4f acc[8];                                        // dims 16 j + 4 g + e' of head r
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
+  for (int j = 0; j < 8; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int32_t* trow = block_table + (int64_t)b * max_blocks;
   const int64_t chunk_tokens = (int64_t)kAttTablePages * page;
@@ -191,7 +205,11 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
       // (there is one) and is masked.
       const uint32_t rel0 = (uint32_t)it * kAttIter;
       const uint32_t pi0 = rel0 / (uint32_t)page, off0 = rel0 - pi0 * (uint32_t)page;
-      auto locate = [&](int k, uint64_t& at) -> bool {
+      uint4 kx[2][2], vx[2][2];
+      uint64_t okm[2];
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        const int k = 16 * tile + r;
         const bool in = (int)rel0 + k < ntok;
         const uint32_t off = off0 + (uint32_t)k;
         const uint32_t qp = small_div(off, (uint32_t)page, inv_page);
@@ -203,40 +221,39 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
         int64_t base = tbase[pi];
         asm volatile("" : "+v"(lim), "+v"(base));
         const bool ok = in & ((int32_t)o < lim);
-        at = ok ? (uint64_t)base + (uint64_t)o * row_bytes : 0;
-        return ok;
-      };
-      uint4 kl[2], kh[2];                               // bytes [32 g, 32 g + 32) of token r
-      uint2 vc[2][4];
-      uint64_t okm[2];
+        const uint64_t at = ok ? (uint64_t)base + (uint64_t)o * row_bytes : 0;
+        okm[tile] = __ballot(ok) & 0xFFFF;               // bit j: token 16 tile + j
+        const uint4* kp = reinterpret_cast<const uint4*>(kbase + at);
+        const uint4* vp = reinterpret_cast<const uint4*>(vbase + at);
+        kx[tile][0] = kp[0];
+        kx[tile][1] = kp[1];
+        const uint4 v0 = vp[0], v1 = vp[1];
+        // (an absent token's weight is 0; its V is zeroed so that whatever
+        // row 0 holds cannot turn 0 into NaN)
+        vx[tile][0] = ok ? v0 : make_uint4(0, 0, 0, 0);
+        vx[tile][1] = ok ? v1 : make_uint4(0, 0, 0, 0);
+      }
+      // The V tile to LDS, token-major (read back transposed below; the
+      // tile is this wave's own and its LDS operations complete in order).
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile) {
-        uint64_t at;
-        const bool ok = locate(16 * tile + r, at);
-        okm[tile] = __ballot(ok) & 0xFFFF;               // bit j: token 16 tile + j
-        const uint8_t* kp = kbase + at + 32 * g;
-        kl[tile] = *reinterpret_cast<const uint4*>(kp);
-        kh[tile] = *reinterpret_cast<const uint4*>(kp + 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool okv = locate(16 * tile + 4 * tg + i, at);
-          const uint2 v = *reinterpret_cast<const uint2*>(vbase + at);
-          vc[tile][i] = make_uint2(okv ? v.x : 0u, okv ? v.y : 0u);
-        }
+        uint4* dst = reinterpret_cast<uint4*>(vt + (16 * tile + r) * kAttVRow + 32 * g);
+        dst[0] = vx[tile][0];
+        dst[1] = vx[tile][1];
       }
       // Scores (base 2): lane (g, r) gets tokens 16 tile + 4 g + i of head r.
       float sc[2][4];
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile) {
         v4f d = {0.f, 0.f, 0.f, 0.f};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kl[tile].x, kl[tile].y), qf[0], d,
-                                                    0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kl[tile].z, kl[tile].w), qf[1], d,
-                                                    0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kh[tile].x, kh[tile].y), qf[2], d,
-                                                    0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kh[tile].z, kh[tile].w), qf[3], d,
-                                                    0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kx[tile][0].x, kx[tile][0].y),
+                                                    qf[0], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kx[tile][0].z, kx[tile][0].w),
+                                                    qf[1], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kx[tile][1].x, kx[tile][1].y),
+                                                    qf[2], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kx[tile][1].z, kx[tile][1].w),
+                                                    qf[3], d, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           sc[tile][i] = ((okm[tile] >> (4 * g + i)) & 1) ? d[i] * cs : -__builtin_inff();
@@ -248,71 +265,54 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
       const float mn = fmaxf(m, mi);
       // (every token so far skipped: mn = -inf; subtract 0 so that the
       // weights and alpha come out 0 rather than NaN)
-      const float mref = mn == -__builtin_inff() ? 0.f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(m - mref);
+      const float mref = (mn == -__builtin_inff() ? 0.f : mn) - kAttWeightExp;
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
       m = mn;
+      // Weights as fp16 pairs: p = hi + lo to ~2^-21 relative.
       float ps = 0.f;
-      float* prow = reinterpret_cast<float*>(&pbuf[wave][0][0]);
+      _Float16 wh[8], wl[8];
 #pragma unroll
-      for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(sc[tile][i] - mref);
-          ps += pv;
-          if (r < G) prow[(16 * tile + 4 * g + i) * kPS + r] = pv;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(sc[e >> 2][e & 3] - mref);
+        ps += pv;
+        wh[e] = (_Float16)pv;
+        wl[e] = (_Float16)(pv - (float)wh[e]);
+      }
+      const v8h ph = {wh[0], wh[1], wh[2], wh[3], wh[4], wh[5], wh[6], wh[7]};
+      const v8h pl = {wl[0], wl[1], wl[2], wl[3], wl[4], wl[5], wl[6], wl[7]};
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
-      l = l * alpha + ps;
-      // Rescale, then P V in the V layout.  The probabilities were written
-      // by this wave; its LDS operations complete in order.
+      // (alpha = 0 on the first tokens: m was -inf; mn = -inf as well gives
+      // NaN, where l and the outputs are still 0)
+      const float a = mn == -__builtin_inff() ? 1.f : alpha;
+      l = l * a + ps;
+      if (__ballot(a != 1.f)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= a;
+      }
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float ah = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[h][d] *= ah;
+      for (int j = 0; j < 8; ++j) {
+        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(tr_src + 16 * j));
+        const v8h vf = e4m3x8_to_f16((uint32_t)t.x, (uint32_t)t.y);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl, acc[j], 0, 0, 0);
       }
-#pragma unroll
-      for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int k = 16 * tile + 4 * tg + i;
-          float pt[kPS];
-#pragma unroll
-          for (int c = 0; c < kPS / 4; ++c) {
-            const float4 p4 = pbuf[wave][k][c];
-            pt[4 * c + 0] = p4.x;
-            pt[4 * c + 1] = p4.y;
-            pt[4 * c + 2] = p4.z;
-            pt[4 * c + 3] = p4.w;
-          }
-          float vf[8];
-          decode8(vc[tile][i], vf);
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(pt[h], vf[d], acc[h][d]);
-        }
       asm volatile("" ::: "memory");
     }
   }
 
-  // The 4 token groups of a wave, then the 8 waves.
+  // The 8 waves through LDS (in the V tiles' space, once every wave is
+  // past its token loop).
+  Part* part = reinterpret_cast<Part*>(vtile);
+  __syncthreads();
+  if (r < G) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      acc[h][d] += __shfl_xor(acc[h][d], 16, 64);
-      acc[h][d] += __shfl_xor(acc[h][d], 32, 64);
-    }
-  if (tg == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) part[wave][h][8 * dg + d] = acc[h][d];
-    if (r < G) {
+      for (int e = 0; e < 4; ++e) part[wave][r][16 * j + 4 * g + e] = acc[j][e];
+    if (g == 0) {
       part[wave][r][kAttD] = m;
       part[wave][r][kAttD + 1] = l;
     }
