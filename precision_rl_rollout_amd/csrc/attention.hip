@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
   // Per-wave V tile of an iteration, token-major (kAttVRow bytes a token);
   // after the token loop the same space holds the waves' partial results.
   __shared__ __attribute__((aligned(16))) uint8_t vtile[kAttWaves * kAttVTile];
+  __shared__ uint4 qsh[16 * 4 * 4];                 // query operand fragments (bf16)
   __shared__ int32_t pick;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -154,20 +155,25 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     return;
   }
 
-  // The group's query heads, quantized with s_q and decoded to bf16 (exact).
+  // The group's query heads, quantized with s_q and decoded to bf16 (exact),
+  // kept in LDS in the second operand's layout (row r = head r, zero past
+  // the group; slice j of lane (g, r) = dimensions 32 g + 8 j .. + 8) and
+  // read where used, which keeps 16 registers free for the loads in flight.
   const float sq = *q_scale;
-  const BlockDiv dq = block_div(sq);
-  v8bf qf[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) qf[j] = __builtin_bit_cast(v8bf, make_uint4(0, 0, 0, 0));
-  if (r < G) {
+  if (wave == 0) {
+    const BlockDiv dq = block_div(sq);
     const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)kvh * G + r) * kAttD + 32 * g;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint2 c = e4m3_chunk_any<true>(*reinterpret_cast<const uint4*>(qh + 8 * j), sq, dq);
-      qf[j] = e4m3x8_to_bf16(c.x, c.y);
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (r < G) {
+        const uint2 c = e4m3_chunk_any<true>(*reinterpret_cast<const uint4*>(qh + 8 * j), sq, dq);
+        w = __builtin_bit_cast(uint4, e4m3x8_to_bf16(c.x, c.y));
+      }
+      qsh[(r * 4 + g) * 4 + j] = w;
     }
   }
+  const uint4* qrow = &qsh[(r * 4 + g) * 4];
   // Score scale in the base-2 domain.  Weights are 2^(s - m + 14), in
   // [0, 2^14], so that their fp16 halves stay clear of the subnormals; the
   // factor cancels in O / L.
@@ -197,16 +203,14 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
     __syncthreads();
     const int iters = (int)((c1 - c0 + kAttIter - 1) / kAttIter);
     const int ntok = (int)(c1 - c0);
-    for (int it = wave; it < iters; it += kAttWaves) {
-      // Token k of the iteration is token 32 it + k of the chunk: page
-      // pi0 + (off0 + k) / page of the staged table, all in 32 bits (a
-      // chunk holds at most 2^31 tokens).  A token that is absent (past the
-      // length, or its slot outside the cache) reads row 0 of the cache
-      // (there is one) and is masked.
+    // Token k of iteration it is token 32 it + k of the chunk: page
+    // pi0 + (off0 + k) / page of the staged table, all in 32 bits (a chunk
+    // holds at most 2^31 tokens).  A token that is absent (past the length,
+    // or its slot outside the cache) reads row 0 of the cache (there is one)
+    // and is masked.  Lane (g, r) locates token 16 tile + r.
+    auto locate = [&](int it, uint64_t at[2], bool ok[2]) {
       const uint32_t rel0 = (uint32_t)it * kAttIter;
       const uint32_t pi0 = rel0 / (uint32_t)page, off0 = rel0 - pi0 * (uint32_t)page;
-      uint4 kx[2][2], vx[2][2];
-      uint64_t okm[2];
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile) {
         const int k = 16 * tile + r;
@@ -220,43 +224,78 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_kernel(
         int32_t lim = tlim[pi];
         int64_t base = tbase[pi];
         asm volatile("" : "+v"(lim), "+v"(base));
-        const bool ok = in & ((int32_t)o < lim);
-        const uint64_t at = ok ? (uint64_t)base + (uint64_t)o * row_bytes : 0;
-        okm[tile] = __ballot(ok) & 0xFFFF;               // bit j: token 16 tile + j
-        const uint4* kp = reinterpret_cast<const uint4*>(kbase + at);
-        const uint4* vp = reinterpret_cast<const uint4*>(vbase + at);
-        kx[tile][0] = kp[0];
-        kx[tile][1] = kp[1];
-        const uint4 v0 = vp[0], v1 = vp[1];
-        // (an absent token's weight is 0; its V is zeroed so that whatever
-        // row 0 holds cannot turn 0 into NaN)
-        vx[tile][0] = ok ? v0 : make_uint4(0, 0, 0, 0);
-        vx[tile][1] = ok ? v1 : make_uint4(0, 0, 0, 0);
+        ok[tile] = in & ((int32_t)o < lim);
+        at[tile] = ok[tile] ? (uint64_t)base + (uint64_t)o * row_bytes : 0;
       }
-      // The V tile to LDS, token-major (read back transposed below; the
-      // tile is this wave's own and its LDS operations complete in order).
+    };
+    auto load_k = [&](const uint64_t at[2], uint4 kx[2][2]) {
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile) {
-        uint4* dst = reinterpret_cast<uint4*>(vt + (16 * tile + r) * kAttVRow + 32 * g);
-        dst[0] = vx[tile][0];
-        dst[1] = vx[tile][1];
+        const uint4* kp = reinterpret_cast<const uint4*>(kbase + at[tile]);
+        kx[tile][0] = kp[0];
+        kx[tile][1] = kp[1];
       }
+    };
+    auto load_v = [&](const uint64_t at[2], uint4 vx[2][2]) {
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        const uint4* vp = reinterpret_cast<const uint4*>(vbase + at[tile]);
+        vx[tile][0] = vp[0];
+        vx[tile][1] = vp[1];
+      }
+    };
+    // Each wave keeps the next iteration's loads in flight behind this
+    // one's work: its K loads go out once Q K^T has consumed the current
+    // K, its V loads once the current V is in the LDS tile (same registers).
+    uint64_t at[2];
+    bool ok[2];
+    uint4 kx[2][2], vx[2][2];
+    if (wave < iters) {
+      locate(wave, at, ok);
+      load_k(at, kx);
+      load_v(at, vx);
+    }
+    for (int it = wave; it < iters; it += kAttWaves) {
+      const bool more = it + kAttWaves < iters;
+      uint64_t at_n[2] = {0, 0};
+      bool ok_n[2] = {false, false};
+      if (more) locate(it + kAttWaves, at_n, ok_n);
+      uint64_t okm[2];
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) okm[tile] = __ballot(ok[tile]) & 0xFFFF;  // bit j: token 16 tile + j
       // Scores (base 2): lane (g, r) gets tokens 16 tile + 4 g + i of head r.
       float sc[2][4];
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile) {
         v4f d = {0.f, 0.f, 0.f, 0.f};
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kx[tile][0].x, kx[tile][0].y),
-                                                    qf[0], d, 0, 0, 0);
+                                                    __builtin_bit_cast(v8bf, qrow[0]), d, 0, 0, 0);
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kx[tile][0].z, kx[tile][0].w),
-                                                    qf[1], d, 0, 0, 0);
+                                                    __builtin_bit_cast(v8bf, qrow[1]), d, 0, 0, 0);
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kx[tile][1].x, kx[tile][1].y),
-                                                    qf[2], d, 0, 0, 0);
+                                                    __builtin_bit_cast(v8bf, qrow[2]), d, 0, 0, 0);
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(kx[tile][1].z, kx[tile][1].w),
-                                                    qf[3], d, 0, 0, 0);
+                                                    __builtin_bit_cast(v8bf, qrow[3]), d, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           sc[tile][i] = ((okm[tile] >> (4 * g + i)) & 1) ? d[i] * cs : -__builtin_inff();
+      }
+      if (more) load_k(at_n, kx);
+      // The V tile to LDS, token-major (read back transposed below; the
+      // tile is this wave's own and its LDS operations complete in order).
+      // An absent token's weight is 0; its V is zeroed so that whatever row
+      // 0 holds cannot turn 0 into NaN.
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        uint4* dst = reinterpret_cast<uint4*>(vt + (16 * tile + r) * kAttVRow + 32 * g);
+        dst[0] = ok[tile] ? vx[tile][0] : make_uint4(0, 0, 0, 0);
+        dst[1] = ok[tile] ? vx[tile][1] : make_uint4(0, 0, 0, 0);
+      }
+      if (more) load_v(at_n, vx);
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        at[tile] = at_n[tile];
+        ok[tile] = ok_n[tile];
       }
       float mi = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                        fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
