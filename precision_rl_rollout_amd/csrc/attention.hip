@@ -9,9 +9,11 @@
 // Bound by HBM: every cached token costs 2 x 128 bytes per KV head (its K
 // and V codes) against ~5 flops per byte for a group of 5 query heads.
 //
-//  * One 512-thread workgroup per (sequence, KV head); wave w takes
-//    iterations w, w + 8, ... of the sequence, 32 tokens (two tiles of 16)
-//    an iteration, with every load of an iteration issued before any math.
+//  * One 512-thread workgroup per (sequence, KV head), taken longest
+//    sequence first (ranked in-kernel from the lengths, up to 256
+//    sequences); wave w takes iterations w, w + 8, ... of the sequence, 32
+//    tokens (two tiles of 16) an iteration, and keeps the next iteration's
+//    K and V loads in flight behind the current one's math.
 //  * Q K^T on the matrix cores in bf16: e4m3 -> bf16 is exact, and the bf16
 //    16x16x32 instruction sums its products to fp32 accuracy, while the
 //    e4m3 instructions of gfx950 keep only ~13 bits inside a dot product
@@ -20,12 +22,14 @@
 //    tile of 16 tokens against the group's query heads (rows past G zero) is
 //    four instructions, with no cross-lane reduction.
 //  * Online softmax in the base-2 domain (scores carry log2 e), updated once
-//    per iteration per head; P V on the vector ALUs in fp32 with the
-//    probabilities passed through a per-wave LDS tile; the 8 waves are
-//    combined through LDS at the end.
-//  * The sequence's block-table row is staged in LDS (2048 pages at a time).
-//    A token whose page entry is negative or points past the cache is
-//    skipped; the loads of skipped and padding tokens are not issued.
+//    per iteration per head.  P V on the matrix cores in fp16: each weight
+//    is split into fp16 hi + lo parts (~2^-21 relative together), V is
+//    decoded exactly from e4m3 to fp16 after a transposing LDS read of the
+//    wave's token-major V tile.  The 8 waves are combined through LDS.
+//  * The sequence's block-table row is staged in LDS (2048 pages at a
+//    time) as a byte base and a count of valid slots per page.  Loads are
+//    branch-free: an absent token (past the length, or its slot outside the
+//    cache) reads cache row 0 and is masked out of the softmax.
 #include "launch.h"
 #include "prr_device.h"
 
