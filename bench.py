@@ -28,7 +28,9 @@ every expert, activation quantization, the grouped GEMM), ``tis_batch``
 (TIS and MIS token weights of 1024 responses padded to 8192 tokens),
 ``stack32b_gemm`` (the decode GEMMs of a 32B layer stack at M = 1 and 64),
 ``att32b_decode`` (decode attention over an FP8 KV cache: 64 sequences of
-1024-8192 tokens, 40 query heads over 8 KV heads).
+1024-8192 tokens, 40 query heads over 8 KV heads; the call with its
+workspace, which splits the batch's tokens over the CUs; ``batch_sizes``
+adds the first 1, 2, 8 and 64 sequences with and without the split).
 """
 
 from __future__ import annotations
@@ -601,14 +603,50 @@ def run_att(args, torch, B, W):
     sv = torch.tensor([2.0 ** -8], dtype=torch.float32, device=dev)
     out = torch.empty((Bn, Hq, D), dtype=torch.bfloat16, device=dev)
     tokens = int(lens.sum())
-    work = (2 * tokens * Hkv * D + 4 * Bn * Hq * D + 4 * int(((lens + page - 1) // page).sum())
-            + 4 * Bn)
+
+    def att_work(ls):
+        return (2 * int(ls.sum()) * Hkv * D + 4 * len(ls) * Hq * D
+                + 4 * int(((ls + page - 1) // page).sum()) + 4 * len(ls))
+
+    work = att_work(lens)
+    # the batch split over the CUs, with the workspace the library asks for
+    wsb = B.attention_workspace_bytes(Bn, Hq, Hkv, D)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev) if wsb else None
 
     def step(_i, timer=None):
-        f = lambda: B.fp8_kv_decode_attention(q, sq, kc, vc, sk, sv, tb, sl, Hkv, page, out=out)
+        f = lambda: B.fp8_kv_decode_attention(q, sq, kc, vc, sk, sv, tb, sl, Hkv, page, out=out,
+                                              workspace=ws)
         timer.run("fp8_kv_decode_attention", f) if timer else f()
 
     dt, us, dom = timed_steps(torch, step, args)
+
+    # Long-tail batches (the first b sequences of the same cache): both launch
+    # forms, median of 20 event-timed calls each.
+    def median_us(f, n=20):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, e in ev:
+            a.record()
+            f()
+            e.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(e) * 1e3 for a, e in ev]))
+
+    tail = {}
+    for b in (1, 2, 8, Bn):
+        wb = B.attention_workspace_bytes(b, Hq, Hkv, D)
+        wt = torch.empty((wb,), dtype=torch.uint8, device=dev) if wb else None
+        ob = out[:b]
+        row = {}
+        for name, w in (("split", wt), ("one_pass", None)):
+            t = median_us(lambda: B.fp8_kv_decode_attention(q[:b], sq, kc, vc, sk, sv, tb[:b],
+                                                            sl[:b], Hkv, page, out=ob,
+                                                            workspace=w))
+            row[name] = {"us": round(t, 1), "GB/s": round(att_work(lens[:b]) / t / 1e3, 1)}
+        tail[f"B{b}"] = row
     line = {"metric": METRIC, "value": round(work / dt / 1e9, 1), "unit": "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak",
@@ -621,7 +659,8 @@ def run_att(args, torch, B, W):
                          "unit": "GB/s", "frac": round(work / us[dom] / 1e3 / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic(dom, "att32b_decode")},
             "kernels": {k: {"us": round(v, 2), "algorithmic_bytes": work,
-                            "GB/s": round(work / v / 1e3, 1)} for k, v in us.items()}}
+                            "GB/s": round(work / v / 1e3, 1)} for k, v in us.items()},
+            "batch_sizes": tail}
     if not args.no_cpu_baseline:
         from oracle import attention as oatt
         from oracle import kv as okv

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PRR_ABI_VERSION 6
+#define PRR_ABI_VERSION 7
 
 typedef enum prr_status {
   PRR_OK = 0,
@@ -302,6 +302,39 @@ prr_status fp8_kv_decode_attention(const uint16_t* q_bf16, const float* q_scale,
                                    int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page,
                                    int64_t max_blocks, int64_t num_slots, float softmax_scale,
                                    uint16_t* out_bf16, hipStream_t stream);
+
+/*
+ * fp8_kv_decode_attention_workspace_size / fp8_kv_decode_attention_ws -- the
+ * call above with an optional caller-owned workspace (same definition,
+ * arguments, errors and tolerance).  With it the batch's cached tokens,
+ * sequence after sequence, are cut into one equal range per compute unit; a
+ * workgroup reads whole cache rows (every KV head of a token) over its
+ * range and leaves a partial softmax state (unnormalized output, running
+ * maximum and sum per query head) in the workspace for each sequence its
+ * range meets; a second kernel combines the partial states of each
+ * sequence in a fixed order (bitwise repeatable) and rounds once to bf16.
+ * The one-pass call gives each (sequence, KV head) a workgroup of its own,
+ * which reads 128 bytes of every Hkv x 128-byte cache row and leaves CUs
+ * idle when the batch is small.
+ *   fp8_kv_decode_attention_workspace_size: *bytes = the workspace the _ws
+ *       call uses for B sequences of Hq query heads over Hkv KV heads of D
+ *       on the current device (0: the shape takes the one-pass kernel:
+ *       D != 128, B > 2048, or Hkv not a divisor of 8).
+ *   workspace: device memory, 16-byte aligned, not shared with a call in
+ *       flight on another stream; NULL or workspace_bytes below the size ->
+ *       the one-pass kernel (never an error).  The library does not keep
+ *       the pointer.  workspace_bytes < 0 -> PRR_ERR_INVALID_ARG.
+ */
+prr_status fp8_kv_decode_attention_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                                  int64_t* bytes);
+prr_status fp8_kv_decode_attention_ws(const uint16_t* q_bf16, const float* q_scale,
+                                      const uint8_t* k_cache, const uint8_t* v_cache,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page,
+                                      int64_t max_blocks, int64_t num_slots, float softmax_scale,
+                                      uint16_t* out_bf16, void* workspace,
+                                      int64_t workspace_bytes, hipStream_t stream);
 
 /*
  * tis_token_weights -- token-level importance weights for correcting the

@@ -39,6 +39,9 @@ _SIGNATURES = {
     "w8a8_gemm_workspace_size": [_I64, _I64, _I64, _P],
     "fp8_kv_decode_attention": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
                                 _I64, _I64, ctypes.c_float, _P, _P],
+    "fp8_kv_decode_attention_workspace_size": [_I64, _I64, _I64, _I64, _P],
+    "fp8_kv_decode_attention_ws": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                   _I64, _I64, ctypes.c_float, _P, _P, _I64, _P],
     "w8a8_block_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
     "w8a8_int8_channel_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
 }
@@ -50,7 +53,7 @@ _lib = None
 
 # PRR_ABI_VERSION of the signatures below; a library of another version is
 # refused at load time.
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class PrrError(RuntimeError):
@@ -330,13 +333,30 @@ def tis_token_weights(lp_train: torch.Tensor, lp_rollout: torch.Tensor, mask: to
     return w, rs, tt
 
 
+def attention_workspace_bytes(B: int, Hq: int, Hkv: int, D: int) -> int:
+    """Workspace (bytes) fp8_kv_decode_attention_ws uses for these dimensions
+    on the current device; 0 when the one-pass kernel is used."""
+    key = ("att", torch.cuda.current_device(), int(B), int(Hq), int(Hkv), int(D))
+    if key not in _ws_sizes:
+        n = ctypes.c_int64(0)
+        _check("fp8_kv_decode_attention_workspace_size",
+               load().fp8_kv_decode_attention_workspace_size(int(B), int(Hq), int(Hkv), int(D),
+                                                             ctypes.addressof(n)))
+        _ws_sizes[key] = int(n.value)
+    return _ws_sizes[key]
+
+
 def fp8_kv_decode_attention(q: torch.Tensor, q_scale: torch.Tensor, k_cache: torch.Tensor,
                             v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
                             block_table: torch.Tensor, seq_lens: torch.Tensor, Hkv: int,
-                            page: int, softmax_scale: float | None = None, out=None):
+                            page: int, softmax_scale: float | None = None, out=None,
+                            workspace="auto"):
     """Decode attention over the FP8 KV cache: q bf16 [B, Hq, D]; scales fp32
     [1] on the device; caches uint8 [num_slots, Hkv * D]; block_table int32
-    [B, max_blocks]; seq_lens int32 [B].  Returns bf16 [B, Hq, D]."""
+    [B, max_blocks]; seq_lens int32 [B].  Returns bf16 [B, Hq, D].  With a
+    workspace (by default one of the size the library asks for) the batch's
+    tokens are split evenly over the CUs (fp8_kv_decode_attention_ws);
+    workspace=None runs the one-pass kernel."""
     if q.dim() != 3:
         raise ValueError("q: expected [B, Hq, D]")
     B, Hq, D = q.shape
@@ -353,10 +373,21 @@ def fp8_kv_decode_attention(q: torch.Tensor, q_scale: torch.Tensor, k_cache: tor
     _operand(seq_lens, torch.int32, (B,), "seq_lens")
     o = _out(out, torch.bfloat16, (B, Hq, D), q, "out")
     c = float(1.0 / D ** 0.5) if softmax_scale is None else float(softmax_scale)
-    _check("fp8_kv_decode_attention",
-           load().fp8_kv_decode_attention(_ptr(q), q_scale.data_ptr(), _ptr(k_cache),
-                                          _ptr(v_cache), k_scale.data_ptr(), v_scale.data_ptr(),
-                                          _ptr(block_table), _ptr(seq_lens), B, Hq, Hkv, D,
-                                          page, block_table.shape[1], num_slots, c, _ptr(o),
-                                          _stream(q)))
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace: 'auto', None or a uint8 CUDA tensor")
+        n = attention_workspace_bytes(B, Hq, Hkv, D) if B > 0 and Hq > 0 and Hkv > 0 else 0
+        workspace = torch.empty((n,), dtype=torch.uint8, device=q.device) if n else None
+    elif workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_cuda
+                                    or not workspace.is_contiguous()):
+        raise ValueError("workspace: expected a contiguous CUDA uint8 tensor")
+    args = (_ptr(q), q_scale.data_ptr(), _ptr(k_cache), _ptr(v_cache), k_scale.data_ptr(),
+            v_scale.data_ptr(), _ptr(block_table), _ptr(seq_lens), B, Hq, Hkv, D, page,
+            block_table.shape[1], num_slots, c, _ptr(o))
+    if workspace is None:
+        _check("fp8_kv_decode_attention", load().fp8_kv_decode_attention(*args, _stream(q)))
+    else:
+        _check("fp8_kv_decode_attention_ws",
+               load().fp8_kv_decode_attention_ws(*args, _ptr(workspace), workspace.numel(),
+                                                 _stream(q)))
     return o

@@ -271,6 +271,33 @@ prr_status tis_token_weights(const float* logp_train, const float* logp_rollout,
                                                 mode, weights, row_stats, totals, stream));
 }
 
+// Checks shared by the two attention calls; PRR_OK with *empty set when
+// there is nothing to compute.
+static prr_status attention_common(const uint16_t* q_bf16, const float* q_scale,
+                                   const uint8_t* k_cache, const uint8_t* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens, int64_t B,
+                                   int64_t Hq, int64_t Hkv, int64_t D, int64_t page,
+                                   int64_t max_blocks, int64_t num_slots, float softmax_scale,
+                                   uint16_t* out_bf16, bool* empty) {
+  *empty = false;
+  PRR_TRY(check_dims(B, Hq, Hkv));
+  PRR_TRY(check_dims(D, page, max_blocks));
+  PRR_TRY(check_dims(num_slots, 0));
+  if (!std::isfinite(softmax_scale)) return PRR_ERR_INVALID_ARG;
+  if (B == 0 || Hq == 0) {
+    *empty = true;
+    return PRR_OK;
+  }
+  if (Hkv == 0 || page == 0 || max_blocks == 0) return PRR_ERR_INVALID_ARG;
+  if (D != 128 || Hq % Hkv != 0 || Hq / Hkv > 8) return PRR_ERR_UNSUPPORTED_SHAPE;
+  if (B * Hkv > kMaxGrid || page > (int64_t(1) << 20) || max_blocks * page > (int64_t(1) << 40))
+    return PRR_ERR_UNSUPPORTED_SHAPE;
+  PRR_TRY(check_ptrs({q_bf16, q_scale, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens,
+                      out_bf16}));
+  return check_device();
+}
+
 prr_status fp8_kv_decode_attention(const uint16_t* q_bf16, const float* q_scale,
                                    const uint8_t* k_cache, const uint8_t* v_cache,
                                    const float* k_scale, const float* v_scale,
@@ -278,18 +305,51 @@ prr_status fp8_kv_decode_attention(const uint16_t* q_bf16, const float* q_scale,
                                    int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page,
                                    int64_t max_blocks, int64_t num_slots, float softmax_scale,
                                    uint16_t* out_bf16, hipStream_t stream) {
+  bool empty = false;
+  PRR_TRY(attention_common(q_bf16, q_scale, k_cache, v_cache, k_scale, v_scale, block_table,
+                           seq_lens, B, Hq, Hkv, D, page, max_blocks, num_slots, softmax_scale,
+                           out_bf16, &empty));
+  if (empty) return PRR_OK;
+  return from_hip(prr::launch_fp8_decode_attention(q_bf16, q_scale, k_cache, v_cache, k_scale,
+                                                   v_scale, block_table, seq_lens, B, Hq, Hkv,
+                                                   page, max_blocks, num_slots, softmax_scale,
+                                                   out_bf16, stream));
+}
+
+prr_status fp8_kv_decode_attention_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                                  int64_t* bytes) {
+  if (bytes == nullptr) return PRR_ERR_INVALID_ARG;
+  *bytes = 0;
   PRR_TRY(check_dims(B, Hq, Hkv));
-  PRR_TRY(check_dims(D, page, max_blocks));
-  PRR_TRY(check_dims(num_slots, 0));
-  if (!std::isfinite(softmax_scale)) return PRR_ERR_INVALID_ARG;
+  PRR_TRY(check_dims(D, 0, 0));
   if (B == 0 || Hq == 0) return PRR_OK;
-  if (Hkv == 0 || page == 0 || max_blocks == 0) return PRR_ERR_INVALID_ARG;
-  if (D != 128 || Hq % Hkv != 0 || Hq / Hkv > 8) return PRR_ERR_UNSUPPORTED_SHAPE;
-  if (B * Hkv > kMaxGrid || page > (int64_t(1) << 20) || max_blocks * page > (int64_t(1) << 40))
-    return PRR_ERR_UNSUPPORTED_SHAPE;
-  PRR_TRY(check_ptrs({q_bf16, q_scale, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens,
-                      out_bf16}));
   PRR_TRY(check_device());
+  *bytes = prr::fp8_decode_attention_workspace_bytes(B, Hq, Hkv, D);
+  return PRR_OK;
+}
+
+prr_status fp8_kv_decode_attention_ws(const uint16_t* q_bf16, const float* q_scale,
+                                      const uint8_t* k_cache, const uint8_t* v_cache,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page,
+                                      int64_t max_blocks, int64_t num_slots, float softmax_scale,
+                                      uint16_t* out_bf16, void* workspace,
+                                      int64_t workspace_bytes, hipStream_t stream) {
+  if (workspace_bytes < 0) return PRR_ERR_INVALID_ARG;
+  if (workspace != nullptr && workspace_bytes > 0 && B > 0 && Hq > 0)
+    PRR_TRY(check_ptrs({workspace}));
+  bool empty = false;
+  PRR_TRY(attention_common(q_bf16, q_scale, k_cache, v_cache, k_scale, v_scale, block_table,
+                           seq_lens, B, Hq, Hkv, D, page, max_blocks, num_slots, softmax_scale,
+                           out_bf16, &empty));
+  if (empty) return PRR_OK;
+  hipError_t err = hipSuccess;
+  if (prr::launch_fp8_decode_attention_span(q_bf16, q_scale, k_cache, v_cache, k_scale, v_scale,
+                                            block_table, seq_lens, B, Hq, Hkv, page, max_blocks,
+                                            num_slots, softmax_scale, out_bf16, workspace,
+                                            workspace_bytes, stream, &err))
+    return from_hip(err);
   return from_hip(prr::launch_fp8_decode_attention(q_bf16, q_scale, k_cache, v_cache, k_scale,
                                                    v_scale, block_table, seq_lens, B, Hq, Hkv,
                                                    page, max_blocks, num_slots, softmax_scale,

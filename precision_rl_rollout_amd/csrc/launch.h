@@ -43,6 +43,20 @@ hipError_t launch_fp8_decode_attention(const uint16_t* q, const float* q_scale,
                                        int64_t max_blocks, int64_t num_slots,
                                        float softmax_scale, uint16_t* out, hipStream_t stream);
 
+// Decode attention split over the batch's tokens with a caller workspace:
+// the bytes it needs (0: this shape takes the one-pass kernel), and the
+// launch (false, nothing launched, when the shape has no split or the
+// workspace is missing or too small).
+int64_t fp8_decode_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t D);
+bool launch_fp8_decode_attention_span(const uint16_t* q, const float* q_scale,
+                                      const uint8_t* k_cache, const uint8_t* v_cache,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      int64_t B, int64_t Hq, int64_t Hkv, int64_t page,
+                                      int64_t max_blocks, int64_t num_slots, float softmax_scale,
+                                      uint16_t* out, void* ws, int64_t ws_bytes,
+                                      hipStream_t stream, hipError_t* err);
+
 // Split-K decode GEMM plan: S K-slices, G workgroups, MT m-tiles, pw K
 // blocks per wave, `bytes` of fp32 workspace.  False: no split for this
 // shape (the one-pass kernels handle it).

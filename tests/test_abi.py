@@ -42,9 +42,10 @@ def test_header_declares_the_boundary():
                      "int8_weight_channel_quant", "int8_act_token_quant",
                      "w8a8_int8_channel_gemm", "w8a8_block_gemm_grouped",
                      "fp8_kv_scale_recalibrate",
-                     "fp8_kv_cache_write", "tis_token_weights", "w8a8_gemm_workspace_size", "fp8_kv_decode_attention",
-                     "w8a8_block_gemm_ws", "w8a8_int8_channel_gemm_ws", "prr_status_string",
-                     "prr_abi_version"}
+                     "fp8_kv_cache_write", "tis_token_weights", "w8a8_gemm_workspace_size",
+                     "fp8_kv_decode_attention", "fp8_kv_decode_attention_workspace_size",
+                     "fp8_kv_decode_attention_ws", "w8a8_block_gemm_ws",
+                     "w8a8_int8_channel_gemm_ws", "prr_status_string", "prr_abi_version"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -254,3 +255,33 @@ def test_attention_argument_checks():
     assert c(*a) == INVALID
     # nothing to compute: no pointer is needed
     assert c(*([None] * 8 + [0, 40, 8, 128, 16, 64, 4096, 0.088, None, None])) == OK
+
+
+def test_attention_ws_argument_checks():
+    c = lambda *a: binding.call("fp8_kv_decode_attention_ws", *a)
+    ok = [FAKE] * 8 + [4, 40, 8, 128, 16, 64, 4096, 0.088, FAKE, FAKE, 1 << 20, None]
+    a = list(ok)
+    a[18] = -1                                   # negative workspace size
+    assert c(*a) == INVALID
+    for i, v in ((8, -1), (10, -1), (15, float("nan"))):
+        a = list(ok)
+        a[i] = v
+        assert c(*a) == INVALID, (i, v)
+    for i, v in ((11, 64), (9, 41)):
+        a = list(ok)
+        a[i] = v
+        assert c(*a) == SHAPE, (i, v)
+    a = list(ok)
+    a[17] = ODD                                  # a misaligned workspace
+    assert c(*a) == MISALIGNED
+    for i in (0, 6, 16):
+        a = list(ok)
+        a[i] = None
+        assert c(*a) == INVALID
+    # nothing to compute: no pointer is needed
+    assert c(*([None] * 8 + [0, 40, 8, 128, 16, 64, 4096, 0.088, None, None, 0, None])) == OK
+    n = ctypes.c_int64(-1)
+    z = lambda *a: binding.call("fp8_kv_decode_attention_workspace_size", *a)
+    assert z(4, 40, 8, 128, None) == INVALID
+    assert z(-1, 40, 8, 128, ctypes.addressof(n)) == INVALID
+    assert z(0, 40, 8, 128, ctypes.addressof(n)) == OK and n.value == 0

@@ -1,4 +1,6 @@
-"""GPU parity of fp8_kv_decode_attention against the oracle.
+"""GPU parity of fp8_kv_decode_attention (the one-pass kernel, workspace
+None) and fp8_kv_decode_attention_ws (the batch split over the CUs, with the
+workspace the library asks for) against the oracle.
 
 Each case builds a paged FP8 cache with the oracle (K and V rows of the
 activation recipe, per-tensor scales, codes), a random block table and a
@@ -9,7 +11,10 @@ output's rms.  Cases: group sizes 1 to 8, lengths 0, 1, a partial page and
 several thousand tokens, page sizes 16 and 5, tokens skipped through
 invalid block-table entries, lengths beyond the table (clamped), and the
 32B-class layout (40 query heads over 8 KV heads) on sampled sequences of
-the full 64-sequence batch.
+the full 64-sequence batch; for the split: one long sequence cut over every
+CU, hundreds of short sequences sharing workgroups, shapes it does not take
+(Hkv not a divisor of 8, more than 2048 sequences, a workspace too small),
+and bitwise-repeatable results.
 """
 
 import numpy as np
@@ -41,13 +46,16 @@ def _build(B, Hq, Hkv, lens, page, seed, D=128):
                 sv=sv, table=table, lens=lens, Hkv=Hkv, page=page)
 
 
-def _gpu(p):
+WS = ["auto", None]     # the split with the library's workspace; the one-pass kernel
+
+
+def _gpu(p, ws="auto"):
     f = lambda x: torch.tensor([x], dtype=torch.float32, device="cuda:0")
     B, Hq, D = p["q"].shape
     out = binding.fp8_kv_decode_attention(
         bits_to_dev(p["q"].reshape(B, -1)).view(B, Hq, D), f(p["sq"]), _dev(p["kc"]),
         _dev(p["vc"]), f(p["sk"]), f(p["sv"]), _dev(p["table"]), _dev(p["lens"]), p["Hkv"],
-        p["page"])
+        p["page"], workspace=ws)
     return host(out)
 
 
@@ -64,23 +72,69 @@ def _check(got, p, label, rows=None):
     assert not bad.any(), f"{label}: {int(bad.sum())} elements off, first at {np.argwhere(bad)[0]}"
 
 
+@pytest.mark.parametrize("ws", WS)
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (12, 4), (8, 2), (10, 2), (12, 2),
-                                    (14, 2), (8, 1)])
-def test_group_sizes(Hq, Hkv):
+                                    (14, 2), (8, 1), (40, 8), (24, 3)])
+def test_group_sizes(Hq, Hkv, ws):
     p = _build(3, Hq, Hkv, [37, 300, 1], 16, seed=Hq + Hkv)
-    announce(f"fp8_kv_decode_attention Hq{Hq} Hkv{Hkv}")
-    _check(_gpu(p), p, f"Hq{Hq} Hkv{Hkv}")
+    announce(f"fp8_kv_decode_attention Hq{Hq} Hkv{Hkv} workspace {ws}")
+    _check(_gpu(p, ws), p, f"Hq{Hq} Hkv{Hkv}")
 
 
+@pytest.mark.parametrize("ws", WS)
 @pytest.mark.parametrize("lens,page", [([0, 1, 15, 16, 17], 16), ([33, 3000, 5], 5),
-                                       ([4100, 31, 64], 16), ([1, 1, 1, 2], 1)])
-def test_lengths_and_pages(lens, page):
+                                       ([4100, 31, 64], 16), ([1, 1, 1, 2], 1),
+                                       ([0, 0, 0], 16)])
+def test_lengths_and_pages(lens, page, ws):
     p = _build(len(lens), 10, 2, lens, page, seed=sum(lens))
-    announce(f"fp8_kv_decode_attention lens {lens} page {page}")
-    _check(_gpu(p), p, f"lens {lens} page {page}")
+    announce(f"fp8_kv_decode_attention lens {lens} page {page} workspace {ws}")
+    _check(_gpu(p, ws), p, f"lens {lens} page {page}")
 
 
-def test_skipped_tokens_and_clamped_lengths():
+def test_one_long_sequence_over_every_cu():
+    # 9000 tokens of one sequence: ~36 per workgroup, ranges starting inside
+    # pages (page 7), every KV head of the 32B layout
+    p = _build(1, 40, 8, [9000], 7, seed=5)
+    announce("fp8_kv_decode_attention_ws one sequence of 9000 tokens")
+    _check(_gpu(p, "auto"), p, "one long sequence")
+
+
+def test_many_short_sequences_share_workgroups():
+    rng = np.random.default_rng(3)
+    lens = rng.integers(0, 40, size=300).astype(np.int32)
+    lens[::7] = 0
+    p = _build(300, 16, 4, lens, 16, seed=7)
+    announce("fp8_kv_decode_attention_ws 300 short sequences")
+    _check(_gpu(p, "auto"), p, "300 short sequences")
+
+
+def test_split_not_taken_falls_back():
+    # Hkv = 3 does not divide the 8 waves; more than 2048 sequences; a
+    # workspace below the size asked for: all run the one-pass kernel
+    assert binding.attention_workspace_bytes(4, 12, 3, 128) == 0
+    assert binding.attention_workspace_bytes(2049, 8, 2, 128) == 0
+    n = binding.attention_workspace_bytes(3, 10, 2, 128)
+    assert n > 0
+    p = _build(3, 10, 2, [50, 700, 3], 16, seed=21)
+    small = torch.empty((n - 16,), dtype=torch.uint8, device="cuda:0")
+    announce("fp8_kv_decode_attention_ws workspace too small")
+    _check(_gpu(p, small), p, "workspace too small")
+    lens = np.full(2100, 3, dtype=np.int32)
+    q = _build(2100, 8, 2, lens, 4, seed=2)
+    announce("fp8_kv_decode_attention_ws 2100 sequences")
+    _check(_gpu(q, "auto"), q, "2100 sequences", rows=[0, 1000, 2099])
+
+
+def test_split_is_bitwise_repeatable():
+    p = _build(5, 40, 8, [3000, 10, 2047, 0, 513], 16, seed=9)
+    announce("fp8_kv_decode_attention_ws repeated")
+    a, b = _gpu(p, "auto"), _gpu(p, "auto")
+    assert np.array_equal(a, b)
+    _check(a, p, "repeatable")
+
+
+@pytest.mark.parametrize("ws", WS)
+def test_skipped_tokens_and_clamped_lengths(ws):
     p = _build(3, 8, 2, [40, 40, 40], 8, seed=11)
     # sequence 0: one page entry negative, sequence 1: one past the cache;
     # the oracle is given the same tokens removed (their page dropped)
@@ -89,8 +143,8 @@ def test_skipped_tokens_and_clamped_lengths():
     t[0, 1] = -3
     t[1, 2] = num_slots // 8 + 5
     q = dict(p, table=t)
-    announce("fp8_kv_decode_attention skipped tokens")
-    got = _gpu(q)
+    announce(f"fp8_kv_decode_attention skipped tokens workspace {ws}")
+    got = _gpu(q, ws)
     for b, drop in ((0, 1), (1, 2)):
         keep_pages = [pg for i, pg in enumerate(p["table"][b, :5]) if i != drop]
         ref_table = np.array([keep_pages], dtype=np.int32)
@@ -98,22 +152,23 @@ def test_skipped_tokens_and_clamped_lengths():
         _check(got[b:b + 1], r, f"skipped page of sequence {b}")
     # lengths beyond max_blocks * page are clamped to it
     c = dict(p, lens=np.array([40, 500, 41], np.int32))
-    got = _gpu(c)
+    got = _gpu(c, ws)
     _check(got, dict(p, lens=np.array([40, 40, 40], np.int32)), "clamped lengths")
 
 
-def test_full_32b_batch_sampled():
+@pytest.mark.parametrize("ws", WS)
+def test_full_32b_batch_sampled(ws):
     cfg = workloads.ATT_32B
     B, Hq, Hkv, D, page = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["page"]
     lens = workloads.att_lengths(B, cfg["min_len"], cfg["max_len"], 0)
     table, num_slots = workloads.att_block_table(lens, page, 0)
-    announce(f"fp8_kv_decode_attention full 32B batch B{B} slots{num_slots}")
+    announce(f"fp8_kv_decode_attention full 32B batch B{B} slots{num_slots} workspace {ws}")
     q = workloads.att_query(B, Hq, D, 0)
     kc = workloads.att_random_codes(num_slots, Hkv * D, 0)
     vc = workloads.att_random_codes(num_slots, Hkv * D, 1)
     # scales that keep the scores of random codes in a softmax-relevant range
     p = dict(q=q, sq=kv.kv_scale(q), kc=kc, vc=vc, sk=np.float32(2.0 ** -12),
              sv=np.float32(2.0 ** -8), table=table, lens=lens, Hkv=Hkv, page=page)
-    got = _gpu(p)
+    got = _gpu(p, ws)
     rows = [0, 17, 40, 63]
     _check(got, p, "32B batch", rows=rows)
