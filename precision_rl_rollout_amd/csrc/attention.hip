@@ -594,7 +594,9 @@ hipError_t launch_fp8_decode_attention(const uint16_t* q, const float* q_scale,
 //    workspace slot i + b: i and b both grow along the batch, so slots are
 //    distinct, fewer than gridDim.x + B.
 //  * A second kernel combines, per (sequence, query head), the slots of the
-//    workgroups whose ranges meet the sequence, and rounds once to bf16.
+//    workgroups whose ranges meet the sequence (for a small batch, four
+//    thread groups each take a quarter of them and meet in LDS), and
+//    rounds once to bf16.
 //
 // Workspace: [per, prefix sums of the lengths (B + 1)] as int64, padded to
 // 256 bytes, then (gridDim.x + B) x Hq partial results of kAttD + 2 floats.
@@ -762,55 +764,90 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_span_kernel(
   }
 }
 
-// Thread (h, d) of workgroup (b, y), h = 4 y + threadIdx.x / 128: combines
-// the partial results of the workgroups whose ranges meet sequence b, in
-// one online pass over batches of kSpanBatch independent loads.
+// Combines, for sequence b, the partial results of the workgroups whose
+// ranges meet it.  A workgroup of 512 threads serves 4 / kGroups query heads
+// of one sequence; thread (head, q, d) takes every kGroups-th partial
+// result from the q-th on, in one online pass over batches of kSpanBatch
+// independent loads, and with kGroups > 1 the groups meet in LDS.  (Many
+// partial results per sequence -- a small batch -- take 4 groups; a large
+// batch, a few per sequence, takes 1.)
+template <int kGroups>
 __global__ __launch_bounds__(512) void fp8_decode_attention_combine_kernel(
     const int32_t* __restrict__ seq_lens, int Hq, int64_t n_cap,
     const int64_t* __restrict__ ws_pre, const float* __restrict__ ws_part,
     const float* __restrict__ v_scale, uint16_t* __restrict__ out) {
+  constexpr int kHeads = 4 / kGroups;
+  __shared__ float gm[4], gl[4], go[4][kAttD];
   const int b = blockIdx.x;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 7), d = threadIdx.x & (kAttD - 1);
-  if (h >= Hq) return;
+  const int hl = threadIdx.x / (kAttD * kGroups);
+  const int q = (threadIdx.x / kAttD) % kGroups, d = threadIdx.x & (kAttD - 1);
+  const int h = blockIdx.y * kHeads + hl;
+  if (kGroups == 1 && h >= Hq) return;                // (kGroups > 1: one head, h < Hq)
   const int64_t v = seq_lens[b];
   const int64_t n = min(v < 0 ? (int64_t)0 : v, n_cap);
-  float res = 0.f;
-  if (n > 0) {
-    const int64_t per = ws_pre[0], P = ws_pre[1 + b];
-    const int64_t i0 = P / per, i1 = (P + n - 1) / per;
-    const int64_t stride = (int64_t)Hq * kSpanPart;
-    const float* base = ws_part + (i0 + b) * stride + (int64_t)h * kSpanPart;
-    const int cnt = (int)(i1 - i0 + 1);
-    float M = -__builtin_inff(), L = 0.f, O = 0.f;
-    for (int k0 = 0; k0 < cnt; k0 += kSpanBatch) {
-      float pm[kSpanBatch], pl[kSpanBatch], po[kSpanBatch];
-#pragma unroll
-      for (int u = 0; u < kSpanBatch; ++u) {
-        const bool in = k0 + u < cnt;
-        const float* pp = base + (in ? (int64_t)(k0 + u) * stride : 0);
-        pm[u] = in ? pp[kAttD] : -__builtin_inff();
-        pl[u] = pp[kAttD + 1];
-        po[u] = pp[d];
-      }
-      float mb = pm[0];
-#pragma unroll
-      for (int u = 1; u < kSpanBatch; ++u) mb = fmaxf(mb, pm[u]);
-      const float mn = fmaxf(M, mb);
-      if (mn == -__builtin_inff()) continue;          // nothing attended so far
-      const float a = __builtin_amdgcn_exp2f(M - mn);  // (0 while M is -inf)
-      L *= a;
-      O *= a;
-#pragma unroll
-      for (int u = 0; u < kSpanBatch; ++u) {
-        const float f = __builtin_amdgcn_exp2f(pm[u] - mn);   // 0 for empty pieces
-        L += pl[u] * f;
-        O += po[u] * f;
-      }
-      M = mn;
-    }
-    res = L > 0.f ? *v_scale * (O / L) : 0.f;
+  uint16_t* o = out + ((int64_t)b * Hq + h) * kAttD;
+  if (n == 0) {                                       // (uniform in the workgroup)
+    if (q == 0) o[d] = 0;
+    return;
   }
-  out[((int64_t)b * Hq + h) * kAttD + d] = (uint16_t)f32_to_bf16_rne(res);
+  const int64_t per = ws_pre[0], P = ws_pre[1 + b];
+  const int64_t i0 = P / per, i1 = (P + n - 1) / per;
+  const int64_t stride = (int64_t)Hq * kSpanPart;
+  const float* base = ws_part + (i0 + b) * stride + (int64_t)h * kSpanPart;
+  const int cnt = (int)(i1 - i0 + 1);
+  float M = -__builtin_inff(), L = 0.f, O = 0.f;
+  for (int k0 = q; k0 < cnt; k0 += kGroups * kSpanBatch) {
+    float pm[kSpanBatch], pl[kSpanBatch], po[kSpanBatch];
+#pragma unroll
+    for (int u = 0; u < kSpanBatch; ++u) {
+      const int k = k0 + kGroups * u;
+      const bool in = k < cnt;
+      const float* pp = base + (in ? (int64_t)k * stride : 0);
+      pm[u] = in ? pp[kAttD] : -__builtin_inff();
+      pl[u] = pp[kAttD + 1];
+      po[u] = pp[d];
+    }
+    float mb = pm[0];
+#pragma unroll
+    for (int u = 1; u < kSpanBatch; ++u) mb = fmaxf(mb, pm[u]);
+    const float mn = fmaxf(M, mb);
+    if (mn == -__builtin_inff()) continue;            // nothing attended so far
+    const float a = __builtin_amdgcn_exp2f(M - mn);    // (0 while M is -inf)
+    L *= a;
+    O *= a;
+#pragma unroll
+    for (int u = 0; u < kSpanBatch; ++u) {
+      const float f = __builtin_amdgcn_exp2f(pm[u] - mn);   // 0 for empty pieces
+      L += pl[u] * f;
+      O += po[u] * f;
+    }
+    M = mn;
+  }
+  if constexpr (kGroups > 1) {
+    if (d == 0) {
+      gm[q] = M;
+      gl[q] = L;
+    }
+    go[q][d] = O;
+    __syncthreads();
+    if (q != 0) return;
+    float Mt = gm[0];
+#pragma unroll
+    for (int k = 1; k < kGroups; ++k) Mt = fmaxf(Mt, gm[k]);
+    float Lt = 0.f, Ot = 0.f;
+    if (Mt != -__builtin_inff()) {
+#pragma unroll
+      for (int k = 0; k < kGroups; ++k) {
+        const float f = __builtin_amdgcn_exp2f(gm[k] - Mt);
+        Lt += gl[k] * f;
+        Ot += go[k][d] * f;
+      }
+    }
+    L = Lt;
+    O = Ot;
+  }
+  const float res = L > 0.f ? *v_scale * (O / L) : 0.f;
+  o[d] = (uint16_t)f32_to_bf16_rne(res);
 }
 
 int64_t fp8_decode_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t D) {
@@ -856,9 +893,15 @@ bool launch_fp8_decode_attention_span(const uint16_t* q, const float* q_scale,
       return true;
   }
 #undef PRR_ATT_SPAN
-  hipLaunchKernelGGL(fp8_decode_attention_combine_kernel, dim3((unsigned)B, (unsigned)((Hq + 3) / 4)),
-                     dim3(512), 0, stream, seq_lens, (int)Hq, max_blocks * page, ws_pre, ws_part,
-                     v_scale, out);
+  // about grid / B + 1 partial results per sequence
+  if (B * 8 <= grid)
+    hipLaunchKernelGGL(fp8_decode_attention_combine_kernel<4>, dim3((unsigned)B, (unsigned)Hq),
+                       dim3(512), 0, stream, seq_lens, (int)Hq, max_blocks * page, ws_pre,
+                       ws_part, v_scale, out);
+  else
+    hipLaunchKernelGGL(fp8_decode_attention_combine_kernel<1>,
+                       dim3((unsigned)B, (unsigned)((Hq + 3) / 4)), dim3(512), 0, stream,
+                       seq_lens, (int)Hq, max_blocks * page, ws_pre, ws_part, v_scale, out);
   *err = hipGetLastError();
   return true;
 }
