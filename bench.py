@@ -89,6 +89,8 @@ KERNEL_SOURCES = {
     "w8a8_int8_channel_gemm@decode7b_upgate": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
     "w8a8_block_gemm_grouped": ["gemm_decode.hip", "mfma.h", "prr_device.h"],
     "tis_token_weights": ["tis.hip", "prr_device.h"],
+    "fp8_kv_scale_recalibrate": ["kv_fp8.hip", "prr_device.h"],
+    "fp8_kv_cache_write": ["kv_fp8.hip", "prr_device.h"],
     "fp8_kv_decode_attention": ["attention.hip", "prr_device.h"],
     # M = 8192 runs the many-token kernel.
     "w8a8_block_gemm@prefill32b": ["gemm_prefill.hip", "mfma.h", "prr_device.h"],
@@ -478,7 +480,7 @@ def run_kv32b(args, torch, B, W):
                          "achieved": round(b_write / us["fp8_kv_cache_write"] / 1e3, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(b_write / us["fp8_kv_cache_write"] / 1e3 / HBM_PEAK_GBS, 4),
-                         "traffic": None},
+                         "traffic": measured_traffic("fp8_kv_cache_write", "kv32b_prefill")},
             "kernels": {"fp8_kv_scale_recalibrate": {"us": round(us["fp8_kv_scale_recalibrate"], 2),
                                                      "algorithmic_bytes": b_recal,
                                                      "GB/s": round(b_recal / us["fp8_kv_scale_recalibrate"] / 1e3, 1)},
