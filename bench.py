@@ -30,7 +30,10 @@ every expert, activation quantization, the grouped GEMM), ``tis_batch``
 ``att32b_decode`` (decode attention over an FP8 KV cache: 64 sequences of
 1024-8192 tokens, 40 query heads over 8 KV heads; the call with its
 workspace, which splits the batch's tokens over the CUs; ``batch_sizes``
-adds the first 1, 2, 8 and 64 sequences with and without the split).
+adds the first 1, 2, 8 and 64 sequences with and without the split),
+``sync32b_requant`` (quantize-on-receive: the 32B up/gate weight arriving
+in 8 shards from pinned host memory, each quantized into place in the full
+FP8 weight while the next is in transfer).
 """
 
 from __future__ import annotations
@@ -729,6 +732,93 @@ def run_tis(args, torch, B, W):
     return line
 
 
+def run_sync32b(args, torch, B, W):
+    """Quantize-on-receive of the 32B-class up/gate weight (Wt [27648, 5120]
+    bf16, 283 MB), the step that weight synchronization into the inference
+    engine adds: the weight arrives in 8 chunks of 3456 rows (one tensor-
+    parallel-8 shard each) from pinned host memory on a copy stream (the
+    host link stands in for the link from the trainer), into two staging
+    buffers in turn; each chunk is quantized into place in the full FP8
+    weight (fp8_weight_block_quant_into) on the compute stream as soon as it
+    has landed, while the next one is in transfer.  Reported: the step
+    against the bare transfer of the same chunks and the bare quantization
+    of resident chunks (all host-timed over whole steps)."""
+    N, K, chunks = 27648, 5120, 8
+    rows = N // chunks
+    dev = torch.device("cuda:0")
+    host_w = torch.empty((N, K), dtype=torch.int16, pin_memory=True)
+    host_w.copy_(torch.from_numpy(W.weight(N, K, seed=0).view(np.int16)))
+    stage = [torch.empty((rows, K), dtype=torch.int16, device=dev) for _ in range(2)]
+    q = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sc = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    copy_stream = torch.cuda.Stream(device=dev)          # default priority
+    comp = torch.cuda.current_stream(dev)
+    landed = [torch.cuda.Event() for _ in range(chunks)]
+    consumed = [torch.cuda.Event() for _ in range(chunks)]
+
+    def sync_step(quantize=True, transfer=True):
+        for c in range(chunks):
+            buf = stage[c % 2]
+            if transfer:
+                with torch.cuda.stream(copy_stream):
+                    if c >= 2:
+                        copy_stream.wait_event(consumed[c - 2])
+                    buf.copy_(host_w[c * rows:(c + 1) * rows], non_blocking=True)
+                    landed[c].record(copy_stream)
+                comp.wait_event(landed[c])
+            if quantize:
+                B.fp8_weight_block_quant_into(buf, q, sc, row0=c * rows)
+            consumed[c].record(comp)
+
+    def host_timed(f, n):
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            f()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n
+
+    dt = host_timed(lambda: sync_step(), args.steps)
+    dt_copy = host_timed(lambda: sync_step(quantize=False), args.steps)
+    dt_quant = host_timed(lambda: sync_step(transfer=False), args.steps)
+    torch.cuda.synchronize()
+    # the step's result is the full weight's quantization
+    ref_q, ref_s = B.fp8_weight_block_quant(torch.from_numpy(W.weight(N, K, seed=0).view(np.int16)).to(dev))
+    sync_step()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(q, ref_q) and torch.equal(sc, ref_s))
+    wbytes = 2 * N * K
+    qbytes = quant_bytes(N, K, (N // 128) * (K // 128))
+    line = {"metric": METRIC, "value": round(wbytes / dt / 1e9, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
+            "config": {"workload": "sync32b_requant", "N": N, "K": K, "chunks": chunks,
+                       "source": "pinned host memory (stands in for the inter-GPU link)",
+                       "value": "bf16 weight bytes received and quantized per second"},
+            "transfer_only_ms": round(dt_copy * 1e3, 4),
+            "quantize_only_ms": round(dt_quant * 1e3, 4),
+            "overhead_vs_transfer": round(dt / dt_copy - 1.0, 4),
+            "link_GB/s": round(wbytes / dt_copy / 1e9, 1),
+            "same_as_whole_weight_quant": same,
+            "roofline": {"bound": "hbm", "kernel": "fp8_weight_block_quant_into",
+                         "achieved": round(qbytes / dt_quant / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(qbytes / dt_quant / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": None}}
+    if not args.no_cpu_baseline:
+        from oracle import quant as oq
+        chunk = W.weight(N, K, seed=0)[:rows]
+        t0 = time.perf_counter()
+        oq.fp8_weight_block_quant(chunk)
+        ct = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(2 * rows * K / ct / 1e9, 4), "unit": "GB/s",
+                                "cores": cpu_threads(), "kind": "oracle", "seconds": round(ct, 2),
+                                "sample": f"one chunk ({rows} x {K}) quantized by the oracle"}
+    return line
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -737,7 +827,7 @@ def main(argv=None):
     ap.add_argument("--workload", default="decode7b_upgate",
                     choices=["decode7b_upgate", "decode32b_sweep", "prefill32b", "stack32b_requant",
                              "kv32b_prefill", "moe_decode", "tis_batch", "stack32b_gemm",
-                             "att32b_decode"])
+                             "att32b_decode", "sync32b_requant"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (outside the "
@@ -767,7 +857,7 @@ def main(argv=None):
            "prefill32b": run_prefill32b, "stack32b_requant": run_stack32b,
            "kv32b_prefill": run_kv32b, "moe_decode": run_moe_decode,
            "tis_batch": run_tis, "stack32b_gemm": run_stack_gemm,
-           "att32b_decode": run_att}[args.workload]
+           "att32b_decode": run_att, "sync32b_requant": run_sync32b}[args.workload]
     line = run(args, torch, B, W)
     print(json.dumps(line), flush=True)
     return 0

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PRR_ABI_VERSION 7
+#define PRR_ABI_VERSION 8
 
 typedef enum prr_status {
   PRR_OK = 0,
@@ -100,6 +100,31 @@ typedef enum prr_status {
 prr_status fp8_weight_block_quant(const uint16_t* w_bf16, int64_t N, int64_t K,
                                   uint8_t* w_fp8, float* w_scale,
                                   hipStream_t stream);
+
+/*
+ * fp8_weight_block_quant_into -- the same quantization of one shard of a
+ * weight, written in place into the full weight's code and scale arrays:
+ * the step that turns the bf16 shard a weight synchronization delivers into
+ * the inference engine's FP8 weight (FP8-RL, abstract: the changing policy
+ * weights are quantized again and synchronized into the inference engine
+ * every step), chunk by chunk as the shard arrives.
+ *   w_bf16   in   [rows, cols] bf16 bits, row stride ld_w elements.
+ *   q_fp8    out  [rows, cols] e4m3 codes, row stride ld_q bytes.
+ *   scale    out  [ceil(rows/128), ceil(cols/128)] fp32, row stride
+ *                 ld_scale floats; block (i, j) covers rows 128i.. and
+ *                 columns 128j.. of the shard.
+ *   The shard is quantized as a matrix of its own (blocks anchored at its
+ *   first row and column, partial blocks at its edges).  With q_fp8 and
+ *   scale pointing at row 128a and column 128b of a full weight's arrays
+ *   (ld_q = K, ld_scale = ceil(K/128)), the result is that part of
+ *   fp8_weight_block_quant of the full weight: the blocks are the same.
+ *   rows, cols >= 0; ld_w, ld_q >= cols; ld_scale >= ceil(cols/128)
+ *   (PRR_ERR_INVALID_ARG otherwise); w_bf16 and q_fp8 16-byte aligned,
+ *   scale 4-byte aligned (PRR_ERR_MISALIGNED otherwise).
+ */
+prr_status fp8_weight_block_quant_into(const uint16_t* w_bf16, int64_t rows, int64_t cols,
+                                       int64_t ld_w, uint8_t* q_fp8, int64_t ld_q, float* scale,
+                                       int64_t ld_scale, hipStream_t stream);
 
 /*
  * fp8_act_token_quant -- FP8 e4m3 quantization of bf16 activations in

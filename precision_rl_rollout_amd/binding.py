@@ -27,6 +27,7 @@ _I64 = ctypes.c_int64
 
 _SIGNATURES = {
     "fp8_weight_block_quant": [_P, _I64, _I64, _P, _P, _P],
+    "fp8_weight_block_quant_into": [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P],
     "fp8_act_token_quant": [_P, _I64, _I64, _P, _P, _P],
     "w8a8_block_gemm": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P],
     "int8_weight_channel_quant": [_P, _I64, _I64, _P, _P, _P],
@@ -53,7 +54,7 @@ _lib = None
 
 # PRR_ABI_VERSION of the signatures below; a library of another version is
 # refused at load time.
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class PrrError(RuntimeError):
@@ -147,6 +148,34 @@ def fp8_weight_block_quant(w: torch.Tensor, out=None, scale=None):
     _check("fp8_weight_block_quant",
            load().fp8_weight_block_quant(_ptr(w), N, K, _ptr(q), _ptr(s), _stream(w)))
     return q, s
+
+
+def fp8_weight_block_quant_into(w: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                                row0: int = 0, col0: int = 0):
+    """Quantize the bf16 shard w [rows, cols] (any row stride, unit column
+    stride) into rows row0.. and columns col0.. of a full weight's codes
+    uint8 [N, K] and scales fp32 [ceil(N/128), ceil(K/128)]; row0 and col0
+    are multiples of 128 (the shard's blocks are then the full weight's)."""
+    if w.dtype not in (torch.bfloat16, torch.int16) or not w.is_cuda or w.dim() != 2:
+        raise ValueError("w: expected a 2-D CUDA bf16 tensor")
+    if w.shape[1] > 1 and w.stride(1) != 1:
+        raise ValueError("w: columns must be contiguous")
+    if row0 % 128 or col0 % 128 or row0 < 0 or col0 < 0:
+        raise ValueError("row0 and col0 must be non-negative multiples of 128")
+    rows, cols = w.shape
+    N, K = codes.shape
+    _operand(codes, torch.uint8, (N, K), "codes")
+    _operand(scales, torch.float32, (_cdiv(N, 128), _cdiv(K, 128)), "scales")
+    if row0 + rows > N or col0 + cols > K:
+        raise ValueError("the shard does not fit the full weight at (row0, col0)")
+    if rows == 0 or cols == 0:
+        return codes, scales
+    _check("fp8_weight_block_quant_into",
+           load().fp8_weight_block_quant_into(
+               w.data_ptr(), rows, cols, w.stride(0), codes.data_ptr() + row0 * K + col0, K,
+               scales.data_ptr() + 4 * ((row0 // 128) * scales.shape[1] + col0 // 128),
+               scales.shape[1], _stream(w)))
+    return codes, scales
 
 
 def fp8_act_token_quant(a: torch.Tensor, out=None, scale=None):

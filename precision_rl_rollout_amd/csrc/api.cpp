@@ -83,7 +83,26 @@ prr_status fp8_weight_block_quant(const uint16_t* w_bf16, int64_t N, int64_t K, 
   const int64_t blocks = ((N + 127) / 128) * ((K + 127) / 128);
   if (N == 0 || K == 0) return check_dims(N, K);
   PRR_TRY(quant_common(w_bf16, N, K, w_fp8, w_scale, blocks));
-  return from_hip(prr::launch_fp8_weight_block_quant(w_bf16, N, K, w_fp8, w_scale, stream));
+  return from_hip(prr::launch_fp8_weight_block_quant(w_bf16, N, K, K, w_fp8, K, w_scale,
+                                                     (K + 127) / 128, stream));
+}
+
+prr_status fp8_weight_block_quant_into(const uint16_t* w_bf16, int64_t rows, int64_t cols,
+                                       int64_t ld_w, uint8_t* q_fp8, int64_t ld_q, float* scale,
+                                       int64_t ld_scale, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return PRR_ERR_INVALID_ARG;
+  if (rows == 0 || cols == 0) return check_dims(rows, cols);
+  PRR_TRY(check_dims(rows, cols));
+  PRR_TRY(check_dims(ld_w, ld_q, ld_scale));
+  const int64_t nbk = (cols + 127) / 128;
+  if (ld_w < cols || ld_q < cols || ld_scale < nbk) return PRR_ERR_INVALID_ARG;
+  if (w_bf16 == nullptr || q_fp8 == nullptr || scale == nullptr) return PRR_ERR_INVALID_ARG;
+  PRR_TRY(check_ptrs({w_bf16, q_fp8}));
+  if (reinterpret_cast<uintptr_t>(scale) % 4 != 0) return PRR_ERR_MISALIGNED;
+  if (((rows + 127) / 128) * nbk > kMaxGrid) return PRR_ERR_UNSUPPORTED_SHAPE;
+  PRR_TRY(check_device());
+  return from_hip(prr::launch_fp8_weight_block_quant(w_bf16, rows, cols, ld_w, q_fp8, ld_q,
+                                                     scale, ld_scale, stream));
 }
 
 prr_status fp8_act_token_quant(const uint16_t* a_bf16, int64_t M, int64_t K, uint8_t* a_fp8,

@@ -7,8 +7,10 @@
 
 namespace prr {
 
-hipError_t launch_fp8_weight_block_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q,
-                                         float* scale, hipStream_t stream);
+// (row strides: ldw input elements, ldq code bytes, lds scale floats)
+hipError_t launch_fp8_weight_block_quant(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                                         uint8_t* q, int64_t ldq, float* scale, int64_t lds,
+                                         hipStream_t stream);
 hipError_t launch_fp8_act_token_quant(const uint16_t* a, int64_t M, int64_t K, uint8_t* q,
                                       float* scale, hipStream_t stream);
 hipError_t launch_w8a8_block_gemm(const uint8_t* A, const float* sa, const uint8_t* W,

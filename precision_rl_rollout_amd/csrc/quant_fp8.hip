@@ -22,7 +22,8 @@ namespace prr {
 template <int kClass>
 __device__ __forceinline__ void encode_block_rows(const uint4 (&v)[8], const BlockDiv& d,
                                                   bool full, uint8_t* __restrict__ q, int64_t N,
-                                                  int64_t K, int64_t row0, int seg, int64_t col) {
+                                                  int64_t K, int64_t ldq, int64_t row0, int seg,
+                                                  int64_t col) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t r = row0 + i * 16 + seg;
@@ -30,19 +31,22 @@ __device__ __forceinline__ void encode_block_rows(const uint4 (&v)[8], const Blo
     if constexpr (kClass == 0) c = e4m3_zero_chunk(v[i]);
     else c = e4m3_chunk<kClass == 2>(v[i], d);
     if (full) {
-      *reinterpret_cast<uint2*>(q + r * K + col) = c;
+      *reinterpret_cast<uint2*>(q + r * ldq + col) = c;
     } else {
       const uint32_t cw[2] = {c.x, c.y};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (r < N && col + e < K) q[r * K + col + e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
+        if (r < N && col + e < K) q[r * ldq + col + e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
     }
   }
 }
 
+// An N x K matrix with row strides ldw (input, elements), ldq (codes,
+// bytes) and lds (scales, floats); the whole-weight call has ldw = ldq = K
+// and lds = nbk.
 __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
-    const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ q,
-    float* __restrict__ scale, int nbk) {
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldw, uint8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale, int64_t lds, int nbk) {
   const int bi = blockIdx.x / nbk;
   const int bj = blockIdx.x - bi * nbk;
   const int tid = threadIdx.x;
@@ -50,16 +54,18 @@ __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
   const int l16 = tid & 15;       // 8-element chunk within the row segment
   const int64_t row0 = (int64_t)bi * kBlock;
   const int64_t col = (int64_t)bj * kBlock + l16 * 8;
-  // Workgroup-uniform: a complete block with 16-byte aligned rows takes the
-  // vector path; edge blocks of ragged shapes take the bounds-checked one.
-  const bool full = (row0 + kBlock <= N) && ((int64_t)(bj + 1) * kBlock <= K) && (K % 8 == 0);
+  // Workgroup-uniform: a complete block with 16-byte aligned input rows and
+  // 8-byte aligned code rows takes the vector path; edge blocks of ragged
+  // shapes take the bounds-checked one.
+  const bool full = (row0 + kBlock <= N) && ((int64_t)(bj + 1) * kBlock <= K) &&
+                    (ldw % 8 == 0) && (ldq % 8 == 0);
 
   uint4 v[8];
   if (full) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t r = row0 + i * 16 + seg;
-      v[i] = load_once16(w + r * K + col);
+      v[i] = load_once16(w + r * ldw + col);
     }
   } else {
 #pragma unroll
@@ -68,7 +74,7 @@ __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
       uint32_t h[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        h[e] = (r < N && col + e < K) ? (uint32_t)w[r * K + col + e] : 0u;
+        h[e] = (r < N && col + e < K) ? (uint32_t)w[r * ldw + col + e] : 0u;
       v[i] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                         h[6] | (h[7] << 16));
     }
@@ -88,12 +94,12 @@ __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
   m = max(max(red[0], red[1]), max(red[2], red[3]));
   const float amax = __uint_as_float(m << 16);
   const float s = div_rn(amax, kFp8Max);
-  if (tid == 0) scale[(int64_t)bi * nbk + bj] = s;
+  if (tid == 0) scale[(int64_t)bi * lds + bj] = s;
 
   const BlockDiv d = block_div(s);
-  if (s == 0.0f) encode_block_rows<0>(v, d, full, q, N, K, row0, seg, col);
-  else if (d.tiny) encode_block_rows<2>(v, d, full, q, N, K, row0, seg, col);
-  else encode_block_rows<1>(v, d, full, q, N, K, row0, seg, col);
+  if (s == 0.0f) encode_block_rows<0>(v, d, full, q, N, K, ldq, row0, seg, col);
+  else if (d.tiny) encode_block_rows<2>(v, d, full, q, N, K, ldq, row0, seg, col);
+  else encode_block_rows<1>(v, d, full, q, N, K, ldq, row0, seg, col);
 }
 
 // ---------------------------------------------------------------------------
@@ -143,12 +149,13 @@ __global__ __launch_bounds__(256) void fp8_act_group_kernel(
   }
 }
 
-hipError_t launch_fp8_weight_block_quant(const uint16_t* w, int64_t N, int64_t K, uint8_t* q,
-                                         float* scale, hipStream_t stream) {
+hipError_t launch_fp8_weight_block_quant(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                                         uint8_t* q, int64_t ldq, float* scale, int64_t lds,
+                                         hipStream_t stream) {
   const int64_t nbn = (N + kBlock - 1) / kBlock, nbk = (K + kBlock - 1) / kBlock;
   const int64_t blocks = nbn * nbk;
   hipLaunchKernelGGL(fp8_weight_block_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w,
-                     N, K, q, scale, (int)nbk);
+                     N, K, ldw, q, ldq, scale, lds, (int)nbk);
   return hipGetLastError();
 }
 

@@ -38,7 +38,8 @@ def _gpu_visible():
 
 def test_header_declares_the_boundary():
     names = set(_declared())
-    assert names == {"fp8_weight_block_quant", "fp8_act_token_quant", "w8a8_block_gemm",
+    assert names == {"fp8_weight_block_quant", "fp8_weight_block_quant_into",
+                     "fp8_act_token_quant", "w8a8_block_gemm",
                      "int8_weight_channel_quant", "int8_act_token_quant",
                      "w8a8_int8_channel_gemm", "w8a8_block_gemm_grouped",
                      "fp8_kv_scale_recalibrate",
@@ -285,3 +286,27 @@ def test_attention_ws_argument_checks():
     assert z(4, 40, 8, 128, None) == INVALID
     assert z(-1, 40, 8, 128, ctypes.addressof(n)) == INVALID
     assert z(0, 40, 8, 128, ctypes.addressof(n)) == OK and n.value == 0
+
+
+def test_quant_into_argument_checks():
+    c = lambda *a: binding.call("fp8_weight_block_quant_into", *a)
+    ok = [FAKE, 256, 384, 512, FAKE, 1024, FAKE, 8, None]
+    for i, v in ((1, -1), (2, -5), (3, 383), (5, 100), (7, 2), (3, -1)):
+        a = list(ok)
+        a[i] = v
+        assert c(*a) == INVALID, (i, v)
+    for i in (0, 4, 6):
+        a = list(ok)
+        a[i] = None
+        assert c(*a) == INVALID
+    a = list(ok)
+    a[0] = ODD
+    assert c(*a) == MISALIGNED
+    a = list(ok)
+    a[6] = FAKE + 2                              # scales need 4-byte alignment only
+    assert c(*a) == MISALIGNED
+    a = list(ok)
+    a[6] = FAKE + 4
+    assert c(*a) == NO_DEVICE
+    assert c(*ok) == NO_DEVICE
+    assert c(None, 0, 384, 0, None, 0, None, 0, None) == OK      # empty: nothing touched
