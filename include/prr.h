@@ -344,7 +344,7 @@ prr_status fp8_kv_decode_attention(const uint16_t* q_bf16, const float* q_scale,
  *   fp8_kv_decode_attention_workspace_size: *bytes = the workspace the _ws
  *       call uses for B sequences of Hq query heads over Hkv KV heads of D
  *       on the current device (0: the shape takes the one-pass kernel:
- *       D != 128, B > 2048, or Hkv not a divisor of 8).
+ *       D != 128, B > 2048, or Hkv > 8).
  *   workspace: device memory, 16-byte aligned, not shared with a call in
  *       flight on another stream; NULL or workspace_bytes below the size ->
  *       the one-pass kernel (never an error).  The library does not keep

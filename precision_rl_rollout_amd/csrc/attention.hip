@@ -589,7 +589,8 @@ hipError_t launch_fp8_decode_attention(const uint16_t* q, const float* q_scale,
 //    workgroups; the ranges past the batch are empty).  Workgroup i walks the
 //    sequences its range meets; for each, wave w serves KV head
 //    w / (8 / Hkv) over iterations w % (8 / Hkv), ... of the overlap (the
-//    same token loop as the one-pass kernel), the waves of a head meet in
+//    same token loop as the one-pass kernel; waves past Hkv (8 / Hkv) idle
+//    when Hkv does not divide 8), the waves of a head meet in
 //    LDS, and the result (O unnormalized, m, l of every query head) goes to
 //    workspace slot i + b: i and b both grow along the batch, so slots are
 //    distinct, fewer than gridDim.x + B.
@@ -671,8 +672,10 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_span_kernel(
     else lo = mid + 1;
   }
 
-  const int wpg = kAttWaves / Hkv;                   // waves per KV head (Hkv divides 8)
+  // Waves per KV head; waves past Hkv x wpg (Hkv not a divisor of 8) idle.
+  const int wpg = kAttWaves / Hkv;
   const int kvh = wave / wpg, sub = wave - kvh * wpg;
+  const bool active = kvh < Hkv;
   const int g = lane >> 4, r = lane & 15;
   const uint32_t row_bytes = (uint32_t)Hkv * kAttD;
   const uint8_t* kbase = k_cache + (int64_t)kvh * kAttD + 32 * g;
@@ -684,14 +687,14 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_span_kernel(
   const BlockDiv dq = block_div(sq);
   const float cs = sq * (*k_scale) * softmax_scale * kLog2e;
   const float inv_page = 1.0f / (float)page;
-  const uint4* qrow = &qsh[kvh][(r * 4 + g) * 4];
+  const uint4* qrow = &qsh[active ? kvh : 0][(r * 4 + g) * 4];
   const int chunk_pages = min(kSpanTablePages, (1 << 30) / page);
 
   for (int b = lo; b < B && pre[b] < t1; ++b) {
     const int64_t s0 = max(t0, pre[b]) - pre[b], s1 = min(t1, pre[b + 1]) - pre[b];
     if (s1 <= s0) continue;                            // an empty sequence
     __syncthreads();                                   // last segment's readers of qsh / partials
-    if (sub == 0) {
+    if (sub == 0 && active) {
       const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)kvh * G + r) * kAttD + 32 * g;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -721,8 +724,9 @@ __global__ __launch_bounds__(kAttThreads) void fp8_decode_attention_span_kernel(
         tbase[e] = lim > 0 ? first * row_bytes : 0;
       }
       __syncthreads();
-      att_chunk<G>(tbase, tlim, (int)(c1 - c0), (uint32_t)(c0 - pa * page), page, inv_page,
-                   row_bytes, kbase, vbase, vt, tr_src, qrow, cs, sub, wpg, g, r, m, l, acc);
+      if (active)
+        att_chunk<G>(tbase, tlim, (int)(c1 - c0), (uint32_t)(c0 - pa * page), page, inv_page,
+                     row_bytes, kbase, vbase, vt, tr_src, qrow, cs, sub, wpg, g, r, m, l, acc);
     }
     // The waves of each KV head through LDS; the segment's partial result
     // of every query head to workspace slot blockIdx.x + b.
@@ -851,8 +855,8 @@ __global__ __launch_bounds__(512) void fp8_decode_attention_combine_kernel(
 }
 
 int64_t fp8_decode_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t D) {
-  if (D != kAttD || B < 1 || B > kSpanMaxB || Hkv < 1 || Hkv > kAttWaves ||
-      kAttWaves % Hkv != 0 || Hq < 1 || Hq % Hkv != 0 || Hq / Hkv > 8)
+  if (D != kAttD || B < 1 || B > kSpanMaxB || Hkv < 1 || Hkv > kAttWaves || Hq < 1 ||
+      Hq % Hkv != 0 || Hq / Hkv > 8)
     return 0;
   const int64_t head = ((B + 2) * 8 + 255) / 256 * 256;
   return head + ((int64_t)compute_units() + B) * Hq * kSpanPart * (int64_t)sizeof(float);

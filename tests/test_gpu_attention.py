@@ -13,7 +13,7 @@ invalid block-table entries, lengths beyond the table (clamped), and the
 32B-class layout (40 query heads over 8 KV heads) on sampled sequences of
 the full 64-sequence batch; for the split: one long sequence cut over every
 CU, hundreds of short sequences sharing workgroups, shapes it does not take
-(Hkv not a divisor of 8, more than 2048 sequences, a workspace too small),
+(more than 8 KV heads, more than 2048 sequences, a workspace too small),
 and bitwise-repeatable results.
 """
 
@@ -74,7 +74,8 @@ def _check(got, p, label, rows=None):
 
 @pytest.mark.parametrize("ws", WS)
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (12, 4), (8, 2), (10, 2), (12, 2),
-                                    (14, 2), (8, 1), (40, 8), (24, 3)])
+                                    (14, 2), (8, 1), (40, 8), (24, 3), (35, 5), (18, 6),
+                                    (14, 7), (36, 12)])
 def test_group_sizes(Hq, Hkv, ws):
     p = _build(3, Hq, Hkv, [37, 300, 1], 16, seed=Hq + Hkv)
     announce(f"fp8_kv_decode_attention Hq{Hq} Hkv{Hkv} workspace {ws}")
@@ -109,9 +110,11 @@ def test_many_short_sequences_share_workgroups():
 
 
 def test_split_not_taken_falls_back():
-    # Hkv = 3 does not divide the 8 waves; more than 2048 sequences; a
-    # workspace below the size asked for: all run the one-pass kernel
-    assert binding.attention_workspace_bytes(4, 12, 3, 128) == 0
+    # more than 8 KV heads (one wave each would not do); more than 2048
+    # sequences; a workspace below the size asked for: all run the one-pass
+    # kernel
+    assert binding.attention_workspace_bytes(4, 36, 12, 128) == 0
+    assert binding.attention_workspace_bytes(4, 12, 3, 128) > 0
     assert binding.attention_workspace_bytes(2049, 8, 2, 128) == 0
     n = binding.attention_workspace_bytes(3, 10, 2, 128)
     assert n > 0
