@@ -10,6 +10,10 @@ place into the full weight's code and scale arrays, against the CPU oracle.
 * A ragged shard is quantized as a matrix of its own (the oracle on the
   sub-matrix) and nothing outside its rows, columns and scale blocks is
   written.
+* Full size, in the launch configuration of the quantize-on-receive bench
+  (the 32B up/gate weight in 8 chunks of 3456 rows through two staging
+  buffers): equal to the whole-weight call, and to the oracle on sampled
+  blocks.
 """
 
 import numpy as np
@@ -81,3 +85,26 @@ def test_ragged_shard_writes_only_its_own_blocks():
     so = np.ones(hs.shape, dtype=bool)
     so[b0:b0 + rs.shape[0], bc0:bc0 + rs.shape[1]] = False
     assert np.isnan(hs[so]).all()
+
+
+def test_full_size_32b_upgate_in_eight_chunks():
+    N, K, chunks = 27648, 5120, 8
+    rows = N // chunks
+    w = workloads.weight(N, K, seed=0)
+    wd = bits_to_dev(w)
+    announce("fp8_weight_block_quant_into full-size 32B up/gate, 8 chunks")
+    q, s = _full_buffers(N, K)
+    stage = [torch.empty((rows, K), dtype=torch.int16, device=DEV) for _ in range(2)]
+    for c in range(chunks):
+        buf = stage[c % 2]
+        buf.copy_(wd[c * rows:(c + 1) * rows])
+        binding.fp8_weight_block_quant_into(buf, q, s, row0=c * rows)
+    wq, ws = binding.fp8_weight_block_quant(wd)
+    hq, hs = host(q), host(s)
+    assert np.array_equal(hq, host(wq)) and np.array_equal(hs.view(np.uint32), host(ws).view(np.uint32))
+    rng = np.random.default_rng(4)
+    blocks = sorted({(int(rng.integers(N // 128)), int(rng.integers(K // 128))) for _ in range(48)}
+                    | {(0, 0), (N // 128 - 1, K // 128 - 1), (rows // 128 - 1, 0), (rows // 128, 0)})
+    for (i, j), (rc, rs) in zip(blocks, quant.fp8_weight_blocks(w, blocks)):
+        assert np.array_equal(hq[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128], rc), (i, j)
+        assert np.float32(hs[i, j]).view(np.uint32) == np.float32(rs).view(np.uint32), (i, j)
