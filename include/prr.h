@@ -2,15 +2,19 @@
  * prr.h -- C ABI of libprr.so: MI355X (gfx950) kernels for 8-bit rollout.
  *
  * The calls implement the per-step re-quantization of freshly updated bf16
- * policy weights and activations into FP8 e4m3 with block scales, the W8A8
- * block-scaled linear layer with bf16 output, an INT8 per-channel variant
- * of both, and the FP8 KV cache (per-step scale recalibration and
- * quantize-on-write).  Sources:
+ * policy weights and activations into FP8 e4m3 with block scales (whole
+ * weights, or shards quantized into place as a weight synchronization
+ * delivers them), the W8A8 block-scaled linear layer with bf16 output (also
+ * grouped over the experts of a mixture-of-experts layer), an INT8
+ * per-channel variant of both, the FP8 KV cache (per-step scale
+ * recalibration, quantize-on-write, decode attention over the paged
+ * cache), and token-level TIS / MIS importance weights.  Sources:
  *   - "FP8-RL: A Practical and Stable Low-Precision Stack for LLM
  *     Reinforcement Learning", abstract: policy weights change every step
  *     and must be quantized again every step; item (i): FP8 W8A8
  *     linear-layer rollout with blockwise FP8 quantization; item (ii): FP8
- *     KV cache with per-step QKV scale recalibration.
+ *     KV cache with per-step QKV scale recalibration; item (iii):
+ *     token-level TIS / MIS rollout correction.
  *   - FlashRL article ("FlashRL: 8Bit Rollouts, Full Power RL"), sections
  *     on rollout quantization and online quantization with parameter
  *     updates: INT8 and FP8 rollout.
@@ -41,7 +45,8 @@
  *     memory-safe) results.
  * Pointers and memory:
  *   - Every pointer is a device pointer on the current HIP device, 16-byte
- *     aligned (PRR_ERR_MISALIGNED otherwise).  The caller allocates and owns
+ *     aligned (PRR_ERR_MISALIGNED otherwise; fp8_weight_block_quant_into's
+ *     scale pointer needs 4 bytes).  The caller allocates and owns
  *     every buffer; the library allocates nothing, frees nothing and keeps
  *     no pointer after the call returns.  Inputs and outputs must not
  *     overlap.
@@ -54,7 +59,9 @@
  *     caller's next synchronization with the stream.
  *   - Calls are stateless, thread-safe and deterministic: the same inputs
  *     give the same bits.  The only atomic is the integer maximum of the
- *     KV-scale recalibration, whose result does not depend on order.
+ *     KV-scale recalibration, whose result does not depend on order.  The
+ *     _ws calls use the caller's workspace as scratch for the call's
+ *     duration only (one call at a time per workspace).
  * Errors (returned synchronously, after argument checks and the launch):
  *   - PRR_ERR_INVALID_ARG: a negative dimension, a dimension above
  *     2^31 - 1, or a NULL pointer for a non-empty operand;
