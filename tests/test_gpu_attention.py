@@ -12,7 +12,9 @@ several thousand tokens, page sizes 16 and 5, tokens skipped through
 invalid block-table entries, lengths beyond the table (clamped), and the
 32B-class layout (40 query heads over 8 KV heads) on sampled sequences of
 the full 64-sequence batch; for the split: one long sequence cut over every
-CU, hundreds of short sequences sharing workgroups, shapes it does not take
+CU, hundreds of short sequences sharing workgroups, the most sequences it
+takes (2048), one-token pages with a workgroup range of more than 1024
+pages (its page table staged in several chunks), shapes it does not take
 (more than 8 KV heads, more than 2048 sequences, a workspace too small),
 and bitwise-repeatable results.
 """
@@ -175,3 +177,20 @@ def test_full_32b_batch_sampled(ws):
     got = _gpu(p, ws)
     rows = [0, 17, 40, 63]
     _check(got, p, "32B batch", rows=rows)
+
+
+def test_split_at_most_sequences():
+    lens = np.full(2048, 3, dtype=np.int32)
+    lens[::5] = 0
+    p = _build(2048, 8, 2, lens, 4, seed=2)
+    assert binding.attention_workspace_bytes(2048, 8, 2, 128) > 0
+    announce("fp8_kv_decode_attention_ws 2048 sequences")
+    _check(_gpu(p, "auto"), p, "2048 sequences", rows=[0, 1, 5, 1023, 2046, 2047])
+
+
+def test_split_long_ranges_of_one_token_pages():
+    # 270,000 tokens over the CUs: more than 1024 one-token pages per
+    # workgroup, so each range's page table is staged in several chunks
+    p = _build(2, 2, 1, [140000, 130000], 1, seed=13)
+    announce("fp8_kv_decode_attention_ws 270,000 tokens in one-token pages")
+    _check(_gpu(p, "auto"), p, "one-token pages")
