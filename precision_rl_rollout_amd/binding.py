@@ -5,6 +5,9 @@ Every function here has the name of the C entry point it calls (see
 shapes and devices of torch tensors, allocates the outputs with torch on the
 input's device, passes raw pointers and the current HIP stream, and raises
 ``PrrError`` on a non-OK status.  All arithmetic happens in the HIP kernels.
+Calls with an optional workspace (the GEMMs and the decode attention) take
+``workspace="auto"`` (a buffer of the size the library asks for, the
+default), ``None`` (the calls without one) or a uint8 CUDA tensor.
 
 bf16 inputs may be ``torch.bfloat16`` or ``torch.int16`` / ``torch.uint16``
 tensors holding bf16 bit patterns.  FP8 outputs are ``torch.uint8`` codes
