@@ -1,0 +1,41 @@
+"""The rocprofv3 summarizer that turns traces and counter files into the
+tables under profiles/ (CPU; synthetic CSV files in a temporary directory)."""
+
+import csv
+
+from precision_rl_rollout_amd import rocprof_summary as rs
+
+
+def _write(path, header, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_trace_groups_by_kernel_and_launch_shape(tmp_path):
+    hdr = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "LDS_Block_Size", "VGPR_Count",
+           "Workgroup_Size_X", "Grid_Size_X"]
+    rows = [["void prr::gemm_decode_kernel<4, 4, false>(unsigned char const*)", 0, 30000, 73728,
+             96, 512, 131072],
+            ["void prr::gemm_decode_kernel<4, 4, false>(unsigned char const*)", 50000, 84000, 73728,
+             96, 512, 131072],
+            ["prr::fp8_weight_block_kernel(unsigned short const*)", 0, 70000, 512, 40, 256,
+             2121728]]
+    _write(tmp_path / "run_kernel_trace.csv", hdr, rows)
+    out = rs.trace_table(str(tmp_path)).splitlines()
+    assert out[2] == "| `gemm_decode_kernel` | 256 | 73728 | 96 | 2 | 32.00 | 30.00 | 34.00 |"
+    assert out[3] == "| `fp8_weight_block_kernel` | 8288 | 512 | 40 | 1 | 70.00 | 70.00 | 70.00 |"
+
+
+def test_counters_report_the_copy_calibration(tmp_path):
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value", "Grid_Size", "Workgroup_Size",
+           "LDS_Block_Size", "VGPR_Count"]
+    rows = [["__amd_rocclr_copyBuffer", "FETCH_SIZE", 262144.0, 65536, 256, 0, 8],
+            ["prr::kv_cache_write_kernel(x)", "FETCH_SIZE", 100.0, 524288, 256, 0, 24],
+            ["prr::kv_cache_write_kernel(x)", "FETCH_SIZE", 200.0, 524288, 256, 0, 24],
+            ["prr::kv_cache_write_kernel(x)", "WRITE_SIZE", 999.0, 524288, 256, 0, 24]]
+    _write(tmp_path / "run_counter_collection.csv", hdr, rows)
+    out = rs.counter_table(str(tmp_path), "FETCH_SIZE").splitlines()
+    assert out[0] == "calibration copy: 262144.0 KiB -> scale 2.0000"
+    assert out[-1] == "| `kv_cache_write_kernel` | 2048 | 0 | 24 | 2 | 150.0 |"
