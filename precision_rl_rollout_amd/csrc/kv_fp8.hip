@@ -10,15 +10,17 @@
 
 namespace prr {
 
-// The amax is accumulated in the caller's scale word as the bit pattern of
-// a non-negative float (bit order = value order, so an integer maximum is
-// exact and its result does not depend on the order of the updates), then
-// turned into the scale in place.
+// Each workgroup turns its own amax into a scale, fl32(amax_wg / 448), and
+// folds it into the caller's scale word with an integer atomic maximum: the
+// bit order of non-negative floats is their value order, and a correctly
+// rounded division by a positive constant is monotone, so the maximum of the
+// workgroups' scales is fl32(amax / 448) of the whole tensor, whatever the
+// order of the updates.  No kernel runs after the reduction.
 __global__ void kv_amax_clear_kernel(uint32_t* acc) { *acc = 0u; }
 
 // Each thread takes kAmaxLoads 16-byte chunks per pass, all loads issued
 // before any is used (one load in flight per thread held it to ~1.9 TB/s).
-constexpr int kAmaxLoads = 16;
+constexpr int kAmaxLoads = 32;
 
 __global__ __launch_bounds__(256) void kv_amax_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                       uint32_t* __restrict__ acc) {
@@ -51,13 +53,8 @@ __global__ __launch_bounds__(256) void kv_amax_kernel(const uint16_t* __restrict
   __syncthreads();
   if (tid == 0) {
     m = max(max(red[0], red[1]), max(red[2], red[3]));
-    if (m) atomicMax(acc, m << 16);
+    if (m) atomicMax(acc, __float_as_uint(div_rn(__uint_as_float(m << 16), kFp8Max)));
   }
-}
-
-__global__ void kv_scale_finalize_kernel(uint32_t* acc) {
-  const float amax = __uint_as_float(*acc);
-  *reinterpret_cast<float*>(acc) = div_rn(amax, kFp8Max);
 }
 
 hipError_t launch_fp8_kv_scale_recalibrate(const uint16_t* x, int64_t n, float* scale,
@@ -72,7 +69,6 @@ hipError_t launch_fp8_kv_scale_recalibrate(const uint16_t* x, int64_t n, float* 
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kv_amax_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, n, acc);
   }
-  hipLaunchKernelGGL(kv_scale_finalize_kernel, dim3(1), dim3(1), 0, stream, acc);
   return hipGetLastError();
 }
 
