@@ -66,6 +66,21 @@ def test_recalibrate_zero_and_empty():
     assert _f32_bits(host(s)[0]) == 0
 
 
+def test_recalibrate_past_one_pass_of_the_grid():
+    # 66,000 x 1024 values: more 16-byte chunks than one pass of the largest
+    # grid covers, so threads loop; the second check puts the maximum where
+    # only the second pass reads it
+    T, C = 66000, 1024
+    xb = workloads.kv_rows(T, C, 5, "K")
+    announce(f"fp8_kv_scale_recalibrate T{T} C{C} (two passes)")
+    xd = bits_to_dev(xb)
+    assert _f32_bits(host(binding.fp8_kv_scale_recalibrate(xd))[0]) == _f32_bits(kv.kv_scale(xb))
+    pos = T * C - 84_000
+    xb.ravel()[pos] = 0xC4A0                    # -1280.0
+    xd.view(-1)[pos] = int(np.int16(np.uint16(0xC4A0).view(np.int16)))
+    assert _f32_bits(host(binding.fp8_kv_scale_recalibrate(xd))[0]) == _f32_bits(kv.kv_scale(xb))
+
+
 def _write_case(T, C, num_slots, seed, pad_every=0, extra_slots=None, scale=None, xb=None):
     if xb is None:
         xb = workloads.kv_rows(T, C, seed, "V")

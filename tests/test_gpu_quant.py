@@ -101,6 +101,19 @@ def test_fp8_act_quant_shapes(shape):
         _assert_fp8_act(workloads.activation(*shape, seed=seed, outliers=True), f"seed{seed}")
 
 
+# Above 16 x 4 x 256 = 16,384 groups the activation quantizer gives each 16
+# lanes four consecutive groups: K % 8 != 0 (per-element path) and == 0,
+# groups per row not a multiple of four (runs that cross a row end), a
+# ragged last workgroup.
+ACT_LARGE = [(2100, 1001), (2050, 1160), (4099, 512)]
+
+
+@pytest.mark.parametrize("shape", ACT_LARGE)
+def test_fp8_act_quant_large_grids(shape):
+    for seed in (0, 1):
+        _assert_fp8_act(workloads.activation(*shape, seed=seed, outliers=True), f"seed{seed}")
+
+
 @pytest.mark.parametrize("shape", SHAPES + [(64, 20000)])
 def test_int8_quant_shapes(shape):
     for seed in (0, 1):
