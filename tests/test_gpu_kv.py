@@ -2,7 +2,8 @@
 
 * fp8_kv_scale_recalibrate: the scale's bits, on ragged sizes (tails that are
   not whole 16-byte chunks), an all-zero and an empty tensor, values spread
-  so the maximum sits in different workgroups, and the full 32B-layer size;
+  so the maximum sits in different workgroups, more chunks than one pass of
+  the largest grid (threads loop), and the full 32B-layer size;
 * fp8_kv_cache_write: every byte of the cache after the write, which covers
   the codes of written rows and the untouched rows (filled with a canary
   first), with padding and out-of-range slots, ragged C (per-element path),
