@@ -624,8 +624,11 @@ int compute_units() {
 }
 
 // Smallest P (K blocks per wave) that covers the wave's piece.  Resident
-// activations take MT * P * 8 VGPRs; these ranges compile without spills
-// (K up to 8192 for M <= 32, 6144 for M <= 64).
+// activations take MT * P * 8 VGPRs.  Every instance compiles without spills
+// except MT 4, P 6 (M 33-64 with K 5121-6144), which needs 8 (FP8) or 32
+// (INT8) bytes of scratch per lane: correct, somewhat slower; with a
+// workspace those shapes run the split-K kernel only when the layer is
+// narrow.  K up to 8192 for M <= 32, 6144 for M <= 64.
 template <int MT, bool kInt8>
 static bool launch_decode_mt(const uint8_t* A, const float* sa, const uint8_t* W,
                              const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* C,
@@ -764,6 +767,8 @@ bool launch_gemm_decode(const uint8_t* A, const float* sa, const uint8_t* W, con
   }
 }
 
+// As launch_decode_mt; the MT 4 instances with P 5 and 6 (more than 32 rows
+// for some expert, K 4097-6144) spill 28 and 184 bytes per lane.
 template <int MT>
 static bool launch_grouped_mt(const uint8_t* A, const float* sa, const uint8_t* W,
                               const float* sw, const int64_t* offsets, int64_t E, int64_t M,
