@@ -2,21 +2,23 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is one pass of the whole path over one batch of the workload:
-FP8 block re-quantization of the weight, FP8 per-token-group quantization
-of the activations, the W8A8 block-scaled GEMM, and the INT8 per-channel
-variant of all three.  The default workload is the 7B-class decode FFN
-up/gate layer (A [64, 3584], Wt [37888, 3584]).  Inputs are synthetic
-(seeded, see precision_rl_rollout_amd.workloads), resident in HBM before
-the timed region; two input sets alternate so that no step finds its bf16
-weight in the 256 MB last-level cache.
+The default workload is the 7B-class decode FFN up/gate layer (A [64,
+3584], Wt [37888, 3584]).  One step is one decode pass of it: FP8
+per-token-group quantization of the activations and the W8A8 block-scaled
+GEMM against the FP8 weight (quantized before; five copies alternate so
+that no step finds the weight in the 256 MB last-level cache).  Inputs are
+synthetic (seeded, see precision_rl_rollout_amd.workloads) and resident in
+HBM before the timed region.
 
-Prints one JSON line.  ``value`` is algorithmic bytes of the step / step
-time (GB/s); ``roofline`` gives the dominant kernel's algorithmic GB/s
-(from HIP events on the launch stream, around that kernel's calls in the
-timed steps) against the 8 TB/s HBM peak; ``kernels`` gives every kernel's
-duration from a short instrumented pass before the timed steps;
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same step.
+Prints one JSON line.  ``value`` and ``roofline`` are the GEMM's own
+algorithmic GB/s (HIP events on the launch stream around its calls in the
+timed steps) against the 8 TB/s HBM peak; ``prefill`` carries the other
+half of the metric, the FP8 GEMM of the 32B-class prefill up/gate layer
+(M 8192, N 27648, K 5120) in TFLOP/s against the 5.0 PFLOP/s FP8 peak;
+``requant_step`` is the whole per-step path at the decode shape (FP8 and
+INT8 weight re-quantization, activation quantization and GEMM) with every
+kernel's duration; ``cpu_baseline`` (and ``prefill.cpu_baseline``) time
+the CPU oracle on the same GEMM (a row sample of the prefill one).
 
 Other workloads (``--workload``): ``decode32b_sweep`` (GEMMs at M = 1..128,
 N 27648, K 5120, cold weights), ``prefill32b`` (M 8192 up/gate and down
@@ -182,15 +184,92 @@ def cpu_threads():
 
 # ---------------------------------------------------------------- workloads
 def run_decode7b(args, torch, B, W):
+    """The default line.
+
+    value / roofline: the FP8 W8A8 block GEMM of the 7B-class decode FFN
+    up/gate layer (A [64, 3584], Wt [37888, 3584]), the decode-shape half of
+    the metric, as algorithmic GB/s of the GEMM itself.  One step is one
+    decode pass of the layer: FP8 token-group quantization of the activation
+    batch, then the GEMM against the layer's FP8 weight.  The weight was
+    quantized before (a rollout quantizes it once per training step and
+    decodes with it many times), and five copies of it alternate so that no
+    step finds it in the 256 MB last-level cache.  HIP events on the launch
+    stream around the GEMM calls of the timed steps give its duration.
+
+    prefill: the other half of the metric, the FP8 GEMM of the 32B-class
+    prefill up/gate layer (M 8192, N 27648, K 5120) in TFLOP/s against the
+    FP8 peak, with its own CPU baseline; the down projection beside it.
+
+    requant_step: the whole per-step path at this shape (FP8 block
+    re-quantization of the bf16 weight, activation quantization, GEMM, and
+    the INT8 per-channel variant of all three), as before.
+    """
     M, N, K = 64, 37888, 3584
-    sets = []
+    dev = torch.device("cuda:0")
+    inputs = []
     for seed in (0, 1):
         p = W.gemm_problem(M, N, K, True, seed=seed)
-        sets.append(dict(A=torch.from_numpy(p["A"].view(np.int16)).cuda(),
-                         Wt=torch.from_numpy(p["Wt"].view(np.int16)).cuda()))
+        inputs.append(dict(A=torch.from_numpy(p["A"].view(np.int16)).cuda(),
+                           Wt=torch.from_numpy(p["Wt"].view(np.int16)).cuda()))
+    w8 = B.fp8_weight_block_quant(inputs[0]["Wt"])
+    copies = _cold_copies(torch, lambda i: (w8[0].clone(), w8[1].clone()), N * K)
+    aq8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa8 = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    c8 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    gbytes = gemm_bytes(M, N, K, M * (K // 128), cdiv(N, 128) * (K // 128))
+    abytes = quant_bytes(M, K, M * (K // 128))
+
+    def step(i, timer=None):
+        t = timer.run if timer else (lambda _n, f: f())
+        wq, sw = copies[i % len(copies)]
+        a = inputs[i % 2]["A"]
+        t("fp8_act_token_quant", lambda: B.fp8_act_token_quant(a, out=aq8, scale=sa8))
+        t("w8a8_block_gemm", lambda: B.w8a8_block_gemm(aq8, sa8, wq, sw, out=c8))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer = Timer(torch, only="w8a8_block_gemm")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, timer)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    g_us = timer.avg_us()["w8a8_block_gemm"]
+    achieved = gbytes / g_us / 1e3
+    roofline = {"bound": "hbm", "kernel": "w8a8_block_gemm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("w8a8_block_gemm", "decode7b_upgate")}
+    req = requant_step_decode7b(args, torch, B, W, inputs)
+    line = {
+        "metric": METRIC, "value": round(achieved, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
+        "config": {"workload": "decode7b_upgate", "M": M, "N": N, "K": K,
+                   "value_is": "fp8 W8A8 block GEMM algorithmic GB/s (HIP events), cold weights",
+                   "step": "fp8 A group quant + fp8 W8A8 block GEMM (weight quantized before)",
+                   "gemm_algorithmic_bytes": gbytes,
+                   "step_algorithmic_bytes": gbytes + abytes},
+        "roofline": roofline,
+    }
+    line["prefill"] = prefill_upgate_line(args, torch, B, W)
+    line["requant_step"] = req
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode_gemm(W, gbytes)
+        line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(W)
+    return line
+
+
+def requant_step_decode7b(args, torch, B, W, inputs):
+    """The six calls of one full per-step pass at the 7B decode shape (FP8
+    and INT8 weight re-quantization, activation quantization and GEMM), the
+    two input sets alternating; per-kernel durations from an instrumented
+    pass (event pair around every call)."""
+    M, N, K = 64, 37888, 3584
     dev = torch.device("cuda:0")
     outs = []
-    for _ in sets:
+    for _ in inputs:
         outs.append(dict(
             wq8=torch.empty((N, K), dtype=torch.uint8, device=dev),
             sw8=torch.empty((cdiv(N, 128), K // 128), dtype=torch.float32, device=dev),
@@ -202,7 +281,6 @@ def run_decode7b(args, torch, B, W):
             aqi=torch.empty((M, K), dtype=torch.int8, device=dev),
             sai=torch.empty((M,), dtype=torch.float32, device=dev),
             ci=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
-
     work = {
         "fp8_weight_block_quant": quant_bytes(N, K, cdiv(N, 128) * (K // 128)),
         "fp8_act_token_quant": quant_bytes(M, K, M * (K // 128)),
@@ -214,7 +292,7 @@ def run_decode7b(args, torch, B, W):
     step_bytes = sum(work.values())
 
     def step(i, timer=None):
-        s, o = sets[i % 2], outs[i % 2]
+        s, o = inputs[i % 2], outs[i % 2]
         t = timer.run if timer else (lambda _n, f: f())
         t("fp8_weight_block_quant", lambda: B.fp8_weight_block_quant(s["Wt"], out=o["wq8"], scale=o["sw8"]))
         t("fp8_act_token_quant", lambda: B.fp8_act_token_quant(s["A"], out=o["aq8"], scale=o["sa8"]))
@@ -223,54 +301,97 @@ def run_decode7b(args, torch, B, W):
         t("int8_act_token_quant", lambda: B.int8_act_token_quant(s["A"], out=o["aqi"], scale=o["sai"]))
         t("w8a8_int8_channel_gemm", lambda: B.w8a8_int8_channel_gemm(o["aqi"], o["sai"], o["wqi"], o["swi"], out=o["ci"]))
 
-    dt, us, dom = timed_steps(torch, step, args)
+    sub = argparse.Namespace(steps=min(args.steps, 20), warmup=max(1, min(args.warmup, 3)))
+    dt, us, dom = timed_steps(torch, step, sub)
     kernels = {k: {"us": round(us[k], 2), "algorithmic_bytes": work[k],
                    "GB/s": round(work[k] / us[k] / 1e3, 1)} for k in work}
-    achieved = work[dom] / us[dom] / 1e3
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom, "decode7b_upgate")}
-    line = {
-        "metric": METRIC, "value": round(step_bytes / dt / 1e9, 1), "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8e4m3+int8", "data": "synthetic",
-        "config": {"workload": "decode7b_upgate", "M": M, "N": N, "K": K,
-                   "step": "fp8 W block quant + fp8 A group quant + fp8 W8A8 GEMM + int8 W "
-                           "channel quant + int8 A token quant + int8 W8A8 GEMM",
-                   "step_algorithmic_bytes": step_bytes},
-        "roofline": roofline, "kernels": kernels,
-    }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_decode7b(W, step_bytes)
-    return line
+    return {"steps": sub.steps, "ms_per_step": round(dt * 1e3, 4),
+            "GB/s": round(step_bytes / dt / 1e9, 1), "step_algorithmic_bytes": step_bytes,
+            "step": "fp8 W block quant + fp8 A group quant + fp8 W8A8 GEMM + int8 W channel "
+                    "quant + int8 A token quant + int8 W8A8 GEMM (the GEMMs read the codes the "
+                    "same step wrote)",
+            "dominant": dom, "kernels": kernels}
 
 
-def cpu_baseline_decode7b(W, step_bytes):
-    """The oracle, as it stands, on one whole step of the same workload (all
-    six operations on the full A and Wt, about 10-20 s on 8-16 host cores),
-    in the step's unit (algorithmic GB/s)."""
+def prefill_upgate_line(args, torch, B, W):
+    """FP8 W8A8 block GEMM of the 32B-class prefill up/gate layer (M 8192,
+    N 27648, K 5120) in TFLOP/s by HIP events over `steps` launches (at
+    least 10), against the 5.0 PFLOP/s dense FP8 peak; the down projection
+    (N 5120, K 27648) beside it."""
+    out = {}
+    for which, (N, K) in (("upgate", (27648, 5120)), ("down", (5120, 27648))):
+        p = W.gemm_problem(8192, N, K, True, seed=0, down=which == "down")
+        a = torch.from_numpy(p["A"].view(np.int16)).cuda()
+        w = torch.from_numpy(p["Wt"].view(np.int16)).cuda()
+        aq, sa = B.fp8_act_token_quant(a)
+        wq, sw = B.fp8_weight_block_quant(w)
+        del a, w
+        c = torch.empty((8192, N), dtype=torch.bfloat16, device="cuda:0")
+        for _ in range(max(2, args.warmup)):
+            B.w8a8_block_gemm(aq, sa, wq, sw, out=c)
+        timer = Timer(torch)
+        for _ in range(max(10, args.steps // 4)):
+            timer.run("gemm", lambda: B.w8a8_block_gemm(aq, sa, wq, sw, out=c))
+        torch.cuda.synchronize()
+        us = timer.avg_us()["gemm"]
+        tf = 2 * 8192 * N * K / us / 1e6
+        out[which] = {"M": 8192, "N": N, "K": K, "us": round(us, 2), "TFLOP/s": round(tf, 1),
+                      "frac": round(tf / FP8_PEAK_TFLOPS, 4), "launches": len(timer.pairs["gemm"])}
+        del aq, sa, wq, sw, c
+    up = out["upgate"]
+    return {"workload": "prefill32b up/gate: A [8192, 5120] x Wt [27648, 5120], FP8 blocks",
+            "value": up["TFLOP/s"], "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "kernel": "w8a8_block_gemm",
+                         "achieved": up["TFLOP/s"], "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": up["frac"],
+                         "traffic": measured_traffic("w8a8_block_gemm", "prefill32b")},
+            "gemms": out}
+
+
+def cpu_cores():
+    return {"blas_threads": cpu_threads(), "os_cpu_count": os.cpu_count()}
+
+
+def cpu_baseline_decode_gemm(W, gbytes):
+    """The oracle, as it stands, on the same GEMM: the FP8 GEMM of the full
+    A [64, 3584] against the full FP8 weight [37888, 3584] (fp64 BLAS over the
+    decoded codes), in the line's unit; the operands are quantized by the
+    oracle first, outside the timed part."""
     from oracle import gemm, quant
     M, N, K = 64, 37888, 3584
-    rows = N
     p = W.gemm_problem(M, N, K, True, seed=0)
-    A, Wt = p["A"], p["Wt"][:rows]
+    wq, sw = quant.fp8_weight_block_quant(p["Wt"])
+    aq, sa = quant.fp8_act_token_quant(p["A"])
     t0 = time.perf_counter()
-    wq, sw = quant.fp8_weight_block_quant(Wt)
-    aq, sa = quant.fp8_act_token_quant(A)
     gemm.round_bf16(gemm.w8a8_block_gemm(aq, sa, wq, sw))
-    wqi, swi = quant.int8_weight_channel_quant(Wt)
-    aqi, sai = quant.int8_act_token_quant(A)
-    gemm.round_bf16(gemm.int8_channel_gemm(aqi, sai, wqi, swi))
     dt = time.perf_counter() - t0
-    sample_bytes = (quant_bytes(rows, K, (rows // 128) * (K // 128)) + quant_bytes(M, K, M * (K // 128))
-                    + gemm_bytes(M, rows, K, M * (K // 128), (rows // 128) * (K // 128))
-                    + quant_bytes(rows, K, rows) + quant_bytes(M, K, M)
-                    + gemm_bytes(M, rows, K, M, rows))
-    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+    cores = cpu_cores()
+    return {"value": round(gbytes / dt / 1e9, 4), "unit": "GB/s",
+            "cores": cores["blas_threads"], "os_cpu_count": cores["os_cpu_count"],
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"one whole step: all six operations on A [64, 3584] and Wt [{rows}, 3584]; "
-                      f"numpy elementwise (1 thread) + fp64 BLAS ({cpu_threads()} threads)"}
+            "sample": "the whole GEMM: A [64, 3584] x Wt [37888, 3584] FP8 codes and scales, "
+                      "rounded to bf16; fp64 BLAS with the host's BLAS threads"}
+
+
+def cpu_baseline_prefill(W, rows=512):
+    """The oracle on a row sample of the prefill up/gate GEMM: `rows` token
+    rows of A [8192, 5120] against the full FP8 weight [27648, 5120], in
+    TFLOP/s of that sample (operands quantized by the oracle first, outside
+    the timed part)."""
+    from oracle import gemm, quant
+    N, K = 27648, 5120
+    p = W.gemm_problem(8192, N, K, True, seed=0)
+    wq, sw = quant.fp8_weight_block_quant(p["Wt"])
+    aq, sa = quant.fp8_act_token_quant(p["A"][:rows])
+    t0 = time.perf_counter()
+    gemm.round_bf16(gemm.w8a8_block_gemm(aq, sa, wq, sw))
+    dt = time.perf_counter() - t0
+    cores = cpu_cores()
+    return {"value": round(2 * rows * N * K / dt / 1e12, 5), "unit": "TFLOP/s",
+            "cores": cores["blas_threads"], "os_cpu_count": cores["os_cpu_count"],
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"the first {rows} of 8192 token rows against the full weight "
+                      f"[27648, 5120]; fp64 BLAS with the host's BLAS threads"}
 
 
 def _cold_copies(torch, make, nbytes, budget=600 << 20):
@@ -356,7 +477,7 @@ def run_prefill32b(args, torch, B, W):
                                       "peak_frac": round(tf / FP8_PEAK_TFLOPS, 4)}
         del a, w, c
     up = res["w8a8_block_gemm/upgate"]
-    return {"metric": METRIC, "value": up["TFLOP/s"], "unit": "TFLOP/s", "n_gpus": 1,
+    line = {"metric": METRIC, "value": up["TFLOP/s"], "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
             "vs_baseline": None, "dtype": "fp8e4m3+int8", "data": "synthetic",
             "config": {"workload": "prefill32b", "M": 8192,
@@ -365,6 +486,9 @@ def run_prefill32b(args, torch, B, W):
                          "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": up["peak_frac"],
                          "traffic": measured_traffic("w8a8_block_gemm", "prefill32b")},
             "kernels": res}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(W)
+    return line
 
 
 def run_stack32b(args, torch, B, W):
@@ -497,7 +621,7 @@ def run_kv32b(args, torch, B, W):
             okv.kv_cache_write(np.zeros((S, C), np.uint8), xb, slots_np, okv.kv_scale(xb))
         ct = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(step_bytes / ct / 1e9, 3), "unit": "GB/s",
-                                "cores": cpu_threads(), "kind": "oracle",
+                                "cores": cpu_threads(), "os_cpu_count": os.cpu_count(), "kind": "oracle",
                                 "sample": "one whole step (K and V: recalibration and cache write)"}
     return line
 
@@ -581,7 +705,7 @@ def run_moe_decode(args, torch, B, W):
         sample = (quant_bytes(ns * N, K, ns * NB * KB) + quant_bytes(r1, K, r1 * KB)
                   + grouped_bytes(sub, N, K))
         line["cpu_baseline"] = {"value": round(sample / ct / 1e9, 4), "unit": "GB/s",
-                                "cores": cpu_threads(), "kind": "oracle", "seconds": round(ct, 2),
+                                "cores": cpu_threads(), "os_cpu_count": os.cpu_count(), "kind": "oracle", "seconds": round(ct, 2),
                                 "sample": f"one whole step: weight quant of all {ns} experts, "
                                           f"quant of the {r1} routed rows, the grouped GEMM"}
     return line
@@ -676,7 +800,7 @@ def run_att(args, torch, B, W):
         ct = time.perf_counter() - t0
         sample = 2 * int(lens[rows].sum()) * Hkv * D + 4 * len(rows) * Hq * D
         line["cpu_baseline"] = {"value": round(sample / ct / 1e9, 4), "unit": "GB/s",
-                                "cores": cpu_threads(), "kind": "oracle", "seconds": round(ct, 2),
+                                "cores": cpu_threads(), "os_cpu_count": os.cpu_count(), "kind": "oracle", "seconds": round(ct, 2),
                                 "sample": f"sequences {rows[0]}, {rows[1]}, ... {rows[-1]} "
                                           f"({len(rows)} of {Bn}) of the same batch"}
     return line
@@ -727,7 +851,7 @@ def run_tis(args, torch, B, W):
             otis.importance_weights(p["lp_train"], p["lp_rollout"], p["mask"], cap, m)
         ct = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(2 * per_call / ct / 1e9, 4), "unit": "GB/s",
-                                "cores": cpu_threads(), "kind": "oracle", "seconds": round(ct, 2),
+                                "cores": cpu_threads(), "os_cpu_count": os.cpu_count(), "kind": "oracle", "seconds": round(ct, 2),
                                 "sample": "one whole step (TIS and MIS over the full batch)"}
     return line
 
@@ -814,7 +938,7 @@ def run_sync32b(args, torch, B, W):
         oq.fp8_weight_block_quant(chunk)
         ct = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(2 * rows * K / ct / 1e9, 4), "unit": "GB/s",
-                                "cores": cpu_threads(), "kind": "oracle", "seconds": round(ct, 2),
+                                "cores": cpu_threads(), "os_cpu_count": os.cpu_count(), "kind": "oracle", "seconds": round(ct, 2),
                                 "sample": f"one chunk ({rows} x {K}) quantized by the oracle"}
     return line
 

@@ -65,8 +65,10 @@
  * Errors (returned synchronously, after argument checks and the launch):
  *   - PRR_ERR_INVALID_ARG: a negative dimension, a dimension above
  *     2^31 - 1, or a NULL pointer for a non-empty operand;
- *   - PRR_ERR_UNSUPPORTED_SHAPE: a GEMM with K % 128 != 0, or an INT8 GEMM
- *     with K > 133143 (127^2 K could overflow its int32 accumulator);
+ *   - PRR_ERR_UNSUPPORTED_SHAPE: a GEMM with K % 128 != 0 or K > 8388480
+ *     (65535 blocks: the many-token kernel's 32-bit tile offsets), or an
+ *     INT8 GEMM with K > 133143 (127^2 K could overflow its int32
+ *     accumulator);
  *   - PRR_ERR_MISALIGNED: a pointer that is not 16-byte aligned;
  *   - PRR_ERR_NO_DEVICE: no HIP device is visible;
  *   - PRR_ERR_UNSUPPORTED_DEVICE: the current device is not gfx950;
@@ -157,7 +159,8 @@ prr_status fp8_act_token_quant(const uint16_t* a_bf16, int64_t M, int64_t K,
  *   a_fp8 [M, K], a_scale [M, K/128]   as written by fp8_act_token_quant.
  *   w_fp8 [N, K], w_scale [ceil(N/128), K/128] as written by
  *                                      fp8_weight_block_quant.
- *   M, N >= 0; K >= 0 with K % 128 == 0 (K == 0 writes +0.0).
+ *   M, N >= 0; K >= 0 with K % 128 == 0 and K <= 8388480 (K == 0 writes
+ *   +0.0).
  *   c_bf16 out [M, N] bf16 bits, row-major.
  */
 prr_status w8a8_block_gemm(const uint8_t* a_fp8, const float* a_scale,

@@ -13,8 +13,10 @@ granularity, format or write rule; the readings taken here:
   block;
 * quantize-on-write: a token row ``x`` (``C = kv_heads * head_dim`` bf16
   values) lands in cache row ``slot`` as ``E4M3_sat_RNE(fl32(x / s))``;
-  values above the calibration range saturate to +-448; ``s == 0`` writes
-  the signed zeros of ``x`` (the all-zero-block rule);
+  values above the calibration range saturate to +-448, including values
+  whose quotient ``x / s`` overflows binary32 (a stale scale far below the
+  new values); ``s == 0`` writes the signed zeros of ``x`` (the
+  all-zero-block rule);
 * a slot outside ``[0, num_slots)`` (negative: a padding token) is skipped;
   distinct tokens map to distinct slots, and cache rows no token maps to are
   left as they were.
@@ -45,7 +47,13 @@ def kv_encode_rows(x_bits, s: np.float32) -> np.ndarray:
     _check_finite(x)
     if np.float32(s) == 0:
         return np.where(np.signbit(x), np.uint8(0x80), np.uint8(0x00)).astype(np.uint8)
-    return e4m3.encode(_quotient(x, np.float32(s)))
+    with np.errstate(over="ignore"):
+        v = _quotient(x, np.float32(s))
+    # A scale from an earlier batch can be so small that fl32(x / s) leaves
+    # the binary32 range: such a quotient is a value above the calibrated
+    # range like any other and saturates to +-448 (the sign is that of x).
+    v = np.where(np.isinf(v), np.copysign(np.float32(448.0), v), v).astype(np.float32)
+    return e4m3.encode(v)
 
 
 def kv_cache_write(cache: np.ndarray, x_bits, slot_mapping, s: np.float32) -> np.ndarray:

@@ -2,7 +2,8 @@
 
 ``python -m precision_rl_rollout_amd.build`` compiles every source under
 ``csrc/`` into ``precision_rl_rollout_amd/libprr.so``.  No GPU is needed:
-hipcc cross-compiles for gfx950.
+hipcc cross-compiles for gfx950.  Sources compile in parallel to objects
+under ``_build/`` (git-ignored), which are then linked.
 """
 
 from __future__ import annotations
@@ -11,21 +12,23 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libprr.so")
+OBJ_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "quant_fp8.hip", "quant_int8.hip", "gemm.hip", "gemm_decode.hip", "gemm_prefill.hip", "kv_fp8.hip",
-           "tis.hip", "attention.hip"]
+SOURCES = ["api.cpp", "quant_fp8.hip", "quant_int8.hip", "gemm.hip", "gemm_decode.hip",
+           "gemm_prefill.hip", "kv_fp8.hip", "tis.hip", "attention.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 # No fast-math or denormal-flush flags: the quantizers rely on IEEE fp32
 # division with subnormals kept.
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
@@ -38,19 +41,37 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def _filter(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines()
+                     if "packed-fp32-ops' is not a recognized feature" not in l)
+
+
+def _compile(src: str) -> tuple[str, int, str]:
+    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    return obj, res.returncode, _filter(res.stderr)
+
+
 def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    jobs = max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_compile, srcs))
+    for (obj, rc, err), src in zip(results, srcs):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {os.path.basename(src)} ({rc}):\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *[r[0] for r in results],
+           "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in res.stderr.splitlines()
-                    if "packed-fp32-ops' is not a recognized feature" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{_filter(res.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 

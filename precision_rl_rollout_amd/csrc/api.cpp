@@ -14,6 +14,10 @@ namespace {
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;        // 2^31 - 1
 constexpr int64_t kMaxInt8GemmK = 133143;      // 127^2 * K < 2^31
+// Longest K of the dense GEMMs: the many-token kernel addresses one 256-row
+// operand tile with 32-bit buffer offsets (256 K below 2^31 - 256), and it
+// takes every shape the decode kernels decline.
+constexpr int64_t kMaxGemmK = 8388480;         // 65535 * 128
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -147,7 +151,7 @@ prr_status int8_act_token_quant(const uint16_t* a_bf16, int64_t M, int64_t K, in
 static prr_status gemm_common(const void* a, const void* sa, const void* w, const void* sw,
                               int64_t M, int64_t N, int64_t K, const void* c, bool int8) {
   PRR_TRY(check_dims(M, N, K));
-  if (K % 128 != 0) return PRR_ERR_UNSUPPORTED_SHAPE;
+  if (K % 128 != 0 || K > kMaxGemmK) return PRR_ERR_UNSUPPORTED_SHAPE;
   if (int8 && K > kMaxInt8GemmK) return PRR_ERR_UNSUPPORTED_SHAPE;
   if (M == 0 || N == 0) return PRR_OK;
   if (K == 0) {

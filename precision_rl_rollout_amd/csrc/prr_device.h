@@ -71,13 +71,20 @@ __device__ __forceinline__ float div_rn(float x, float s) { return x / s; }
 // remainder never underflows where it matters.  The fma loses the sign of
 // a zero quotient, which the copysign restores (x / s has the sign of x).
 //
-// Used only where its result is encoded to e4m3 or int8.  The encoded
-// results equal those of encode(x / s) for every pair of bf16 values with
-// |x| <= amax and s = fl32(amax / 448) or fl32(amax / 127): this was
-// checked exhaustively on gfx950 (all 32,639 positive finite amax, every
-// bf16 x of either sign up to it, ~2.1e9 pairs per divisor).  The fp32
-// quotients themselves may differ from x / s in the last bit only below
-// 2e-15, where both encode to zero.
+// Used only where its result is encoded to e4m3 or int8, and only with
+// |x| <= 448 s (block scales; the KV-cache path clamps, below).  The GPU
+// parity tests compare the encoded results with the oracle's
+// encode(fl32(x / s)) byte for byte, through the library's quantizers, for
+// every finite bf16 x with |x| <= amax (both signs) and s = fl32(amax / 448)
+// or fl32(amax / 127), over 1,031 amax values spanning every bf16 binade:
+// the power of two, 448 * 2^k (exact quotients, e4m3 ties), the largest
+// and a random mantissa of each, and 16 subnormal amax values, so both the
+// ordinary and the 2^96 path.  (By Markstein's theorem the step returns
+// the correctly rounded quotient whenever its remainder e is exact; e can
+// be inexact only for |x| below about 2^-100, near the fp32 subnormal
+// range, and with s >= 2^-64 -- the 2^96 prescaling sees to it -- those
+// quotients lie below 2^-36, far under the smallest nonzero e4m3 value
+// 2^-9 or the int8 rounding point 1/2, and encode to zero either way.)
 struct BlockDiv {
   float s;   // s, or s * 2^96
   float r;   // RN(1 / s) of the above
@@ -105,22 +112,28 @@ __device__ __forceinline__ float div_block(float x, const BlockDiv& d) {
 // subnormals).  It does not saturate: magnitudes in (464, 480] would give
 // NaN.  Quotients of a block never exceed 448 * (1 + 2^-8) < 464 (the
 // scale is amax / 448 rounded to fp32, relative error below 2^-8 even for
-// subnormal scales), so no clamp is needed.  On every fp32 value with
-// |v| <= 464 the conversion equals the saturating RNE e4m3 code built from
-// the fp32 fields with integer arithmetic (checked exhaustively on gfx950
-// over all such fp32 patterns, both signs, zeros and subnormals included).
+// subnormal scales), so no clamp is needed.  What the GPU parity tests
+// check of it against the oracle's bit-built saturating RNE encoder: every
+// quotient the sweep above produces, and every finite bf16 value itself
+// (a KV-cache write with s = 1, whose quotients are exact).
 __device__ __forceinline__ uint32_t cvt_e4m3x4(float q0, float q1, float q2, float q3) {
   int d = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
   d = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, d, true);
   return (uint32_t)d;
 }
 
-// Quotient clamped to [-448, 448] (sign of zero kept): the saturating RNE
-// code is unchanged, and the conversion then never sees |v| > 464.  Needed
-// where a scale does not bound the quotients (a KV-cache scale calibrated
-// on an earlier batch); block scales do bound them.
+// Quotient saturated to +-448 (sign of zero kept): the saturating RNE code
+// is unchanged, and the conversion then never sees |v| > 464.  Needed where
+// a scale does not bound the quotients (a KV-cache scale calibrated on an
+// earlier batch); block scales do bound them.  With such a scale x / s can
+// exceed the binary32 range, and the correction step above then yields an
+// infinity or a NaN (x r overflows, e = fma(-inf, s, x) = -inf, and
+// fma(-inf, r, inf) is NaN); div_block gives it the sign of x, and every
+// value that is not within [-448, 448] -- NaN included, as the comparison
+// fails -- becomes 448 with its sign: the saturating code of a quotient
+// beyond the range.
 __device__ __forceinline__ float clamp448(float v) {
-  return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+  return __builtin_fabsf(v) <= 448.0f ? v : __builtin_copysignf(448.0f, v);
 }
 
 // Eight bf16 values (one 16-byte chunk) -> eight e4m3 codes (8 bytes).

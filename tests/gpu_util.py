@@ -2,7 +2,9 @@
 
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -57,3 +59,22 @@ class Guarded:
     def intact(self) -> bool:
         b = self.buf.cpu().numpy()
         return bool(np.all(b[:GUARD] == CANARY) and np.all(b[GUARD + self.nbytes:] == CANARY))
+
+
+def oracle_workers() -> int:
+    """Threads for running the oracle over bands of a large input (numpy
+    releases the interpreter lock inside its array operations)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_by_rows(fn, bits: np.ndarray, band: int):
+    """fn applied to consecutive bands of `band` rows of `bits`, in parallel
+    threads, with the bands' outputs concatenated along the rows.  fn returns
+    (codes, scales); every row-wise quantizer, and the block quantizer with
+    `band` a multiple of 128, is a function of its band alone (the oracle's
+    shard-commutation pin), so the result is fn(bits)."""
+    starts = list(range(0, bits.shape[0], band))
+    with ThreadPoolExecutor(oracle_workers()) as ex:
+        parts = list(ex.map(lambda r: fn(bits[r:r + band]), starts))
+    return (np.concatenate([p[0] for p in parts], axis=0),
+            np.concatenate([p[1] for p in parts], axis=0))

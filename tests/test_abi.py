@@ -123,6 +123,19 @@ def test_int8_gemm_rejects_k_that_could_overflow_int32():
         assert binding.call("w8a8_block_gemm", *P, 1, 16, K, FAKE, None) == NO_DEVICE
 
 
+@pytest.mark.parametrize("fn", GEMMS + ["w8a8_block_gemm_ws", "w8a8_int8_channel_gemm_ws"])
+def test_gemm_rejects_k_beyond_the_tile_offsets(fn):
+    """K above 65535 blocks is refused before any device work, for every
+    dense GEMM call (the last accepted K, 8388480, reaches the device check
+    in a process without a GPU)."""
+    P = [FAKE] * 4
+    ws = (None, 0) if fn.endswith("_ws") else ()
+    assert binding.call(fn, *P, 65, 16, 8388608, FAKE, *ws, None) == SHAPE
+    assert binding.call(fn, *P, 1, 16, 8388480 + 128, FAKE, *ws, None) == SHAPE
+    if not _gpu_visible() and not fn.startswith("w8a8_int8"):
+        assert binding.call(fn, *P, 65, 16, 8388480, FAKE, *ws, None) == NO_DEVICE
+
+
 @pytest.mark.skipif(_gpu_visible(), reason="needs a process without a GPU")
 @pytest.mark.parametrize("fn", QUANTS + GEMMS)
 def test_no_device_is_reported(fn):

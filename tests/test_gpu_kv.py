@@ -125,6 +125,20 @@ def test_cache_write_saturates_and_zero_scale():
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("scale", [2.0 ** -120 / 448, 2.0 ** -70, 2.0 ** -140, 1e-30, 2.0 ** -60])
+def test_cache_write_stale_tiny_scale_saturates(scale):
+    """A stale scale so small that x / s leaves the binary32 range (both the
+    ordinary and the 2^96-prescaled division path): every such value
+    saturates to +-448, the rest encode as usual."""
+    announce(f"fp8_kv_cache_write stale tiny scale {scale:.3e}")
+    xb = workloads.kv_rows(64, 128, 12, "K")
+    xb[0, :8] = [0x3F80, 0xBF80, 0x0000, 0x8000, 0x0001, 0x8001, 0x7F7F, 0xFF7F]
+    got, want = _write_case(64, 128, 256, seed=12, scale=np.float32(scale), xb=xb)
+    assert np.array_equal(got, want)
+    row0 = got[workloads.kv_slot_mapping(64, 256, 16, 12, 0)[0]]
+    assert list(row0[[0, 1, 2, 3, 6, 7]]) == [0x7E, 0xFE, 0x00, 0x80, 0x7E, 0xFE]
+
+
 def test_full_32b_prefill_write():
     cfg = workloads.KV_32B
     T, C, S = cfg["T"], cfg["C"], cfg["num_slots"]

@@ -5,8 +5,8 @@ Cases: the 16 x 256 / 256 x 256 layer, ragged shapes (partial blocks,
 K % 8 != 0, single rows), special blocks (all-zero, signed zeros,
 saturating, bf16-max and bf16-subnormal amax, exact e4m3 blocks), every
 finite bf16 pattern under a spread of block scales, and the full-size
-weights and activations of the 7B / 32B-class layers (oracle on sampled
-blocks or rows, invariants on all of them).  Output buffers carry canary
+weights and activations of the 7B / 32B-class layers (every byte and
+scale of the whole arrays).  Output buffers carry canary
 margins; repeated calls must give identical bits.
 """
 
@@ -16,7 +16,7 @@ import torch
 
 from oracle import e4m3, quant
 from precision_rl_rollout_amd import binding, workloads
-from tests.gpu_util import Guarded, announce, bits_to_dev, host
+from tests.gpu_util import Guarded, announce, bits_to_dev, host, oracle_by_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -114,7 +114,7 @@ def test_fp8_act_quant_large_grids(shape):
         _assert_fp8_act(workloads.activation(*shape, seed=seed, outliers=True), f"seed{seed}")
 
 
-@pytest.mark.parametrize("shape", SHAPES + [(64, 20000)])
+@pytest.mark.parametrize("shape", SHAPES + [(64, 20000), (4, 40960), (3, 40963)])
 def test_int8_quant_shapes(shape):
     for seed in (0, 1):
         _assert_int8(workloads.weight(*shape, seed=seed), f"seed{seed}")
@@ -233,56 +233,60 @@ def test_empty_inputs():
 
 
 # ----------------------------------------------------------------- full size
-def _sampled_blocks(nb, kb, count, seed):
-    rng = np.random.default_rng(seed)
-    ids = {(0, 0), (nb - 1, kb - 1), (0, kb - 1), (nb - 1, 0)}
-    while len(ids) < count:
-        ids.add((int(rng.integers(nb)), int(rng.integers(kb))))
-    return sorted(ids)
+# Whole arrays, every code byte and every scale bit, against the oracle run
+# over row bands in parallel threads (the oracle's shard-commutation pin
+# makes a band's result that part of the whole result).
+
+def _assert_same(codes, scales, rc, rs, label):
+    bad = int(np.count_nonzero(codes != rc))
+    assert bad == 0, f"{label}: {bad} code bytes differ, first at {np.argwhere(codes != rc)[0]}"
+    assert _same_f32_bits(scales, rs), f"{label}: scale bits differ"
 
 
-def _full_weight_check(w, label, count=96):
+def _full_fp8_weight(w, label):
     announce(f"fp8_weight_block_quant full-size {label} {w.shape}")
     codes, scales = _fp8_w_gpu(w)
+    rc, rs = oracle_by_rows(quant.fp8_weight_block_quant, w, 1024)
+    _assert_same(codes, scales, rc, rs, f"fp8 {label}")
     nb, kb = scales.shape
-    for (i, j), (rc, rs) in zip(_sampled_blocks(nb, kb, count, 1),
-                                quant.fp8_weight_blocks(w, _sampled_blocks(nb, kb, count, 1))):
-        blk = codes[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
-        assert _same_f32_bits(scales[i, j], rs), (label, i, j)
-        assert np.array_equal(blk, rc), (label, i, j, np.count_nonzero(blk != rc))
-    # invariant on every block: the largest code magnitude is 448 (0x7E)
+    # every block's largest code magnitude is 448 (0x7E), attained by its amax
     mx = (codes & 0x7F).reshape(nb, 128, kb, 128).max(axis=(1, 3))
-    assert np.all(mx == 0x7E)
-    assert np.all(scales > 0)
+    assert np.all(mx == 0x7E) and np.all(scales > 0)
+
+
+def _full_int8(fn, ref, bits, label):
+    announce(f"{fn.__name__} full-size {label} {bits.shape}")
+    codes, scales = _int8_gpu(fn, bits)
+    rc, rs = oracle_by_rows(ref, bits, 512)
+    _assert_same(codes, scales, rc, rs, f"int8 {label}")
+    assert np.all(np.abs(codes.astype(np.int32)).max(axis=1) == 127)
 
 
 def test_full_size_7b_upgate_weight():
     w = workloads.weight(37888, 3584, seed=0)
-    _full_weight_check(w, "7B up/gate")
-    announce("int8_weight_channel_quant full-size 7B up/gate")
-    codes, scales = _int8_gpu(binding.int8_weight_channel_quant, w)
-    rows = np.random.default_rng(2).choice(w.shape[0], 256, replace=False)
-    rc, rs = quant.int8_weight_channel_quant(w[rows])
-    assert np.array_equal(codes[rows], rc) and _same_f32_bits(scales[rows], rs)
-    assert np.all(np.abs(codes.astype(np.int32)).max(axis=1) == 127)
+    _full_fp8_weight(w, "7B up/gate")
+    _full_int8(binding.int8_weight_channel_quant, quant.int8_weight_channel_quant, w,
+               "7B up/gate")
 
 
-def test_full_size_32b_stack_weights():
-    for name in ("k", "down"):
-        _full_weight_check(workloads.stack_layer(name, seed=0), f"32B {name}")
+@pytest.mark.parametrize("name", [n for n, _, _ in workloads.STACK_32B])
+def test_full_size_32b_stack_weight(name):
+    """Each of the seven weights of the 32B-class layer stack, FP8 blocks and
+    INT8 channels, every byte and scale."""
+    w = workloads.stack_layer(name, seed=0)
+    _full_fp8_weight(w, f"32B {name}")
+    _full_int8(binding.int8_weight_channel_quant, quant.int8_weight_channel_quant, w,
+               f"32B {name}")
 
 
-def test_full_size_32b_prefill_activations():
-    for K, stream in ((5120, "A"), (27648, "A_down")):
-        a = workloads.activation(8192, K, seed=0, outliers=True, stream=stream)
-        announce(f"fp8_act_token_quant full-size 32B prefill {a.shape}")
-        codes, scales = _fp8_a_gpu(a)
-        rows = np.random.default_rng(K).choice(8192, 128, replace=False)
-        rc, rs = quant.fp8_act_token_quant(a[rows])
-        assert _same_f32_bits(scales[rows], rs)
-        assert np.array_equal(codes[rows], rc)
-        assert np.all((codes & 0x7F).reshape(8192, -1, 128).max(axis=2) == 0x7E)
-        announce(f"int8_act_token_quant full-size 32B prefill {a.shape}")
-        codes, scales = _int8_gpu(binding.int8_act_token_quant, a)
-        rc, rs = quant.int8_act_token_quant(a[rows])
-        assert np.array_equal(codes[rows], rc) and _same_f32_bits(scales[rows], rs)
+@pytest.mark.parametrize("K,stream", [(5120, "A"), (27648, "A_down")])
+def test_full_size_32b_prefill_activations(K, stream):
+    """All 8192 token rows of both prefill activations, FP8 groups and INT8
+    rows."""
+    a = workloads.activation(8192, K, seed=0, outliers=True, stream=stream)
+    announce(f"fp8_act_token_quant full-size 32B prefill {a.shape}")
+    codes, scales = _fp8_a_gpu(a)
+    rc, rs = oracle_by_rows(quant.fp8_act_token_quant, a, 512)
+    _assert_same(codes, scales, rc, rs, f"fp8 act K{K}")
+    assert np.all((codes & 0x7F).reshape(8192, -1, 128).max(axis=2) == 0x7E)
+    _full_int8(binding.int8_act_token_quant, quant.int8_act_token_quant, a, f"act K{K}")

@@ -74,6 +74,19 @@ def test_values_beyond_calibration_saturate():
     assert list(codes[0]) == [0x7E, 0xFE, 0x7E, 0xFE]
 
 
+def test_quotients_beyond_binary32_saturate():
+    # A stale scale far below the new values: fl32(x / s) overflows to
+    # +-inf, which is a value above the calibrated range and saturates.
+    s = np.float32(np.float32(2.0 ** -120) / np.float32(448))
+    bits = np.array([[0x3F80, 0xBF80, 0x7F7F, 0xFF7F, 0x0000, 0x8000]], dtype=np.uint16)
+    codes = kv.kv_encode_rows(bits, s)
+    assert list(codes[0]) == [0x7E, 0xFE, 0x7E, 0xFE, 0x00, 0x80]
+    # brute force: every code is the saturating code of the exact rational
+    # quotient, which here is far above 448 for the nonzero values
+    x = pins.f32_of_bf16(bits).astype(np.float64)
+    assert np.all(np.abs(x[0, :4]) / float(s) > 3.4e38)
+
+
 def test_exact_e4m3_values_round_trip():
     # amax 448 gives s = 1: every e4m3 value is its own quotient
     vals = np.array([float(v) for _, v in pins.e4m3_book()], dtype=np.float32)
