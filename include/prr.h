@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define PRR_ABI_VERSION 8
+#define PRR_ABI_VERSION 9
 
 typedef enum prr_status {
   PRR_OK = 0,
@@ -235,6 +235,26 @@ prr_status w8a8_int8_channel_gemm_ws(const int8_t* a_i8, const float* a_scale,
                                      const int8_t* w_i8, const float* w_scale, int64_t M,
                                      int64_t N, int64_t K, uint16_t* c_bf16, void* workspace,
                                      int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * w8a8_block_gemm_scratch -- w8a8_block_gemm_ws for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same definition, arguments,
+ * kernels and tolerance, with the split-K partial sums in the library's own
+ * static device array of 16 MiB (one per device, kept until the process
+ * ends) instead of a caller workspace.  The call itself allocates nothing.
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (on two streams, or from two threads) race and give undefined
+ * results; calls in order on one stream are safe.  A shape whose split
+ * needs more than 16 MiB (S x M x N x 4 bytes, as
+ * w8a8_gemm_workspace_size reports) returns PRR_ERR_UNSUPPORTED_SHAPE
+ * without launching; a shape with no split runs the one-pass kernels.  Its
+ * results equal those of w8a8_block_gemm_ws with a large enough workspace,
+ * bit for bit.
+ */
+prr_status w8a8_block_gemm_scratch(const uint8_t* a_fp8, const float* a_scale,
+                                   const uint8_t* w_fp8, const float* w_scale, int64_t M,
+                                   int64_t N, int64_t K, uint16_t* c_bf16, hipStream_t stream);
 
 /*
  * w8a8_block_gemm_grouped -- the FP8 W8A8 linear layer of a mixture of

@@ -48,6 +48,7 @@ _SIGNATURES = {
                                    _I64, _I64, ctypes.c_float, _P, _P, _I64, _P],
     "w8a8_block_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
     "w8a8_int8_channel_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
+    "w8a8_block_gemm_scratch": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P],
 }
 
 IS_TRUNCATE = 0     # TIS: min(ratio, cap)
@@ -57,7 +58,7 @@ _lib = None
 
 # PRR_ABI_VERSION of the signatures below; a library of another version is
 # refused at load time.
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class PrrError(RuntimeError):
@@ -243,6 +244,23 @@ def w8a8_block_gemm(a_fp8, a_scale, w_fp8, w_scale, out=None, workspace="auto"):
         _check("w8a8_block_gemm_ws",
                load().w8a8_block_gemm_ws(_ptr(a_fp8), _ptr(a_scale), _ptr(w_fp8), _ptr(w_scale),
                                          M, N, K, _ptr(c), _ptr(ws), ws.numel(), _stream(a_fp8)))
+    return c
+
+
+def w8a8_block_gemm_scratch(a_fp8, a_scale, w_fp8, w_scale, out=None):
+    """The FP8 GEMM with split-K partial sums in the library's static device
+    scratch (w8a8_block_gemm_scratch): no workspace argument, no allocation
+    in the call.  Pass `out` to allocate nothing here either."""
+    M, K = a_fp8.shape
+    N = w_fp8.shape[0]
+    _operand(a_fp8, torch.uint8, (M, K), "a_fp8")
+    _operand(w_fp8, torch.uint8, (N, K), "w_fp8")
+    _operand(a_scale, torch.float32, (M, _cdiv(K, 128)), "a_scale")
+    _operand(w_scale, torch.float32, (_cdiv(N, 128), _cdiv(K, 128)), "w_scale")
+    c = _out(out, torch.bfloat16, (M, N), a_fp8, "out")
+    _check("w8a8_block_gemm_scratch",
+           load().w8a8_block_gemm_scratch(_ptr(a_fp8), _ptr(a_scale), _ptr(w_fp8),
+                                          _ptr(w_scale), M, N, K, _ptr(c), _stream(a_fp8)))
     return c
 
 

@@ -213,6 +213,26 @@ prr_status w8a8_block_gemm_ws(const uint8_t* a_fp8, const float* a_scale, const 
       prr::launch_w8a8_block_gemm(a_fp8, a_scale, w_fp8, w_scale, M, N, K, c_bf16, stream));
 }
 
+prr_status w8a8_block_gemm_scratch(const uint8_t* a_fp8, const float* a_scale,
+                                   const uint8_t* w_fp8, const float* w_scale, int64_t M,
+                                   int64_t N, int64_t K, uint16_t* c_bf16, hipStream_t stream) {
+  PRR_TRY(gemm_common(a_fp8, a_scale, w_fp8, w_scale, M, N, K, c_bf16, false));
+  if (M == 0 || N == 0) return PRR_OK;
+  prr::SplitPlan plan;
+  if (K > 0 && prr::splitk_plan(M, N, K, &plan)) {
+    if (plan.bytes > prr::kScratchBytes) return PRR_ERR_UNSUPPORTED_SHAPE;
+    hipError_t err = hipSuccess;
+    float* ws = prr::scratch_ptr(&err);
+    if (ws == nullptr) return PRR_ERR_HIP;
+    if (prr::launch_gemm_decode_splitk<false>(a_fp8, a_scale, w_fp8, w_scale, M, N, K, ws,
+                                              prr::kScratchBytes, c_bf16, stream, &err))
+      return from_hip(err);
+  }
+  // No split for this shape: the one-pass kernels, which use no scratch.
+  return from_hip(
+      prr::launch_w8a8_block_gemm(a_fp8, a_scale, w_fp8, w_scale, M, N, K, c_bf16, stream));
+}
+
 prr_status w8a8_int8_channel_gemm_ws(const int8_t* a_i8, const float* a_scale,
                                      const int8_t* w_i8, const float* w_scale, int64_t M,
                                      int64_t N, int64_t K, uint16_t* c_bf16, void* workspace,

@@ -43,6 +43,7 @@
 // int32 MFMA accumulates the wave's whole piece; scales in the epilogue.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "launch.h"
 #include "mfma.h"
@@ -605,6 +606,42 @@ __global__ __launch_bounds__(512) void gemm_grouped_kernel(
     }
     carry = round_end;
   }
+}
+
+// Scratch for callers that cannot allocate (the split-K partial sums of
+// w8a8_block_gemm_scratch).  In host code `scratch` names a host-side
+// stand-in, not the device array: its device address comes from
+// hipGetSymbolAddress, per device, and only that address is passed to
+// kernels.  Every element a split-K call reads is written by the same call
+// first, so nothing needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+float* scratch_ptr(hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex init;
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(init);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      // With device `dev` current: its own copy of the array.
+      *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (*err != hipSuccess || p == nullptr) {
+        if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+        return nullptr;
+      }
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  return static_cast<float*>(p);
 }
 
 // Compute units of the current device (cached per device ordinal).

@@ -79,6 +79,14 @@ bool launch_gemm_decode_splitk(const uint8_t* A, const float* sa, const uint8_t*
 // Compute units of the current device (cached per device; 256 if unknown).
 int compute_units();
 
+// The library's static scratch array (a file-scope __device__ array, one per
+// device the library runs on, held until the process ends): its size, and
+// its device address on the current device, looked up once per device with
+// hipGetSymbolAddress (nullptr, with *err set, if that fails).  Used by the
+// allocation-free split-K GEMM entry point only.
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+float* scratch_ptr(hipError_t* err);
+
 // Decode-sized W8A8 GEMM (activation-resident, persistent).  Returns false,
 // launching nothing, when the shape is outside what it handles.
 template <bool kInt8>

@@ -46,7 +46,8 @@ def test_header_declares_the_boundary():
                      "fp8_kv_cache_write", "tis_token_weights", "w8a8_gemm_workspace_size",
                      "fp8_kv_decode_attention", "fp8_kv_decode_attention_workspace_size",
                      "fp8_kv_decode_attention_ws", "w8a8_block_gemm_ws",
-                     "w8a8_int8_channel_gemm_ws", "prr_status_string", "prr_abi_version"}
+                     "w8a8_int8_channel_gemm_ws", "w8a8_block_gemm_scratch",
+                     "prr_status_string", "prr_abi_version"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -68,7 +69,7 @@ def test_abi_version_and_status_strings():
 
 QUANTS = ["fp8_weight_block_quant", "fp8_act_token_quant", "int8_weight_channel_quant",
           "int8_act_token_quant"]
-GEMMS = ["w8a8_block_gemm", "w8a8_int8_channel_gemm"]
+GEMMS = ["w8a8_block_gemm", "w8a8_int8_channel_gemm", "w8a8_block_gemm_scratch"]
 
 
 @pytest.mark.parametrize("fn", QUANTS)
