@@ -136,6 +136,39 @@ prr_status fp8_weight_block_quant_into(const uint16_t* w_bf16, int64_t rows, int
                                        int64_t ld_scale, hipStream_t stream);
 
 /*
+ * fp8_weight_block_quant_multi / int8_weight_channel_quant_multi -- the
+ * per-step re-quantization of several weights at once, e.g. every weight of
+ * a decoder layer after a training step (FP8-RL, abstract: the policy
+ * weights change every step and are quantized again every step), in one
+ * launch: the same codes and scales, bit for bit, as
+ * fp8_weight_block_quant / int8_weight_channel_quant called once per
+ * weight.  One launch lets small weights (a k or v projection) share the
+ * machine with large ones instead of paying a launch ramp each.
+ *   jobs   host array of `count` descriptors, read during the call only
+ *          (the library copies them into the launch): each names a whole
+ *          weight w_bf16 [N, K] and its outputs, q (FP8: uint8 e4m3 codes;
+ *          INT8: int8 codes) [N, K] and scale (FP8: [ceil(N/128),
+ *          ceil(K/128)]; INT8: [N]) fp32, all row-major device memory.
+ *   count  0 .. PRR_MAX_WEIGHT_JOBS (PRR_ERR_INVALID_ARG otherwise).
+ *   Each job is checked as the single-weight call checks it (dimensions,
+ *   NULL and 16-byte alignment of its pointers); a job with N == 0, or
+ *   K == 0 for FP8, writes nothing (INT8 with K == 0 writes zero scales).
+ *   Jobs must not overlap one another's outputs.  PRR_ERR_UNSUPPORTED_SHAPE
+ *   when the jobs together exceed 2^31 - 1 work units.
+ */
+#define PRR_MAX_WEIGHT_JOBS 16
+typedef struct prr_weight_job {
+  const uint16_t* w_bf16;
+  int64_t N, K;
+  void* q;
+  float* scale;
+} prr_weight_job;
+prr_status fp8_weight_block_quant_multi(const prr_weight_job* jobs, int64_t count,
+                                        hipStream_t stream);
+prr_status int8_weight_channel_quant_multi(const prr_weight_job* jobs, int64_t count,
+                                           hipStream_t stream);
+
+/*
  * fp8_act_token_quant -- FP8 e4m3 quantization of bf16 activations in
  * per-token groups of 128 consecutive input features (FP8-RL, abstract,
  * item (i): the "A8" of W8A8).

@@ -23,7 +23,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libprr.so")
+# PRR_LIB may point the binding at another build of the same library (the
+# CPU tests load a host-AddressSanitizer build of the ABI layer this way).
+LIB_PATH = os.environ.get("PRR_LIB") or os.path.join(_HERE, "libprr.so")
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -49,7 +51,16 @@ _SIGNATURES = {
     "w8a8_block_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
     "w8a8_int8_channel_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
     "w8a8_block_gemm_scratch": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P],
+    "fp8_weight_block_quant_multi": [_P, _I64, _P],
+    "int8_weight_channel_quant_multi": [_P, _I64, _P],
 }
+
+MAX_WEIGHT_JOBS = 16
+
+
+class WeightJob(ctypes.Structure):
+    """prr_weight_job: one whole weight and its outputs."""
+    _fields_ = [("w_bf16", _P), ("N", _I64), ("K", _I64), ("q", _P), ("scale", _P)]
 
 IS_TRUNCATE = 0     # TIS: min(ratio, cap)
 IS_MASK = 1         # MIS: ratio, or 0 above the cap
@@ -262,6 +273,40 @@ def w8a8_block_gemm_scratch(a_fp8, a_scale, w_fp8, w_scale, out=None):
            load().w8a8_block_gemm_scratch(_ptr(a_fp8), _ptr(a_scale), _ptr(w_fp8),
                                           _ptr(w_scale), M, N, K, _ptr(c), _stream(a_fp8)))
     return c
+
+
+def _weight_multi(name, ws, outs, code_dtype, scale_shape):
+    if len(ws) > MAX_WEIGHT_JOBS:
+        raise ValueError(f"{name}: at most {MAX_WEIGHT_JOBS} weights per call")
+    ws = [_bf16_bits(w, f"weights[{i}]") for i, w in enumerate(ws)]
+    if outs is None:
+        outs = [(None, None)] * len(ws)
+    if len(outs) != len(ws):
+        raise ValueError(f"{name}: one (codes, scales) pair per weight")
+    res, jobs = [], (WeightJob * max(1, len(ws)))()
+    for i, (w, (q, s)) in enumerate(zip(ws, outs)):
+        N, K = w.shape
+        q = _out(q, code_dtype, (N, K), w, f"outs[{i}][0]")
+        s = _out(s, torch.float32, scale_shape(N, K), w, f"outs[{i}][1]")
+        jobs[i] = WeightJob(_ptr(w), N, K, _ptr(q), _ptr(s))
+        res.append((q, s))
+    stream = _stream(ws[0]) if ws else torch.cuda.current_stream().cuda_stream
+    _check(name, getattr(load(), name)(ctypes.addressof(jobs), len(ws), stream))
+    return res
+
+
+def fp8_weight_block_quant_multi(weights, outs=None):
+    """Several Wt [N, K] bf16 weights in one launch -> [(codes uint8 [N, K],
+    scales fp32 [ceil(N/128), ceil(K/128)])] (fp8_weight_block_quant_multi)."""
+    return _weight_multi("fp8_weight_block_quant_multi", weights, outs, torch.uint8,
+                         lambda N, K: (_cdiv(N, 128), _cdiv(K, 128)))
+
+
+def int8_weight_channel_quant_multi(weights, outs=None):
+    """Several Wt [N, K] bf16 weights in one launch -> [(codes int8 [N, K],
+    scales fp32 [N])] (int8_weight_channel_quant_multi)."""
+    return _weight_multi("int8_weight_channel_quant_multi", weights, outs, torch.int8,
+                         lambda N, K: (N,))
 
 
 def int8_weight_channel_quant(w: torch.Tensor, out=None, scale=None):

@@ -76,5 +76,45 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def asan_runtime() -> str | None:
+    """The compiler's shared AddressSanitizer runtime (to preload into a
+    process that loads the instrumented library), or None."""
+    import glob
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return found[-1] if found else None
+
+
+def build_asan_abi() -> str:
+    """A copy of the library whose host-side ABI layer (api.cpp: argument,
+    pointer and device checks) is built with AddressSanitizer; the kernels'
+    objects are the regular ones (the sanitizer applies to host code only).
+    Returns the path of _build/libprr_asan.so; it loads only into a process
+    that preloads asan_runtime()."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    others = [s for s in SOURCES if s != "api.cpp"]
+    objs = [os.path.join(OBJ_DIR, s + ".o") for s in others]
+    missing = [os.path.join(CSRC, s) for s, o in zip(others, objs) if not os.path.exists(o)]
+    if missing:
+        with ThreadPoolExecutor(max(1, min(len(missing), os.cpu_count() or 1, 16))) as ex:
+            for obj, rc, err in ex.map(_compile, missing):
+                if rc != 0:
+                    raise RuntimeError(f"hipcc failed on {obj}:\n{err}")
+    api_obj = os.path.join(OBJ_DIR, "api_asan.o")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-shared-libsan"]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", *san,
+           "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc (asan) failed:\n{_filter(res.stderr)}")
+    lib = os.path.join(OBJ_DIR, "libprr_asan.so")
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *san, api_obj, *objs,
+           "-o", lib]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link (asan) failed:\n{_filter(res.stderr)}")
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

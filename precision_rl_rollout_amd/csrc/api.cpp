@@ -109,6 +109,67 @@ prr_status fp8_weight_block_quant_into(const uint16_t* w_bf16, int64_t rows, int
                                                      scale, ld_scale, stream));
 }
 
+// Checks and work-unit layout shared by the two multi-weight calls.
+static prr_status weight_jobs(const prr_weight_job* jobs, int64_t count, bool int8,
+                              prr::WeightJobs* out) {
+  if (count < 0 || count > PRR_MAX_WEIGHT_JOBS) return PRR_ERR_INVALID_ARG;
+  if (count > 0 && jobs == nullptr) return PRR_ERR_INVALID_ARG;
+  memset(out, 0, sizeof(*out));
+  int64_t total = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const prr_weight_job& j = jobs[i];
+    PRR_TRY(check_dims(j.N, j.K));
+    if (j.N == 0 || (j.K == 0 && !int8)) continue;   // nothing to write
+    if (j.K == 0) {
+      PRR_TRY(check_ptrs({j.scale}));                 // INT8: zero scales only
+    } else {
+      PRR_TRY(check_ptrs({j.w_bf16, j.q, j.scale}));
+    }
+    const int c = out->count;
+    out->w[c] = j.w_bf16;
+    out->q[c] = j.q;
+    out->scale[c] = j.scale;
+    out->N[c] = j.N;
+    out->K[c] = j.K;
+    int64_t units;
+    if (int8) {
+      const int cls = prr::int8_row_class(j.K);
+      const int per = prr::int8_rows_per_unit(cls);
+      out->units_per_row[c] = cls;
+      units = (j.N + per - 1) / per;
+    } else {
+      const int64_t nbk = (j.K + 127) / 128;
+      out->units_per_row[c] = (int)nbk;
+      units = ((j.N + 127) / 128) * nbk;
+    }
+    out->first[c] = (int)total;
+    total += units;
+    if (total > kMaxGrid) return PRR_ERR_UNSUPPORTED_SHAPE;
+    out->count = c + 1;
+  }
+  out->first[out->count] = (int)total;
+  // The scan in the kernels reads first[count]; unused slots stay zero.
+  return PRR_OK;
+}
+
+prr_status fp8_weight_block_quant_multi(const prr_weight_job* jobs, int64_t count,
+                                        hipStream_t stream) {
+  prr::WeightJobs wj;
+  PRR_TRY(weight_jobs(jobs, count, false, &wj));
+  if (wj.first[wj.count] == 0) return PRR_OK;
+  PRR_TRY(check_device());
+  return from_hip(prr::launch_fp8_weight_block_quant_multi(wj, stream));
+}
+
+prr_status int8_weight_channel_quant_multi(const prr_weight_job* jobs, int64_t count,
+                                           hipStream_t stream) {
+  prr::WeightJobs wj;
+  PRR_TRY(weight_jobs(jobs, count, true, &wj));
+  if (wj.first[wj.count] == 0) return PRR_OK;
+  PRR_TRY(check_device());
+  return from_hip(prr::launch_int8_weight_channel_quant_multi(wj, stream));
+}
+
 prr_status fp8_act_token_quant(const uint16_t* a_bf16, int64_t M, int64_t K, uint8_t* a_fp8,
                                float* a_scale, hipStream_t stream) {
   if (M < 0 || K < 0) return PRR_ERR_INVALID_ARG;

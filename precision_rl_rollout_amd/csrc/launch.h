@@ -13,6 +13,27 @@ hipError_t launch_fp8_weight_block_quant(const uint16_t* w, int64_t N, int64_t K
                                          hipStream_t stream);
 hipError_t launch_fp8_act_token_quant(const uint16_t* a, int64_t M, int64_t K, uint8_t* q,
                                       float* scale, hipStream_t stream);
+
+// Several whole weights Wt [N, K] quantized in one launch (passed by value
+// in the kernel arguments).  first[j] is the first work unit of job j
+// (first[count] = total): FP8, 128 x 128 blocks (units_per_row = blocks
+// per block row); INT8, row groups of a class chosen per job.
+constexpr int kMaxWeightJobs = 16;
+struct WeightJobs {
+  const uint16_t* w[kMaxWeightJobs];
+  void* q[kMaxWeightJobs];
+  float* scale[kMaxWeightJobs];
+  int64_t N[kMaxWeightJobs];
+  int64_t K[kMaxWeightJobs];
+  int units_per_row[kMaxWeightJobs];   // FP8: blocks per block row; INT8: row class
+  int first[kMaxWeightJobs + 1];
+  int count;
+};
+hipError_t launch_fp8_weight_block_quant_multi(const WeightJobs& jobs, hipStream_t stream);
+hipError_t launch_int8_weight_channel_quant_multi(const WeightJobs& jobs, hipStream_t stream);
+// INT8 row class of a weight with K columns and the rows one work unit takes.
+int int8_row_class(int64_t K);
+int int8_rows_per_unit(int cls);
 hipError_t launch_w8a8_block_gemm(const uint8_t* A, const float* sa, const uint8_t* W,
                                   const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* C,
                                   hipStream_t stream);

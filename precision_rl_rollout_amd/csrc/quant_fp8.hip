@@ -41,14 +41,13 @@ __device__ __forceinline__ void encode_block_rows(const uint4 (&v)[8], const Blo
   }
 }
 
-// An N x K matrix with row strides ldw (input, elements), ldq (codes,
-// bytes) and lds (scales, floats); the whole-weight call has ldw = ldq = K
-// and lds = nbk.
-__global__ __launch_bounds__(256) void fp8_weight_block_kernel(
-    const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldw, uint8_t* __restrict__ q,
-    int64_t ldq, float* __restrict__ scale, int64_t lds, int nbk) {
-  const int bi = blockIdx.x / nbk;
-  const int bj = blockIdx.x - bi * nbk;
+// Block (bi, bj) of an N x K matrix with row strides ldw (input, elements),
+// ldq (codes, bytes) and lds (scales, floats); the whole-weight call has
+// ldw = ldq = K and lds = nbk.  Called by all 256 threads of a workgroup.
+__device__ __forceinline__ void fp8_weight_block(const uint16_t* __restrict__ w, int64_t N,
+                                                 int64_t K, int64_t ldw, uint8_t* __restrict__ q,
+                                                 int64_t ldq, float* __restrict__ scale,
+                                                 int64_t lds, int bi, int bj) {
   const int tid = threadIdx.x;
   const int seg = tid >> 4;       // row within a step, 0..15
   const int l16 = tid & 15;       // 8-element chunk within the row segment
@@ -100,6 +99,35 @@ __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
   if (s == 0.0f) encode_block_rows<0>(v, d, full, q, N, K, ldq, row0, seg, col);
   else if (d.tiny) encode_block_rows<2>(v, d, full, q, N, K, ldq, row0, seg, col);
   else encode_block_rows<1>(v, d, full, q, N, K, ldq, row0, seg, col);
+}
+
+__global__ __launch_bounds__(256) void fp8_weight_block_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldw, uint8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale, int64_t lds, int nbk) {
+  const int bi = blockIdx.x / nbk;
+  const int bj = blockIdx.x - bi * nbk;
+  fp8_weight_block(w, N, K, ldw, q, ldq, scale, lds, bi, bj);
+}
+
+// Several weights in one grid (a layer stack re-quantized after a training
+// step): the jobs' blocks are numbered one after another, workgroup b takes
+// block b; the job is found by a scan of the block prefix counts (uniform,
+// at most kMaxWeightJobs entries, in the kernel arguments).  One launch
+// instead of one per weight: small weights (a 10 MB k or v projection) no
+// longer pay a launch ramp and drain of their own, and their blocks fill
+// the machine beside the large ones.
+__global__ __launch_bounds__(256) void fp8_weight_block_multi_kernel(WeightJobs jobs) {
+  const int b = blockIdx.x;
+  int j = 0;
+#pragma unroll 1
+  while (j + 1 < jobs.count && b >= jobs.first[j + 1]) ++j;
+  j = __builtin_amdgcn_readfirstlane(j);
+  const int local = b - jobs.first[j];
+  const int nbk = jobs.units_per_row[j];
+  const int bi = local / nbk, bj = local - bi * nbk;
+  const int64_t K = jobs.K[j];
+  fp8_weight_block(jobs.w[j], jobs.N[j], K, K, static_cast<uint8_t*>(jobs.q[j]), K,
+                   jobs.scale[j], nbk, bi, bj);
 }
 
 // ---------------------------------------------------------------------------
@@ -178,6 +206,14 @@ hipError_t launch_fp8_weight_block_quant(const uint16_t* w, int64_t N, int64_t K
   const int64_t blocks = nbn * nbk;
   hipLaunchKernelGGL(fp8_weight_block_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w,
                      N, K, ldw, q, ldq, scale, lds, (int)nbk);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_weight_block_quant_multi(const WeightJobs& jobs, hipStream_t stream) {
+  const int blocks = jobs.first[jobs.count];
+  if (blocks > 0)
+    hipLaunchKernelGGL(fp8_weight_block_multi_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, jobs);
   return hipGetLastError();
 }
 

@@ -34,15 +34,16 @@ __device__ __forceinline__ void int8_store_row(const uint4 (&v)[kMaxChunks], con
   }
 }
 
-// Register-resident row: kLanes lanes (64: a wave, 256: the workgroup) per row.
+// Register-resident row: kLanes lanes (64: a wave, 256: the workgroup) per
+// row; work unit u is rows 256 / kLanes u ...  Called by all 256 threads.
 template <int kLanes>
-__global__ __launch_bounds__(256) void int8_row_resident_kernel(
-    const uint16_t* __restrict__ x, int64_t R, int64_t K, int8_t* __restrict__ q,
-    float* __restrict__ scale) {
+__device__ __forceinline__ void int8_rows_resident(const uint16_t* __restrict__ x, int64_t R,
+                                                   int64_t K, int8_t* __restrict__ q,
+                                                   float* __restrict__ scale, int64_t unit) {
   constexpr int kRowsPerWg = 256 / kLanes;
   const int tid = threadIdx.x;
   const int lane = tid % kLanes;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + tid / kLanes;
+  const int64_t row = unit * kRowsPerWg + tid / kLanes;
   const bool live = row < R;                    // uniform per row group
   const int64_t chunks = K / 8;
   const uint16_t* src = x + row * K;
@@ -75,13 +76,19 @@ __global__ __launch_bounds__(256) void int8_row_resident_kernel(
   else int8_store_row<1, kLanes>(v, d, dst, chunks, lane);
 }
 
-// Any K: a workgroup per row, two passes; 16-byte chunks when K % 8 == 0,
-// single elements otherwise.
-__global__ __launch_bounds__(256) void int8_row_twopass_kernel(
-    const uint16_t* __restrict__ x, int64_t K, int8_t* __restrict__ q,
+template <int kLanes>
+__global__ __launch_bounds__(256) void int8_row_resident_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t K, int8_t* __restrict__ q,
     float* __restrict__ scale) {
+  int8_rows_resident<kLanes>(x, R, K, q, scale, blockIdx.x);
+}
+
+// Any K: a workgroup per row, two passes; 16-byte chunks when K % 8 == 0,
+// single elements otherwise.  Called by all 256 threads.
+__device__ __forceinline__ void int8_row_twopass(const uint16_t* __restrict__ x, int64_t K,
+                                                 int8_t* __restrict__ q,
+                                                 float* __restrict__ scale, int64_t row) {
   __shared__ uint32_t red[4];
-  const int64_t row = blockIdx.x;
   const uint16_t* src = x + row * K;
   uint8_t* dst = reinterpret_cast<uint8_t*>(q) + row * K;
   const int tid = threadIdx.x;
@@ -121,12 +128,53 @@ __global__ __launch_bounds__(256) void int8_row_twopass_kernel(
   }
 }
 
+__global__ __launch_bounds__(256) void int8_row_twopass_kernel(
+    const uint16_t* __restrict__ x, int64_t K, int8_t* __restrict__ q,
+    float* __restrict__ scale) {
+  int8_row_twopass(x, K, q, scale, blockIdx.x);
+}
+
+// Row classes: 0 = a wave per row (4 rows per work unit), 1 = a workgroup
+// per row held in registers, 2 = two passes.
+int int8_row_class(int64_t K) {
+  if (K % 8 == 0 && K <= 64 * 8 * kMaxChunks) return 0;
+  if (K % 8 == 0 && K <= 256 * 8 * kMaxChunks) return 1;
+  return 2;
+}
+
+int int8_rows_per_unit(int cls) { return cls == 0 ? 4 : 1; }
+
+// Several weights in one grid, as the FP8 multi-weight kernel: workgroup b
+// takes work unit b of the job whose range holds it; the job's row class is
+// uniform, so each workgroup runs one of the three row paths.
+__global__ __launch_bounds__(256) void int8_row_multi_kernel(WeightJobs jobs) {
+  const int b = blockIdx.x;
+  int j = 0;
+#pragma unroll 1
+  while (j + 1 < jobs.count && b >= jobs.first[j + 1]) ++j;
+  j = __builtin_amdgcn_readfirstlane(j);
+  const int64_t unit = b - jobs.first[j];
+  const int cls = jobs.units_per_row[j];
+  int8_t* q = static_cast<int8_t*>(jobs.q[j]);
+  if (cls == 0) int8_rows_resident<64>(jobs.w[j], jobs.N[j], jobs.K[j], q, jobs.scale[j], unit);
+  else if (cls == 1) int8_rows_resident<256>(jobs.w[j], jobs.N[j], jobs.K[j], q, jobs.scale[j], unit);
+  else int8_row_twopass(jobs.w[j], jobs.K[j], q, jobs.scale[j], unit);
+}
+
+hipError_t launch_int8_weight_channel_quant_multi(const WeightJobs& jobs, hipStream_t stream) {
+  const int units = jobs.first[jobs.count];
+  if (units > 0)
+    hipLaunchKernelGGL(int8_row_multi_kernel, dim3((unsigned)units), dim3(256), 0, stream, jobs);
+  return hipGetLastError();
+}
+
 static hipError_t launch_int8_rows(const uint16_t* x, int64_t R, int64_t K, int8_t* q,
                                    float* scale, hipStream_t stream) {
-  if (K % 8 == 0 && K <= 64 * 8 * kMaxChunks)
+  const int cls = int8_row_class(K);
+  if (cls == 0)
     hipLaunchKernelGGL(int8_row_resident_kernel<64>, dim3((unsigned)((R + 3) / 4)), dim3(256), 0,
                        stream, x, R, K, q, scale);
-  else if (K % 8 == 0 && K <= 256 * 8 * kMaxChunks)
+  else if (cls == 1)
     hipLaunchKernelGGL(int8_row_resident_kernel<256>, dim3((unsigned)R), dim3(256), 0, stream, x,
                        R, K, q, scale);
   else

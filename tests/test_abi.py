@@ -47,6 +47,7 @@ def test_header_declares_the_boundary():
                      "fp8_kv_decode_attention", "fp8_kv_decode_attention_workspace_size",
                      "fp8_kv_decode_attention_ws", "w8a8_block_gemm_ws",
                      "w8a8_int8_channel_gemm_ws", "w8a8_block_gemm_scratch",
+                     "fp8_weight_block_quant_multi", "int8_weight_channel_quant_multi",
                      "prr_status_string", "prr_abi_version"}
 
 
@@ -324,3 +325,24 @@ def test_quant_into_argument_checks():
     assert c(*a) == NO_DEVICE
     assert c(*ok) == NO_DEVICE
     assert c(None, 0, 384, 0, None, 0, None, 0, None) == OK      # empty: nothing touched
+
+
+@pytest.mark.parametrize("fn", ["fp8_weight_block_quant_multi", "int8_weight_channel_quant_multi"])
+def test_multi_weight_argument_checks(fn):
+    J = binding.WeightJob
+    c = lambda jobs, n: binding.call(fn, None if jobs is None else ctypes.addressof(jobs), n, None)
+    one = (J * 1)(J(FAKE, 4, 128, FAKE, FAKE))
+    assert c(None, 0) == OK                               # nothing to do
+    assert c(None, 1) == INVALID                          # jobs missing
+    assert c(one, -1) == INVALID
+    assert c(one, binding.MAX_WEIGHT_JOBS + 1) == INVALID
+    for bad, want in ((J(FAKE, -1, 128, FAKE, FAKE), INVALID), (J(FAKE, 4, 2 ** 31, FAKE, FAKE), INVALID),
+                      (J(None, 4, 128, FAKE, FAKE), INVALID), (J(FAKE, 4, 128, None, FAKE), INVALID),
+                      (J(FAKE, 4, 128, FAKE, None), INVALID), (J(ODD, 4, 128, FAKE, FAKE), MISALIGNED),
+                      (J(FAKE, 4, 128, ODD, FAKE), MISALIGNED), (J(FAKE, 4, 128, FAKE, ODD), MISALIGNED)):
+        two = (J * 2)(J(FAKE, 4, 128, FAKE, FAKE), bad)
+        assert c(two, 2) == want
+    empty = (J * 2)(J(None, 0, 128, None, None), J(None, 0, 0, None, None))
+    assert c(empty, 2) == OK                              # empty jobs: no device work
+    if not _gpu_visible():
+        assert c(one, 1) == NO_DEVICE
