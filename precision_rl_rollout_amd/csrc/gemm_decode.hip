@@ -163,15 +163,35 @@ __device__ __forceinline__ void decode_segment(
   for (int q = 0; q < R - 1; ++q) load_task(q);
 
   // Resident activation fragments of all m-tiles for this wave's K piece.
+  // Every CU reads all of the activations (M x K bytes), so how they are
+  // fetched matters: a fragment load gives lane 16 g + n 16 bytes of token n,
+  // so each group of 16 lanes touches 16 different 64-byte sectors, 16 bytes
+  // of each, and at 64 rows fetching the activations that way took 6-8 us of
+  // a 36-39 us kernel.  With two or more m-tiles they are instead loaded so
+  // that each group of 4 lanes reads one whole 64-byte sector -- instruction
+  // h gives lane s chunk 4 h + (s & 3) of token s / 4 -- and one
+  // ds_bpermute per register then moves lane 4 n + g to lane 16 g + n: the
+  // fragment layout (measured 5-8% faster over the whole GEMM at 32-64
+  // rows).
   const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(A, (int64_t)M * ld);
+  constexpr bool kSectorLoads = MT >= 2;
   v8i afr[MT][P];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int j = 0; j < P; ++j) {
-      const int m = mt * 16 + r16;
-      const int off = (j < pw) ? m * ld + (kbf + kb0 + j) * kBlock + g * 16 : kOutOfRange;
-      afr[mt][j] = buffer_load32(ares, off, 0);
+      if constexpr (kSectorLoads) {
+        const int off = (j < pw) ? (mt * 16 + (lane >> 2)) * ld + (kbf + kb0 + j) * kBlock +
+                                       (lane & 3) * 16
+                                 : kOutOfRange;
+        const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
+        const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(ares, (j < pw) ? off + 64 : off, 0, 0);
+        afr[mt][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        const int m = mt * 16 + r16;
+        const int off = (j < pw) ? m * ld + (kbf + kb0 + j) * kBlock + g * 16 : kOutOfRange;
+        afr[mt][j] = buffer_load32(ares, off, 0);
+      }
     }
 
   // Dynamic LDS: the FP8 activation scales of all rows, transposed to
@@ -214,6 +234,16 @@ __device__ __forceinline__ void decode_segment(
 #pragma unroll
       for (int q = 0; q < 8; ++q) asm volatile("" : : "v"(__int_as_float(afr[mt][j][q])));
     if constexpr (kInt8) asm volatile("" : : "v"(sa_row[mt]));
+  }
+  if constexpr (kSectorLoads) {
+    // lane 16 g + n takes lane 4 n + g of the same register (byte address)
+    const int src = (((lane & 15) << 2) | (lane >> 4)) << 2;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < P; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) afr[mt][j][q] = __builtin_amdgcn_ds_bpermute(src, afr[mt][j][q]);
   }
   if constexpr (!kInt8) lds_barrier();
 
