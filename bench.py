@@ -215,33 +215,50 @@ def run_decode7b(args, torch, B, W):
                            Wt=torch.from_numpy(p["Wt"].view(np.int16)).cuda()))
     w8 = B.fp8_weight_block_quant(inputs[0]["Wt"])
     copies = _cold_copies(torch, lambda i: (w8[0].clone(), w8[1].clone()), N * K)
-    aq8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    sa8 = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    # One activation batch per timed step (the decode of K tokens' worth of
+    # batches), quantized in the step.
+    nsteps = max(1, args.steps)
+    aq8 = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nsteps)]
+    sa8 = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(nsteps)]
     c8 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     gbytes = gemm_bytes(M, N, K, M * (K // 128), cdiv(N, 128) * (K // 128))
     abytes = quant_bytes(M, K, M * (K // 128))
 
-    def step(i, timer=None):
-        t = timer.run if timer else (lambda _n, f: f())
+    def quant(i):
+        B.fp8_act_token_quant(inputs[i % 2]["A"], out=aq8[i % nsteps], scale=sa8[i % nsteps])
+
+    def gemm(i):
         wq, sw = copies[i % len(copies)]
-        a = inputs[i % 2]["A"]
-        t("fp8_act_token_quant", lambda: B.fp8_act_token_quant(a, out=aq8, scale=sa8))
-        t("w8a8_block_gemm", lambda: B.w8a8_block_gemm(aq8, sa8, wq, sw, out=c8))
+        B.w8a8_block_gemm(aq8[i % nsteps], sa8[i % nsteps], wq, sw, out=c8)
 
     for i in range(args.warmup):
-        step(i)
+        quant(i)
+        gemm(i)
     torch.cuda.synchronize()
-    timer = Timer(torch, only="w8a8_block_gemm")
+    # Timed region: the K steps' activation quantizations, then their K GEMMs
+    # back to back (each on the next of the cold weight copies); a pair of HIP
+    # events on the launch stream brackets each of the two runs, so the GEMM's
+    # average launch duration includes the dispatch gap between launches.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     t0 = time.perf_counter()
+    ev[0].record()
     for i in range(args.steps):
-        step(i, timer)
+        quant(i)
+    ev[1].record()
+    for i in range(args.steps):
+        gemm(i)
+    ev[2].record()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
-    g_us = timer.avg_us()["w8a8_block_gemm"]
+    q_us = ev[0].elapsed_time(ev[1]) * 1e3 / args.steps
+    g_us = ev[1].elapsed_time(ev[2]) * 1e3 / args.steps
     achieved = gbytes / g_us / 1e3
     roofline = {"bound": "hbm", "kernel": "w8a8_block_gemm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "us_per_launch": round(g_us, 2),
                 "traffic": measured_traffic("w8a8_block_gemm", "decode7b_upgate")}
+    act = {"fp8_act_token_quant": {"us_per_launch": round(q_us, 2),
+                                   "GB/s": round(abytes / q_us / 1e3, 1)}}
     req = requant_step_decode7b(args, torch, B, W, inputs)
     line = {
         "metric": METRIC, "value": round(achieved, 1), "unit": "GB/s",
@@ -249,11 +266,12 @@ def run_decode7b(args, torch, B, W):
         "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
         "config": {"workload": "decode7b_upgate", "M": M, "N": N, "K": K,
-                   "value_is": "fp8 W8A8 block GEMM algorithmic GB/s (HIP events), cold weights",
+                   "value_is": "fp8 W8A8 block GEMM algorithmic GB/s: HIP events around the "
+                               "timed steps' GEMMs launched back to back, cold weights",
                    "step": "fp8 A group quant + fp8 W8A8 block GEMM (weight quantized before)",
                    "gemm_algorithmic_bytes": gbytes,
                    "step_algorithmic_bytes": gbytes + abytes},
-        "roofline": roofline,
+        "roofline": roofline, "step_kernels": act,
     }
     line["prefill"] = prefill_upgate_line(args, torch, B, W)
     line["requant_step"] = req
@@ -317,9 +335,9 @@ def requant_step_decode7b(args, torch, B, W, inputs):
 
 def prefill_upgate_line(args, torch, B, W):
     """FP8 W8A8 block GEMM of the 32B-class prefill up/gate layer (M 8192,
-    N 27648, K 5120) in TFLOP/s by HIP events over `steps` launches (at
-    least 10), against the 5.0 PFLOP/s dense FP8 peak; the down projection
-    (N 5120, K 27648) beside it."""
+    N 27648, K 5120) in TFLOP/s: one pair of HIP events around steps / 4
+    (at least 10) launches back to back, against the 5.0 PFLOP/s dense FP8
+    peak; the down projection (N 5120, K 27648) beside it."""
     out = {}
     for which, (N, K) in (("upgate", (27648, 5120)), ("down", (5120, 27648))):
         p = W.gemm_problem(8192, N, K, True, seed=0, down=which == "down")
@@ -331,14 +349,18 @@ def prefill_upgate_line(args, torch, B, W):
         c = torch.empty((8192, N), dtype=torch.bfloat16, device="cuda:0")
         for _ in range(max(2, args.warmup)):
             B.w8a8_block_gemm(aq, sa, wq, sw, out=c)
-        timer = Timer(torch)
-        for _ in range(max(10, args.steps // 4)):
-            timer.run("gemm", lambda: B.w8a8_block_gemm(aq, sa, wq, sw, out=c))
+        n = max(10, args.steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        us = timer.avg_us()["gemm"]
+        e0.record()
+        for _ in range(n):
+            B.w8a8_block_gemm(aq, sa, wq, sw, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
         tf = 2 * 8192 * N * K / us / 1e6
         out[which] = {"M": 8192, "N": N, "K": K, "us": round(us, 2), "TFLOP/s": round(tf, 1),
-                      "frac": round(tf / FP8_PEAK_TFLOPS, 4), "launches": len(timer.pairs["gemm"])}
+                      "frac": round(tf / FP8_PEAK_TFLOPS, 4), "launches": n}
         del aq, sa, wq, sw, c
     up = out["upgate"]
     return {"workload": "prefill32b up/gate: A [8192, 5120] x Wt [27648, 5120], FP8 blocks",

@@ -156,43 +156,10 @@ __device__ __forceinline__ void decode_segment(
   };
   constexpr int kLoadsPerTask = 3;
 
-  // The ring's first R - 1 tasks go out first, then the activations and
-  // their scales, so that all of the segment's start-up loads are in
-  // flight together (one memory latency, not two).
+  // The ring's first R - 1 tasks go out first, then the activation scales
+  // and the activations, so that the segment's start-up loads overlap.
 #pragma unroll
   for (int q = 0; q < R - 1; ++q) load_task(q);
-
-  // Resident activation fragments of all m-tiles for this wave's K piece.
-  // Every CU reads all of the activations (M x K bytes), so how they are
-  // fetched matters: a fragment load gives lane 16 g + n 16 bytes of token n,
-  // so each group of 16 lanes touches 16 different 64-byte sectors, 16 bytes
-  // of each, and at 64 rows fetching the activations that way took 6-8 us of
-  // a 36-39 us kernel.  With two or more m-tiles they are instead loaded so
-  // that each group of 4 lanes reads one whole 64-byte sector -- instruction
-  // h gives lane s chunk 4 h + (s & 3) of token s / 4 -- and one
-  // ds_bpermute per register then moves lane 4 n + g to lane 16 g + n: the
-  // fragment layout (measured 5-8% faster over the whole GEMM at 32-64
-  // rows).
-  const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(A, (int64_t)M * ld);
-  constexpr bool kSectorLoads = MT >= 2;
-  v8i afr[MT][P];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      if constexpr (kSectorLoads) {
-        const int off = (j < pw) ? (mt * 16 + (lane >> 2)) * ld + (kbf + kb0 + j) * kBlock +
-                                       (lane & 3) * 16
-                                 : kOutOfRange;
-        const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
-        const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(ares, (j < pw) ? off + 64 : off, 0, 0);
-        afr[mt][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      } else {
-        const int m = mt * 16 + r16;
-        const int off = (j < pw) ? m * ld + (kbf + kb0 + j) * kBlock + g * 16 : kOutOfRange;
-        afr[mt][j] = buffer_load32(ares, off, 0);
-      }
-    }
 
   // Dynamic LDS: the FP8 activation scales of all rows, transposed to
   // [K block][row] (kept for the whole segment), then two partial-sum
@@ -223,6 +190,40 @@ __device__ __forceinline__ void decode_segment(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) sa_row[mt] = (mt * 16 + r16 < M) ? sa[mt * 16 + r16] : 0.f;
   }
+
+  // Resident activation fragments of all m-tiles for this wave's K piece.
+  // Every CU reads all of the activations (M x K bytes), so how they are
+  // fetched matters: a fragment load gives lane 16 g + n 16 bytes of token n,
+  // so each group of 16 lanes touches 16 different 64-byte sectors, 16 bytes
+  // of each, and at 64 rows fetching the activations that way took 6-8 us of
+  // a 36-39 us kernel.  With two or more m-tiles they are instead loaded so
+  // that each group of 4 lanes reads one whole 64-byte sector -- instruction
+  // h gives lane s chunk 4 h + (s & 3) of token s / 4 -- and one
+  // ds_bpermute per register then moves lane 4 n + g to lane 16 g + n: the
+  // fragment layout (measured 5-8% faster over the whole GEMM at 32-64
+  // rows).  They are issued after the activation scales have been staged in
+  // LDS (so that staging waits for the scales alone), block by block.
+  const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(A, (int64_t)M * ld);
+  constexpr bool kSectorLoads = MT >= 2;
+  v8i afr[MT][P];
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if constexpr (kSectorLoads) {
+        const int off = (j < pw) ? (mt * 16 + (lane >> 2)) * ld + (kbf + kb0 + j) * kBlock +
+                                       (lane & 3) * 16
+                                 : kOutOfRange;
+        const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
+        const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(ares, (j < pw) ? off + 64 : off, 0, 0);
+        afr[mt][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        const int m = mt * 16 + r16;
+        const int off = (j < pw) ? m * ld + (kbf + kb0 + j) * kBlock + g * 16 : kOutOfRange;
+        afr[mt][j] = buffer_load32(ares, off, 0);
+      }
+    }
+
   // Wait for the activations here, with nothing queued behind them: an
   // empty asm that consumes the registers makes the compiler place its own
   // wait here rather than at their first use, where it would also wait for
@@ -410,13 +411,32 @@ __device__ __forceinline__ void decode_segment(
 }
 
 // Dense layer: strips l, l + G, l + 2G, ... of one weight (l below).
+//
+// With m_split = 2 (65 to 128 token rows, more than the registers of one
+// workgroup hold) the token rows are cut in two, rows [0, m_half) and
+// [m_half, M): workgroups b and b + 8 of every group of 16 take the same
+// strips for the two row ranges.  They run on one XCD (workgroup b runs on
+// XCD b % 8) at the same time, so the second reads each weight strip from
+// that XCD's L2 the first one's loads filled, and the weight streams from
+// HBM once.  Every CU fetches only its half of the activations.
 template <int MT, int P, bool kInt8>
 __global__ __launch_bounds__(512) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
-    const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int nstrips) {
+    const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int nstrips,
+    int m_split, int m_half) {
   __shared__ __align__(16) DecodeRing ring;
   extern __shared__ __align__(16) float lds_dyn[];
-  const int G = gridDim.x, b = blockIdx.x;
+  int G = gridDim.x, b = blockIdx.x;
+  if (m_split == 2) {
+    const int h = (b >> 3) & 1;
+    b = (b & 7) | ((b >> 4) << 3);
+    G >>= 1;
+    const int m0 = h * m_half;
+    A += (int64_t)m0 * K;
+    sa += kInt8 ? m0 : (int64_t)m0 * (K / kBlock);
+    C += (int64_t)m0 * N;
+    M = h ? M - m_half : m_half;
+  }
   // A strip writes 32 bytes of each output row, a quarter of a 128-byte
   // line.  The strips of a round are mapped so that the 4 strips of each
   // 64-channel line group run on one XCD (workgroup b runs on XCD b % 8),
@@ -704,14 +724,24 @@ static bool launch_decode_mt(const uint8_t* A, const float* sa, const uint8_t* W
   const int pw = (KB + kDecodeWaves - 1) / kDecodeWaves;
   const int nstrips = (int)((N + 15) / 16);
   const int cus = compute_units();
-  const int grid = nstrips < cus ? nstrips : cus;
+  int grid = nstrips < cus ? nstrips : cus;
+  // More than 64 rows: two row ranges of at most 64 (the first a multiple of
+  // 16, the halves as equal as that allows), on pairs of workgroups; needs
+  // a grid of whole groups of 16 and at least one strip per pair.
+  const int m_split = M > 64 ? 2 : 1;
+  const int m_half = m_split == 2 ? (int)std::min<int64_t>(64, ((M + 1) / 2 + 15) / 16 * 16) : (int)M;
+  if (m_split == 2) {
+    grid = std::min(cus, 2 * nstrips) / 16 * 16;
+    if (grid < 16 || M - m_half > 64) return false;
+  }
   const size_t lds = ((size_t)2 * kDecodeWaves * MT * 4 * 64 + (kInt8 ? 0 : (size_t)MT * 16 * KB)) *
                      sizeof(float);
   if (lds + sizeof(DecodeSlot) * kDecodeWaves * kDecodeRing > (size_t)kLdsBytes) return false;
 #define PRR_DECODE_P(PV)                                                                  \
   if (pw <= PV) {                                                                         \
     hipLaunchKernelGGL((gemm_decode_kernel<MT, PV, kInt8>), dim3(grid), dim3(512), lds,   \
-                       stream, A, sa, W, sw, (int)M, (int)N, (int)K, C, nstrips);         \
+                       stream, A, sa, W, sw, (int)M, (int)N, (int)K, C, nstrips, m_split,  \
+                       m_half);                                                           \
     *err = hipGetLastError();                                                             \
     return true;                                                                          \
   }
@@ -820,11 +850,14 @@ bool launch_gemm_decode(const uint8_t* A, const float* sa, const uint8_t* W, con
                         int64_t M, int64_t N, int64_t K, uint16_t* C, hipStream_t stream,
                         hipError_t* err) {
   // 32-bit offsets: a 16-row strip and all of A must stay below 2^31 bytes.
-  // Activations of more than 64 rows do not fit in registers.
+  // Activations of more than 64 rows do not fit in one workgroup's
+  // registers: 65-128 rows take two row ranges on pairs of workgroups.
   // Scale offsets (4 N for INT8, 4 ceil(N/128) K/128 for FP8) are 32-bit too.
-  if (M < 1 || M > 64 || K < kBlock || 128 * K >= 0x7FFFFF00LL || N > 0x1FFFFFF0LL) return false;
+  if (M < 1 || M > 128 || K < kBlock || 128 * K >= 0x7FFFFF00LL || N > 0x1FFFFFF0LL) return false;
+  if (M * K >= 0x7FFFFF00LL) return false;
   if (!kInt8 && 4 * ((N + kBlock - 1) / kBlock) * (K / kBlock) >= 0x7FFFFF00LL) return false;
-  if (!kInt8 && ((M + 15) / 16 * 16) * (K / kBlock) > 8192) return false;   // scales in LDS
+  if (!kInt8 && (std::min<int64_t>(64, (M + 15) / 16 * 16)) * (K / kBlock) > 8192) return false;
+  if (M > 64) return launch_decode_mt<4, kInt8>(A, sa, W, sw, M, N, K, C, stream, err);
   switch ((M + 15) / 16) {
     case 1: return launch_decode_mt<1, kInt8>(A, sa, W, sw, M, N, K, C, stream, err);
     case 2: return launch_decode_mt<2, kInt8>(A, sa, W, sw, M, N, K, C, stream, err);

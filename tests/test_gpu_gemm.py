@@ -95,6 +95,12 @@ GEMM_SHAPES = [(16, 256, 256), (5, 200, 384), (1, 16, 128), (17, 129, 256), (33,
                # long K, few channels (one strip per workgroup, K over 4 waves):
                # every m-tile count, ragged N
                (5, 300, 16384), (33, 1000, 20480), (64, 2000, 12800), (20, 777, 10240),
+               # 65-128 rows: two row ranges on pairs of decode workgroups
+               # (uneven halves, ragged N, a grid below 32 workers, a single
+               # strip that falls back to the many-token kernel, K beyond the
+               # register budget that does too)
+               (65, 1000, 640), (72, 20000, 1024), (100, 3000, 6144), (96, 130, 256),
+               (80, 16, 128), (128, 777, 8192), (113, 5120, 5120),
                # many-token kernel (256 x 256 tiles): odd K-block count over a
                # 3 x 4 tile grid, a single K block over 9 x 2 tiles, 4 x 4 tiles
                (513, 777, 1152), (2304, 512, 128), (1024, 1024, 256)]
