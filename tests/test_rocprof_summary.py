@@ -39,3 +39,20 @@ def test_counters_report_the_copy_calibration(tmp_path):
     out = rs.counter_table(str(tmp_path), "FETCH_SIZE").splitlines()
     assert out[0] == "calibration copy: 262144.0 KiB -> scale 2.0000"
     assert out[-1] == "| `kv_cache_write_kernel` | 2048 | 0 | 24 | 2 | 150.0 |"
+
+
+def test_trace_split_by_dispatch_order(tmp_path):
+    hdr = ["Kernel_Name", "Dispatch_Id", "Start_Timestamp", "End_Timestamp", "LDS_Block_Size",
+           "VGPR_Count", "Workgroup_Size_X", "Grid_Size_X"]
+    k = "void prr::gemm_decode_kernel<4, 4, false>(unsigned char const*)"
+    rows = [[k, 3, 0, 40000, 73728, 96, 512, 131072],     # dispatch order 1, 2, 3, 4
+            [k, 1, 0, 10000, 73728, 96, 512, 131072],
+            ["prr::fp8_act_group_kernel(x)", 2, 0, 5000, 0, 12, 256, 28672],
+            [k, 2, 0, 20000, 73728, 96, 512, 131072],
+            [k, 4, 0, 50000, 73728, 96, 512, 131072]]
+    _write(tmp_path / "run_kernel_trace.csv", hdr, rows)
+    out = rs.trace_table(str(tmp_path), "gemm_decode_kernel=1,2").splitlines()
+    assert out[2] == "| `gemm_decode_kernel #1` | 256 | 73728 | 96 | 1 | 10.00 | 10.00 | 10.00 |"
+    assert out[3] == "| `gemm_decode_kernel #2` | 256 | 73728 | 96 | 2 | 30.00 | 20.00 | 40.00 |"
+    assert out[4] == "| `gemm_decode_kernel #3` | 256 | 73728 | 96 | 1 | 50.00 | 50.00 | 50.00 |"
+    assert out[5].startswith("| `fp8_act_group_kernel` | 112 |")
