@@ -16,7 +16,9 @@
 //  * The weight reaches each wave through its own ring of R LDS slots.  A
 //    slot holds one task, one K block (16 rows x 128 bytes) of one strip,
 //    written by two direct-to-LDS buffer loads of 8 whole 128-byte rows
-//    (full cache lines), plus a 4-byte load of the task's weight scale
+//    (full cache lines, non-temporal: the weight is read once, and the L2
+//    is better spent on the activations and the partly written output
+//    lines), plus a 4-byte load of the task's weight scale
 //    (FP8; INT8: the strip's 16 channel scales, with its first task).  The
 //    wave keeps R - 1 tasks in flight: it starts task t + R - 1, waits for
 //    task t, reads the fragment from LDS and runs its MFMAs.  No other wave
@@ -145,8 +147,8 @@ __device__ __forceinline__ void decode_segment(
     const bool jl = j < pw;
     const int kofs = (kbf + kb0 + j) * kBlock;
     DecodeSlot& sl = ring[wave][t % R];
-    dma_b128(rw, lds_addr(sl.w), jl ? lofs0 + kofs : kOutOfRange, 0);
-    dma_b128(rw, lds_addr(sl.w + 1024), jl ? lofs1 + kofs : kOutOfRange, 0);
+    dma_b128_stream(rw, lds_addr(sl.w), jl ? lofs0 + kofs : kOutOfRange, 0);
+    dma_b128_stream(rw, lds_addr(sl.w + 1024), jl ? lofs1 + kofs : kOutOfRange, 0);
     int vs;
     if constexpr (kInt8)
       vs = (live && j == 0 && lane < 16 && n0 + lane < N) ? (n0 + lane) * 4 : kOutOfRange;

@@ -123,6 +123,19 @@ __device__ __forceinline__ void dma_b128(v4i rsrc, uint32_t lds, int voff, int s
                : "memory", "m0");
 }
 
+// The same for data read exactly once (the decode GEMM's weight stream),
+// marked non-temporal ("nt"): the L2 keeps it as streaming data, to be
+// replaced first, so the lines the kernel reuses (activations, partial
+// output lines that later strips of the same XCD complete) stay resident.
+// Measured on the decode GEMM with cold weights: 7-9% faster at 32-64
+// rows and 2-7% at one row; the scope bits (sc0, sc1) made no difference.
+__device__ __forceinline__ void dma_b128_stream(v4i rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ void dma_b32(v4i rsrc, uint32_t lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
