@@ -18,8 +18,9 @@ namespace prr {
 // steps, so every lane holds 64 bf16 in 8 x 16-byte registers.
 // ---------------------------------------------------------------------------
 // Encode the 8 chunks a lane holds and store them (block-uniform class:
-// kClass 0 = all-zero block, 1 = ordinary, 2 = tiny scale).
-template <int kClass>
+// kClass 0 = all-zero block, 1 = ordinary, 2 = tiny scale; kStream:
+// non-temporal code stores, see store_codes8).
+template <int kClass, bool kStream>
 __device__ __forceinline__ void encode_block_rows(const uint4 (&v)[8], const BlockDiv& d,
                                                   bool full, uint8_t* __restrict__ q, int64_t N,
                                                   int64_t K, int64_t ldq, int64_t row0, int seg,
@@ -31,7 +32,7 @@ __device__ __forceinline__ void encode_block_rows(const uint4 (&v)[8], const Blo
     if constexpr (kClass == 0) c = e4m3_zero_chunk(v[i]);
     else c = e4m3_chunk<kClass == 2>(v[i], d);
     if (full) {
-      *reinterpret_cast<uint2*>(q + r * ldq + col) = c;
+      store_codes8<kStream>(q + r * ldq + col, c);
     } else {
       const uint32_t cw[2] = {c.x, c.y};
 #pragma unroll
@@ -44,6 +45,7 @@ __device__ __forceinline__ void encode_block_rows(const uint4 (&v)[8], const Blo
 // Block (bi, bj) of an N x K matrix with row strides ldw (input, elements),
 // ldq (codes, bytes) and lds (scales, floats); the whole-weight call has
 // ldw = ldq = K and lds = nbk.  Called by all 256 threads of a workgroup.
+template <bool kStream>
 __device__ __forceinline__ void fp8_weight_block(const uint16_t* __restrict__ w, int64_t N,
                                                  int64_t K, int64_t ldw, uint8_t* __restrict__ q,
                                                  int64_t ldq, float* __restrict__ scale,
@@ -96,9 +98,9 @@ __device__ __forceinline__ void fp8_weight_block(const uint16_t* __restrict__ w,
   if (tid == 0) scale[(int64_t)bi * lds + bj] = s;
 
   const BlockDiv d = block_div(s);
-  if (s == 0.0f) encode_block_rows<0>(v, d, full, q, N, K, ldq, row0, seg, col);
-  else if (d.tiny) encode_block_rows<2>(v, d, full, q, N, K, ldq, row0, seg, col);
-  else encode_block_rows<1>(v, d, full, q, N, K, ldq, row0, seg, col);
+  if (s == 0.0f) encode_block_rows<0, kStream>(v, d, full, q, N, K, ldq, row0, seg, col);
+  else if (d.tiny) encode_block_rows<2, kStream>(v, d, full, q, N, K, ldq, row0, seg, col);
+  else encode_block_rows<1, kStream>(v, d, full, q, N, K, ldq, row0, seg, col);
 }
 
 __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
     int64_t ldq, float* __restrict__ scale, int64_t lds, int nbk) {
   const int bi = blockIdx.x / nbk;
   const int bj = blockIdx.x - bi * nbk;
-  fp8_weight_block(w, N, K, ldw, q, ldq, scale, lds, bi, bj);
+  fp8_weight_block<false>(w, N, K, ldw, q, ldq, scale, lds, bi, bj);
 }
 
 // Several weights in one grid (a layer stack re-quantized after a training
@@ -115,7 +117,8 @@ __global__ __launch_bounds__(256) void fp8_weight_block_kernel(
 // at most kMaxWeightJobs entries, in the kernel arguments).  One launch
 // instead of one per weight: small weights (a 10 MB k or v projection) no
 // longer pay a launch ramp and drain of their own, and their blocks fill
-// the machine beside the large ones.
+// the machine beside the large ones.  A stack's codes outgrow the
+// last-level cache, so they are stored non-temporal.
 __global__ __launch_bounds__(256) void fp8_weight_block_multi_kernel(WeightJobs jobs) {
   const int b = blockIdx.x;
   int j = 0;
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(256) void fp8_weight_block_multi_kernel(WeightJobs 
   const int nbk = jobs.units_per_row[j];
   const int bi = local / nbk, bj = local - bi * nbk;
   const int64_t K = jobs.K[j];
-  fp8_weight_block(jobs.w[j], jobs.N[j], K, K, static_cast<uint8_t*>(jobs.q[j]), K,
+  fp8_weight_block<true>(jobs.w[j], jobs.N[j], K, K, static_cast<uint8_t*>(jobs.q[j]), K,
                    jobs.scale[j], nbk, bi, bj);
 }
 

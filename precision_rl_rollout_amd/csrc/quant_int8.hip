@@ -23,20 +23,21 @@ __device__ __forceinline__ uint2 int8_chunk_class(uint4 w, const BlockDiv& d) {
   else return int8_chunk<kClass == 2>(w, d);
 }
 
-template <int kClass, int kLanes>
+template <int kClass, int kLanes, bool kStream>
 __device__ __forceinline__ void int8_store_row(const uint4 (&v)[kMaxChunks], const BlockDiv& d,
                                                uint8_t* __restrict__ dst, int64_t chunks,
                                                int lane) {
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int64_t c = (int64_t)i * kLanes + lane;
-    if (c < chunks) *reinterpret_cast<uint2*>(dst + c * 8) = int8_chunk_class<kClass>(v[i], d);
+    if (c < chunks) store_codes8<kStream>(dst + c * 8, int8_chunk_class<kClass>(v[i], d));
   }
 }
 
 // Register-resident row: kLanes lanes (64: a wave, 256: the workgroup) per
 // row; work unit u is rows 256 / kLanes u ...  Called by all 256 threads.
-template <int kLanes>
+// kStream: non-temporal code stores (store_codes8).
+template <int kLanes, bool kStream>
 __device__ __forceinline__ void int8_rows_resident(const uint16_t* __restrict__ x, int64_t R,
                                                    int64_t K, int8_t* __restrict__ q,
                                                    float* __restrict__ scale, int64_t unit) {
@@ -71,20 +72,21 @@ __device__ __forceinline__ void int8_rows_resident(const uint16_t* __restrict__ 
   if (lane == 0) scale[row] = s;
   const BlockDiv d = block_div(s);
   uint8_t* dst = reinterpret_cast<uint8_t*>(q) + row * K;
-  if (s == 0.0f) int8_store_row<0, kLanes>(v, d, dst, chunks, lane);
-  else if (d.tiny) int8_store_row<2, kLanes>(v, d, dst, chunks, lane);
-  else int8_store_row<1, kLanes>(v, d, dst, chunks, lane);
+  if (s == 0.0f) int8_store_row<0, kLanes, kStream>(v, d, dst, chunks, lane);
+  else if (d.tiny) int8_store_row<2, kLanes, kStream>(v, d, dst, chunks, lane);
+  else int8_store_row<1, kLanes, kStream>(v, d, dst, chunks, lane);
 }
 
 template <int kLanes>
 __global__ __launch_bounds__(256) void int8_row_resident_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t K, int8_t* __restrict__ q,
     float* __restrict__ scale) {
-  int8_rows_resident<kLanes>(x, R, K, q, scale, blockIdx.x);
+  int8_rows_resident<kLanes, false>(x, R, K, q, scale, blockIdx.x);
 }
 
 // Any K: a workgroup per row, two passes; 16-byte chunks when K % 8 == 0,
 // single elements otherwise.  Called by all 256 threads.
+template <bool kStream>
 __device__ __forceinline__ void int8_row_twopass(const uint16_t* __restrict__ x, int64_t K,
                                                  int8_t* __restrict__ q,
                                                  float* __restrict__ scale, int64_t row) {
@@ -116,7 +118,7 @@ __device__ __forceinline__ void int8_row_twopass(const uint16_t* __restrict__ x,
   if (vec) {
     for (int64_t c = tid; c < K / 8; c += 256) {
       const uint4 v = *reinterpret_cast<const uint4*>(src + c * 8);
-      *reinterpret_cast<uint2*>(dst + c * 8) = int8_chunk_any(v, s, d);
+      store_codes8<kStream>(dst + c * 8, int8_chunk_any(v, s, d));
     }
   } else {
     for (int64_t k = tid; k < K; k += 256) {
@@ -131,7 +133,7 @@ __device__ __forceinline__ void int8_row_twopass(const uint16_t* __restrict__ x,
 __global__ __launch_bounds__(256) void int8_row_twopass_kernel(
     const uint16_t* __restrict__ x, int64_t K, int8_t* __restrict__ q,
     float* __restrict__ scale) {
-  int8_row_twopass(x, K, q, scale, blockIdx.x);
+  int8_row_twopass<false>(x, K, q, scale, blockIdx.x);
 }
 
 // Row classes: 0 = a wave per row (4 rows per work unit), 1 = a workgroup
@@ -146,7 +148,8 @@ int int8_rows_per_unit(int cls) { return cls == 0 ? 4 : 1; }
 
 // Several weights in one grid, as the FP8 multi-weight kernel: workgroup b
 // takes work unit b of the job whose range holds it; the job's row class is
-// uniform, so each workgroup runs one of the three row paths.
+// uniform, so each workgroup runs one of the three row paths.  Codes are
+// stored non-temporal, as in the FP8 multi-weight kernel.
 __global__ __launch_bounds__(256) void int8_row_multi_kernel(WeightJobs jobs) {
   const int b = blockIdx.x;
   int j = 0;
@@ -156,9 +159,12 @@ __global__ __launch_bounds__(256) void int8_row_multi_kernel(WeightJobs jobs) {
   const int64_t unit = b - jobs.first[j];
   const int cls = jobs.units_per_row[j];
   int8_t* q = static_cast<int8_t*>(jobs.q[j]);
-  if (cls == 0) int8_rows_resident<64>(jobs.w[j], jobs.N[j], jobs.K[j], q, jobs.scale[j], unit);
-  else if (cls == 1) int8_rows_resident<256>(jobs.w[j], jobs.N[j], jobs.K[j], q, jobs.scale[j], unit);
-  else int8_row_twopass(jobs.w[j], jobs.K[j], q, jobs.scale[j], unit);
+  if (cls == 0)
+    int8_rows_resident<64, true>(jobs.w[j], jobs.N[j], jobs.K[j], q, jobs.scale[j], unit);
+  else if (cls == 1)
+    int8_rows_resident<256, true>(jobs.w[j], jobs.N[j], jobs.K[j], q, jobs.scale[j], unit);
+  else
+    int8_row_twopass<true>(jobs.w[j], jobs.K[j], q, jobs.scale[j], unit);
 }
 
 hipError_t launch_int8_weight_channel_quant_multi(const WeightJobs& jobs, hipStream_t stream) {
