@@ -714,8 +714,8 @@ int compute_units() {
 
 // Smallest P (K blocks per wave) that covers the wave's piece.  Resident
 // activations take MT * P * 8 VGPRs.  Every instance compiles without spills
-// except MT 4, P 6 (M 33-64 with K 5121-6144), which needs 8 (FP8) or 32
-// (INT8) bytes of scratch per lane: correct, somewhat slower; with a
+// except MT 4, P 6 (M 33-64, or a half of 65-128 rows, with K 5121-6144),
+// which needs 8 (FP8) or 36 (INT8) bytes of scratch per lane: correct, somewhat slower; with a
 // workspace those shapes run the split-K kernel only when the layer is
 // narrow.  K up to 8192 for M <= 32, 6144 for M <= 64.
 template <int MT, bool kInt8>
@@ -870,7 +870,7 @@ bool launch_gemm_decode(const uint8_t* A, const float* sa, const uint8_t* W, con
 }
 
 // As launch_decode_mt; the MT 4 instances with P 5 and 6 (more than 32 rows
-// for some expert, K 4097-6144) spill 28 and 184 bytes per lane.
+// for some expert, K 4097-6144) spill 36 and 208 bytes per lane.
 template <int MT>
 static bool launch_grouped_mt(const uint8_t* A, const float* sa, const uint8_t* W,
                               const float* sw, const int64_t* offsets, int64_t E, int64_t M,
