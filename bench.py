@@ -376,6 +376,19 @@ def cpu_cores():
     return {"blas_threads": cpu_threads(), "os_cpu_count": os.cpu_count()}
 
 
+def _repeat_timed(fn, min_seconds=8.0, max_reps=50):
+    """Run fn until min_seconds of it have been timed (at least twice):
+    (repeats, total seconds).  One call of the oracle GEMM takes 0.5-2 s,
+    short enough for the host's timer noise to show."""
+    reps, total = 0, 0.0
+    while reps < 2 or (total < min_seconds and reps < max_reps):
+        t0 = time.perf_counter()
+        fn()
+        total += time.perf_counter() - t0
+        reps += 1
+    return reps, total
+
+
 def cpu_baseline_decode_gemm(W, gbytes):
     """The oracle, as it stands, on the same GEMM: the FP8 GEMM of the full
     A [64, 3584] against the full FP8 weight [37888, 3584] (fp64 BLAS over the
@@ -386,15 +399,13 @@ def cpu_baseline_decode_gemm(W, gbytes):
     p = W.gemm_problem(M, N, K, True, seed=0)
     wq, sw = quant.fp8_weight_block_quant(p["Wt"])
     aq, sa = quant.fp8_act_token_quant(p["A"])
-    t0 = time.perf_counter()
-    gemm.round_bf16(gemm.w8a8_block_gemm(aq, sa, wq, sw))
-    dt = time.perf_counter() - t0
+    reps, total = _repeat_timed(lambda: gemm.round_bf16(gemm.w8a8_block_gemm(aq, sa, wq, sw)))
     cores = cpu_cores()
-    return {"value": round(gbytes / dt / 1e9, 4), "unit": "GB/s",
+    return {"value": round(reps * gbytes / total / 1e9, 4), "unit": "GB/s",
             "cores": cores["blas_threads"], "os_cpu_count": cores["os_cpu_count"],
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "the whole GEMM: A [64, 3584] x Wt [37888, 3584] FP8 codes and scales, "
-                      "rounded to bf16; fp64 BLAS with the host's BLAS threads"}
+            "kind": "oracle", "seconds": round(total, 2), "repeats": reps,
+            "sample": f"the whole GEMM, {reps} times: A [64, 3584] x Wt [37888, 3584] FP8 "
+                      "codes and scales, rounded to bf16; fp64 BLAS with the host's BLAS threads"}
 
 
 def cpu_baseline_prefill(W, rows=512):
@@ -407,15 +418,13 @@ def cpu_baseline_prefill(W, rows=512):
     p = W.gemm_problem(8192, N, K, True, seed=0)
     wq, sw = quant.fp8_weight_block_quant(p["Wt"])
     aq, sa = quant.fp8_act_token_quant(p["A"][:rows])
-    t0 = time.perf_counter()
-    gemm.round_bf16(gemm.w8a8_block_gemm(aq, sa, wq, sw))
-    dt = time.perf_counter() - t0
+    reps, total = _repeat_timed(lambda: gemm.round_bf16(gemm.w8a8_block_gemm(aq, sa, wq, sw)))
     cores = cpu_cores()
-    return {"value": round(2 * rows * N * K / dt / 1e12, 5), "unit": "TFLOP/s",
+    return {"value": round(reps * 2 * rows * N * K / total / 1e12, 5), "unit": "TFLOP/s",
             "cores": cores["blas_threads"], "os_cpu_count": cores["os_cpu_count"],
-            "kind": "oracle", "seconds": round(dt, 2),
+            "kind": "oracle", "seconds": round(total, 2), "repeats": reps,
             "sample": f"the first {rows} of 8192 token rows against the full weight "
-                      f"[27648, 5120]; fp64 BLAS with the host's BLAS threads"}
+                      f"[27648, 5120], {reps} times; fp64 BLAS with the host's BLAS threads"}
 
 
 def _cold_copies(torch, make, nbytes, budget=600 << 20):
