@@ -329,6 +329,20 @@ __device__ __forceinline__ void decode_segment(
     store4(C, M, N, m, n, v);
   };
 
+  // FP8: the activation scales of the wave's own K blocks are the same for
+  // every strip; held in registers (MT x P of them) they save an LDS read
+  // per m-tile and task (1.5% at 64 rows).  Not where the resident
+  // activations leave no room: at four m-tiles with more than 4 blocks a
+  // wave, the grouped kernel spilled 96 bytes a lane instead of 36.
+  constexpr bool kScaleRegs = !kInt8 && (MT < 4 || P <= 4);
+  float sareg[MT][P];
+  if constexpr (kScaleRegs) {
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        sareg[mt][j] = lsa[min(kb0 + j, KB - 1) * kRows + mt * 16 + r16];
+  }
   for (int i = 0; i < my_n; ++i) {
     float accf[MT][4];
     v4i acci[MT];
@@ -374,7 +388,10 @@ __device__ __forceinline__ void decode_segment(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const v4f p = mfma_fp8(wf, afr[mt][j]);
-          const float sc = lsa[kb * kRows + mt * 16 + r16 + opaque0] * swv;
+          float sa_v;
+          if constexpr (kScaleRegs) sa_v = sareg[mt][j];
+          else sa_v = lsa[kb * kRows + mt * 16 + r16 + opaque0];
+          const float sc = sa_v * swv;
 #pragma unroll
           for (int r = 0; r < 4; ++r) accf[mt][r] = fmaf(p[r], sc, accf[mt][r]);
         }
