@@ -108,11 +108,15 @@ def counter_table(directory: str, counter: str, split: str | None = None) -> str
                 items.append((_key(row), float(row["Counter_Value"]), _order(row)))
     groups = _split_groups(items, split)
     lines = []
+    # FETCH_SIZE / WRITE_SIZE are in KiB; other counters (cycles, the
+    # percent of a derived metric such as MfmaUtil) carry their own unit.
+    kib = counter in ("FETCH_SIZE", "WRITE_SIZE")
     for (name, wgs, _lds, _vgpr), v in groups:
-        if name == "__amd_rocclr_copyBuffer" and wgs == 256:
+        if kib and name == "__amd_rocclr_copyBuffer" and wgs == 256:
             lines.append(f"calibration copy: {statistics.mean(v):.1f} KiB -> scale "
                          f"{COPY_KIB / statistics.mean(v):.4f}")
-    lines += [f"| kernel | workgroups | LDS bytes | VGPRs | dispatches | {counter} KiB (mean) |",
+    unit = " KiB" if kib else ""
+    lines += [f"| kernel | workgroups | LDS bytes | VGPRs | dispatches | {counter}{unit} (mean) |",
               "|---|---:|---:|---:|---:|---:|"]
     for (name, wgs, lds, vgpr), v in groups:
         lines.append(f"| `{name}` | {wgs} | {lds} | {vgpr} | {len(v)} | {statistics.mean(v):.1f} |")

@@ -56,3 +56,16 @@ def test_trace_split_by_dispatch_order(tmp_path):
     assert out[3] == "| `gemm_decode_kernel #2` | 256 | 73728 | 96 | 2 | 30.00 | 20.00 | 40.00 |"
     assert out[4] == "| `gemm_decode_kernel #3` | 256 | 73728 | 96 | 1 | 50.00 | 50.00 | 50.00 |"
     assert out[5].startswith("| `fp8_act_group_kernel` | 112 |")
+
+
+def test_counters_other_than_bytes_carry_no_kib_unit(tmp_path):
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value", "Grid_Size", "Workgroup_Size",
+           "LDS_Block_Size", "VGPR_Count"]
+    rows = [["__amd_rocclr_copyBuffer", "MfmaUtil", 0.0, 65536, 256, 0, 8],
+            ["prr::gemm_prefill_kernel(x)", "MfmaUtil", 50.0, 1703936, 512, 135168, 124],
+            ["prr::gemm_prefill_kernel(x)", "MfmaUtil", 55.0, 1703936, 512, 135168, 124]]
+    _write(tmp_path / "run_counter_collection.csv", hdr, rows)
+    out = rs.counter_table(str(tmp_path), "MfmaUtil").splitlines()
+    assert not any(line.startswith("calibration copy") for line in out)
+    assert out[0] == "| kernel | workgroups | LDS bytes | VGPRs | dispatches | MfmaUtil (mean) |"
+    assert out[-1] == "| `gemm_prefill_kernel` | 3328 | 135168 | 124 | 2 | 52.5 |"
