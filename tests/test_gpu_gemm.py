@@ -88,9 +88,8 @@ GEMM_SHAPES = [(16, 256, 256), (5, 200, 384), (1, 16, 128), (17, 129, 256), (33,
                # decode kernel: 5, 6 and 8 K blocks per wave; 601 strips, so a
                # workgroup streams several strips through its LDS ring
                (64, 640, 5120), (48, 500, 6144), (24, 300, 8192), (40, 9607, 1024),
-               # decode kernel with whole rounds of 4-strip quads (staged output):
-               # a ragged strip inside the last quad, N not a multiple of 8
-               # (element-wise row segments), quads followed by single strips
+               # decode kernel over ~4 to 80 strips per workgroup: a ragged last
+               # strip, N not a multiple of 8 (element-wise output stores)
                (33, 16376, 256), (64, 16379, 384), (17, 20000, 512),
                # long K, few channels (one strip per workgroup, K over 4 waves):
                # every m-tile count, ragged N
