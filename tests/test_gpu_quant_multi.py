@@ -60,3 +60,19 @@ def test_multi_empty_and_repeat():
     a = binding.fp8_weight_block_quant_multi([w, w])
     torch.cuda.synchronize()
     assert torch.equal(a[0][0], a[1][0]) and torch.equal(a[0][1], a[1][1])
+
+
+def test_multi_at_the_job_limit():
+    # As many weights as one launch takes (the job table travels in the
+    # kernel arguments), the last job's blocks at the end of the grid.
+    shapes = [(64 + 37 * i, 128 + 61 * i) for i in range(binding.MAX_WEIGHT_JOBS)]
+    ws = [workloads.weight(N, K, seed=100 + i) for i, (N, K) in enumerate(shapes)]
+    devs = [bits_to_dev(w) for w in ws]
+    announce(f"fp8/int8 multi-weight quant, {len(ws)} weights (the job limit)")
+    got8 = binding.fp8_weight_block_quant_multi(devs)
+    goti = binding.int8_weight_channel_quant_multi(devs)
+    for w, (q8, s8), (qi, si), shape in zip(ws, got8, goti, shapes):
+        rc, rs = quant.fp8_weight_block_quant(w)
+        assert np.array_equal(host(q8), rc) and _same_bits(host(s8), rs), ("fp8", shape)
+        rc, rs = quant.int8_weight_channel_quant(w)
+        assert np.array_equal(host(qi), rc) and _same_bits(host(si), rs), ("int8", shape)
