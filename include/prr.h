@@ -245,12 +245,17 @@ prr_status w8a8_int8_channel_gemm(const int8_t* a_i8, const float* a_scale,
  * decode-sized batches (M <= 64) of layers with few output channels or long
  * K (e.g. a down projection, N 5120 x K 27648), where one workgroup per
  * 16-channel strip over all of K leaves CUs idle or cannot hold the
- * activations.  With the workspace the call splits K into S slices, writes
- * fp32 partial sums (INT8: int32 accumulators) to it and adds the slices in
- * a fixed order (bitwise repeatable; same definition and tolerance as the
- * one-pass call).  Callers that cannot provide one use the calls above.
+ * activations, and for many-token batches (M > 128) of long-K layers
+ * (K >= 8192) whose output tiles leave a last, partial round on the CUs.
+ * With the workspace the call splits K into S slices (for many tokens,
+ * those of the last round's tile columns only), writes fp32 partial sums
+ * (INT8: int32 accumulators) to it and adds the slices in a fixed order
+ * (bitwise repeatable; same definition and tolerance as the one-pass call;
+ * INT8 results are identical to the one-pass call's).  Callers that cannot
+ * provide one use the calls above.
  *   w8a8_gemm_workspace_size: *bytes = the workspace the _ws calls use for
- *       this shape on the current device (S x M x N x 4; 0 = no split, the
+ *       this shape on the current device (S x M x N x 4 for decode batches,
+ *       S x M x the split columns x 4 for many tokens; 0 = no split, the
  *       _ws call runs the one-pass kernels).  Same for FP8 and INT8.
  *   workspace: device memory, 16-byte aligned, not shared with a call in
  *       flight on another stream; NULL or workspace_bytes below the size

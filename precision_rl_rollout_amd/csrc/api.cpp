@@ -252,7 +252,9 @@ prr_status w8a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t* by
   if (M == 0 || N == 0 || K == 0) return PRR_OK;
   PRR_TRY(check_device());
   prr::SplitPlan plan;
+  prr::PrefillTailPlan tail;
   if (prr::splitk_plan(M, N, K, &plan)) *bytes = plan.bytes;
+  else if (prr::prefill_tail_plan(M, N, K, &tail)) *bytes = tail.bytes;
   return PRR_OK;
 }
 
@@ -269,6 +271,10 @@ prr_status w8a8_block_gemm_ws(const uint8_t* a_fp8, const float* a_scale, const 
   if (K > 0 && prr::launch_gemm_decode_splitk<false>(a_fp8, a_scale, w_fp8, w_scale, M, N, K,
                                                       static_cast<float*>(workspace),
                                                       workspace_bytes, c_bf16, stream, &err))
+    return from_hip(err);
+  if (K > 0 && prr::launch_gemm_prefill_ws<false>(a_fp8, a_scale, w_fp8, w_scale, M, N, K, c_bf16,
+                                                   static_cast<float*>(workspace),
+                                                   workspace_bytes, stream, &err))
     return from_hip(err);
   return from_hip(
       prr::launch_w8a8_block_gemm(a_fp8, a_scale, w_fp8, w_scale, M, N, K, c_bf16, stream));
@@ -308,6 +314,11 @@ prr_status w8a8_int8_channel_gemm_ws(const int8_t* a_i8, const float* a_scale,
                    reinterpret_cast<const uint8_t*>(a_i8), a_scale,
                    reinterpret_cast<const uint8_t*>(w_i8), w_scale, M, N, K,
                    static_cast<float*>(workspace), workspace_bytes, c_bf16, stream, &err))
+    return from_hip(err);
+  if (K > 0 && prr::launch_gemm_prefill_ws<true>(
+                   reinterpret_cast<const uint8_t*>(a_i8), a_scale,
+                   reinterpret_cast<const uint8_t*>(w_i8), w_scale, M, N, K, c_bf16,
+                   static_cast<float*>(workspace), workspace_bytes, stream, &err))
     return from_hip(err);
   return from_hip(
       prr::launch_w8a8_int8_channel_gemm(a_i8, a_scale, w_i8, w_scale, M, N, K, c_bf16, stream));

@@ -19,6 +19,8 @@
 // LDS rows are 128 bytes; 16-byte chunk c of row r is stored at chunk
 // c ^ ((r >> 1) & 7): the 16 rows one fragment read touches then fall on 16
 // distinct 16-byte bank groups.
+#include <algorithm>
+
 #include "launch.h"
 #include "mfma.h"
 
@@ -67,15 +69,15 @@ constexpr int kDmaPerStage = 4 + TN / 64 + (kInt8 ? 0 : 1);
 
 // DMA of K block kb into a stage: both tiles, and (FP8) the activation
 // scales (waves 0..3, 64 rows each) and the weight-block scales (wave 4).
-// A block at or past KB loads nothing (every offset out of range, no memory
-// traffic) but still issues the same instructions, so the wait counts stay
-// the same.  Branch-free: a branch here makes the register allocator
+// A block at or past kb_end loads nothing (every offset out of range, no
+// memory traffic) but still issues the same instructions, so the wait counts
+// stay the same.  KB is the row length of the scale arrays.  Branch-free: a branch here makes the register allocator
 // shuffle the accumulators around the join.
 template <bool kInt8, int TN>
 __device__ __forceinline__ void stage_load(Stage<TN>& st, v4i ra, v4i rw, v4i rsa, v4i rsw,
-                                           DmaOffsets da, DmaOffsets dw, int K, int KB, int kb,
-                                           int wave, int lane) {
-  const bool live = kb < KB;
+                                           DmaOffsets da, DmaOffsets dw, int K, int KB,
+                                           int kb_end, int kb, int wave, int lane) {
+  const bool live = kb < kb_end;
   const int soff = live ? kb * kBlock : 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -203,7 +205,8 @@ template <bool kInt8, int TN>
 __device__ __forceinline__ void k_block(Stage<TN>& cur, const Stage<TN>& nxt,
                                         Acc<kInt8, TN / 32>& acc, Front& f, Pending& pend, v4i ra,
                                         v4i rw, v4i rsa, v4i rsw, DmaOffsets da, DmaOffsets dw,
-                                        int K, int KB, int kb, int wave, int wm, int wn, int lane,
+                                        int K, int KB, int kb_end, int kb, int wave, int wm,
+                                        int wn, int lane,
                                         FragOffsets o) {
   constexpr int NJ = TN / 32, kWaveN = TN / 2;
 #pragma unroll
@@ -228,7 +231,7 @@ __device__ __forceinline__ void k_block(Stage<TN>& cur, const Stage<TN>& nxt,
     if (j == NJ - 2) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's loads of block kb + 1 landed
       lds_barrier();                             // everyone's have; nobody reads `cur` any more
-      stage_load<kInt8, TN>(cur, ra, rw, rsa, rsw, da, dw, K, KB, kb + 2, wave, lane);
+      stage_load<kInt8, TN>(cur, ra, rw, rsa, rsw, da, dw, K, KB, kb_end, kb + 2, wave, lane);
     }
     f.wf = f.wf1;
     f.wf1 = w2;
@@ -263,11 +266,15 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
 }
 
 // Output columns [n_base, N) in tiles_m x tiles_n tiles of 256 x TN.
-template <bool kInt8, int TN>
+// kPartial: workgroup (b, s) of a grid with gridDim.y = S slices takes K
+// blocks [s KB / S, (s + 1) KB / S) of tile b and writes its fp32 partial
+// sums (FP8: scaled; INT8: the int32 accumulators, bit-cast) to slab s of
+// ws, [S][M][N - n_base], instead of C; a second kernel adds the slabs.
+template <bool kInt8, int TN, bool kPartial = false>
 __global__ __launch_bounds__(512) void gemm_prefill_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ C, int n_base,
-    int tiles_m, int tiles_n) {
+    int tiles_m, int tiles_n, float* __restrict__ ws) {
   constexpr int NJ = TN / 32, kWaveN = TN / 2;
   // Two stages as two objects, so the compiler can tell that the fragment
   // reads of one stage do not wait for the loads into the other.
@@ -281,6 +288,9 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
   const int m0 = tm * kTileM, n0 = n_base + tn * TN;
   const int KB = K / kBlock;
   const int rows_a = min(M - m0, kTileM), rows_w = min(N - n0, TN);
+  const int n_slices = kPartial ? (int)gridDim.y : 1, slice = kPartial ? (int)blockIdx.y : 0;
+  const int kb_lo = (int)((int64_t)slice * KB / n_slices);
+  const int kb_hi = (int)((int64_t)(slice + 1) * KB / n_slices);
 
   // Every buffer range ends at the tile's last valid row, so rows past M or
   // N (offsets at or beyond it) read zeros.
@@ -301,8 +311,8 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc.v[j][i][r] = 0;
 
-  stage_load<kInt8, TN>(st0, ra, rw, rsa, rsw, da, dw, K, KB, 0, wave, lane);
-  stage_load<kInt8, TN>(st1, ra, rw, rsa, rsw, da, dw, K, KB, 1, wave, lane);
+  stage_load<kInt8, TN>(st0, ra, rw, rsa, rsw, da, dw, K, KB, kb_hi, kb_lo, wave, lane);
+  stage_load<kInt8, TN>(st1, ra, rw, rsa, rsw, da, dw, K, KB, kb_hi, kb_lo + 1, wave, lane);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerStage<kInt8, TN>));   // block 0 landed
   lds_barrier();
   Front f;
@@ -315,16 +325,16 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
   }
   // K blocks in pairs (stage 0, stage 1), then an odd last block; one exit
   // keeps the accumulators in place across iterations.
-  int kb = 0;
-  for (; kb + 2 <= KB; kb += 2) {
-    k_block<kInt8, TN>(st0, st1, acc, f, pend, ra, rw, rsa, rsw, da, dw, K, KB, kb, wave, wm, wn,
-                       lane, fo);
-    k_block<kInt8, TN>(st1, st0, acc, f, pend, ra, rw, rsa, rsw, da, dw, K, KB, kb + 1, wave, wm,
-                       wn, lane, fo);
+  int kb = kb_lo;
+  for (; kb + 2 <= kb_hi; kb += 2) {
+    k_block<kInt8, TN>(st0, st1, acc, f, pend, ra, rw, rsa, rsw, da, dw, K, KB, kb_hi, kb, wave,
+                       wm, wn, lane, fo);
+    k_block<kInt8, TN>(st1, st0, acc, f, pend, ra, rw, rsa, rsw, da, dw, K, KB, kb_hi, kb + 1,
+                       wave, wm, wn, lane, fo);
   }
-  if (kb < KB)
-    k_block<kInt8, TN>(st0, st1, acc, f, pend, ra, rw, rsa, rsw, da, dw, K, KB, kb, wave, wm, wn,
-                       lane, fo);
+  if (kb < kb_hi)
+    k_block<kInt8, TN>(st0, st1, acc, f, pend, ra, rw, rsa, rsw, da, dw, K, KB, kb_hi, kb, wave,
+                       wm, wn, lane, fo);
   if constexpr (!kInt8) {   // the last region's products
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -335,10 +345,41 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
   // Every load (the trailing ones are out of range) has landed and every
   // wave is done with the stages before they hold the output tile.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  const int r16 = lane & 15, g = lane >> 4;
+  if constexpr (kPartial) {
+    // The partial sums, 16 bytes (4 columns of one row) a lane and
+    // fragment, to slab `slice` [M][ncols] of the workspace.
+    const int64_t ncols = N - n_base;
+    float* slab = ws + (int64_t)slice * M * ncols;
+    const bool vec = (ncols & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + wm * 64 + i * 16 + r16;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t nl = (int64_t)(n0 - n_base) + wn * kWaveN + j * 16 + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (kInt8) v[r] = __int_as_float(acc.v[j][i][r]);
+          else v[r] = acc.v[j][i][r];
+        }
+        float* dst = slab + m * ncols + nl;
+        if (vec && nl + 4 <= ncols) {
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (nl + r < ncols) dst[r] = v[r];
+        }
+      }
+    }
+    return;
+  }
   lds_barrier();
 
   // Output tile -> bf16 in LDS -> 16-byte row-contiguous stores.
-  const int r16 = lane & 15, g = lane >> 4;
   uint8_t* const lds0 = reinterpret_cast<uint8_t*>(&st0);   // 128 rows of 2 TN bytes
   uint8_t* const lds1 = reinterpret_cast<uint8_t*>(&st1);   // fit in each stage
   uint8_t* half = wm < 2 ? lds0 : lds1;
@@ -391,6 +432,48 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
   }
 }
 
+// C[:, n_base:] = bf16 of the S partial slabs [S][M][ncols] added in slab
+// order (INT8: exactly, then sa[m] sw[n], as the one-pass epilogue does).
+// A thread takes 4 consecutive columns of one row (16-byte slab reads when
+// ncols % 4 == 0, element by element otherwise).
+template <bool kInt8>
+__global__ __launch_bounds__(256) void gemm_prefill_tail_reduce_kernel(
+    const float* __restrict__ ws, int S, int64_t M, int64_t N, int64_t n_base,
+    const float* __restrict__ sa, const float* __restrict__ sw, uint16_t* __restrict__ C) {
+  const int64_t ncols = N - n_base, q4 = (ncols + 3) / 4;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= M * q4) return;
+  const int64_t m = t / q4, c0 = (t - m * q4) * 4;
+  const int64_t MN = M * ncols;
+  const float* src = ws + m * ncols + c0;
+  float f[4] = {0.f, 0.f, 0.f, 0.f};
+  int32_t iacc[4] = {0, 0, 0, 0};
+  const bool vec = (ncols & 3) == 0;
+  for (int s = 0; s < S; ++s) {
+    float v[4];
+    if (vec) {
+      const float4 x = *reinterpret_cast<const float4*>(src + s * MN);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = c0 + r < ncols ? src[s * MN + r] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (kInt8) iacc[r] += __float_as_int(v[r]);
+      else f[r] += v[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t n = n_base + c0 + r;
+    if (c0 + r >= ncols) break;
+    float v = f[r];
+    if constexpr (kInt8) v = (float)iacc[r] * (sa[m] * sw[n]);
+    C[m * N + n] = (uint16_t)f32_to_bf16_rne(v);
+  }
+}
+
 }  // namespace
 
 // Output columns [n_base, n_end) in 256 x TN tiles.
@@ -401,30 +484,64 @@ static void launch_cols(const uint8_t* A, const float* sa, const uint8_t* W, con
   const int64_t tiles_m = (M + kTileM - 1) / kTileM, tiles_n = (n_end - n_base + TN - 1) / TN;
   hipLaunchKernelGGL((gemm_prefill_kernel<kInt8, TN>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(kWaves * 64), 0, stream, A, sa, W, sw, (int)M, (int)N, (int)K, C,
-                     (int)n_base, (int)tiles_m, (int)tiles_n);
+                     (int)n_base, (int)tiles_m, (int)tiles_n, nullptr);
+}
+
+// The shapes the many-token kernel takes (buffer offsets inside one 256-row
+// tile are 32-bit; dims fit int), and how its 256-wide tiles fall on the
+// compute units: c > 0 trailing tile columns make a last round of at most
+// half the units, run apart from the whole rounds before them.
+static bool prefill_layout(int64_t M, int64_t N, int64_t K, int64_t* tiles_m, int64_t* tn256,
+                           int64_t* c) {
+  if (M < 1 || N < 1 || K < kBlock || (int64_t)kTileM * K >= kOutOfRange) return false;
+  if (M > 0x7FFFFFFF || N > 0x7FFFFFFF) return false;
+  *tiles_m = (M + kTileM - 1) / kTileM;
+  if (*tiles_m * ((N + 127) / 128) > 0x7FFFFFFF) return false;
+  const int64_t cus = compute_units();
+  *tn256 = (N + 255) / 256;
+  *c = 0;
+  for (int64_t cc = 1; cc < *tn256 && *c == 0; ++cc)
+    if (((*tn256 - cc) * *tiles_m) % cus == 0 && 2 * cc * *tiles_m <= cus) *c = cc;
+  if (*tiles_m * *tn256 < cus) *c = -1;   // 128-wide tiles throughout
+  return true;
+}
+
+// With a caller workspace, the trailing tile columns of a long-K layer run
+// as 256-wide tiles split over K (S slices, at least 16 K blocks each) on
+// the otherwise idle units, their fp32 partial sums added by a second
+// kernel, instead of as 128-wide tiles: a 128-wide tile reads its
+// activation tile for half the work, and ran at a third of the matrix-core
+// busy fraction of the 256-wide ones.  Only for K of 64 blocks or more:
+// the slabs (S x M x the tail's columns x 4 bytes, written and read once)
+// cost more than they save on short layers.
+bool prefill_tail_plan(int64_t M, int64_t N, int64_t K, PrefillTailPlan* plan) {
+  int64_t tiles_m, tn256, c;
+  if (M <= 128 || !prefill_layout(M, N, K, &tiles_m, &tn256, &c) || c <= 0) return false;
+  const int64_t KB = K / kBlock;
+  if (KB < 64) return false;
+  const int64_t cus = compute_units();
+  int64_t S = cus / (c * tiles_m);
+  S = std::min<int64_t>(std::min<int64_t>(S, 8), KB / 16);
+  if (S < 2) return false;
+  plan->n_split = (tn256 - c) * 256;
+  plan->S = (int)S;
+  plan->bytes = S * M * (N - plan->n_split) * (int64_t)sizeof(float);
+  return true;
 }
 
 template <bool kInt8>
 bool launch_gemm_prefill(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
                          int64_t M, int64_t N, int64_t K, uint16_t* C, hipStream_t stream,
                          hipError_t* err) {
-  // Buffer offsets inside one 256-row tile are 32-bit; dims fit int.
-  if (M < 1 || N < 1 || K < kBlock || (int64_t)kTileM * K >= kOutOfRange) return false;
-  if (M > 0x7FFFFFFF || N > 0x7FFFFFFF) return false;
-  const int64_t tiles_m = (M + kTileM - 1) / kTileM;
-  if (tiles_m * ((N + 127) / 128) > 0x7FFFFFFF) return false;
   // 256-wide tiles, except that when they leave a last partial round of at
   // most half the compute units busy, the trailing tile columns of that
   // round run as twice as many 128-wide tiles in a second launch (whole
   // rounds first, then one round of half-size tiles instead of a half-empty
   // round of full ones).  With fewer 256-wide tiles than compute units
   // (few tokens), 128-wide tiles throughout.
-  const int64_t cus = compute_units();
-  const int64_t tn256 = (N + 255) / 256;
-  int64_t c = 0;
-  for (int64_t cc = 1; cc < tn256 && c == 0; ++cc)
-    if (((tn256 - cc) * tiles_m) % cus == 0 && 2 * cc * tiles_m <= cus) c = cc;
-  if (tiles_m * tn256 < cus) {
+  int64_t tiles_m, tn256, c;
+  if (!prefill_layout(M, N, K, &tiles_m, &tn256, &c)) return false;
+  if (c < 0) {
     launch_cols<kInt8, 128>(A, sa, W, sw, M, N, K, C, 0, N, stream);
   } else if (c == 0) {
     launch_cols<kInt8, 256>(A, sa, W, sw, M, N, K, C, 0, N, stream);
@@ -436,6 +553,33 @@ bool launch_gemm_prefill(const uint8_t* A, const float* sa, const uint8_t* W, co
   *err = hipGetLastError();
   return true;
 }
+
+template <bool kInt8>
+bool launch_gemm_prefill_ws(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
+                            int64_t M, int64_t N, int64_t K, uint16_t* C, float* ws,
+                            int64_t ws_bytes, hipStream_t stream, hipError_t* err) {
+  PrefillTailPlan pl;
+  if (ws == nullptr || !prefill_tail_plan(M, N, K, &pl) || ws_bytes < pl.bytes) return false;
+  launch_cols<kInt8, 256>(A, sa, W, sw, M, N, K, C, 0, pl.n_split, stream);
+  const int64_t tiles_m = (M + kTileM - 1) / kTileM, tiles_n = (N - pl.n_split + 255) / 256;
+  hipLaunchKernelGGL((gemm_prefill_kernel<kInt8, 256, true>),
+                     dim3((unsigned)(tiles_m * tiles_n), (unsigned)pl.S), dim3(kWaves * 64), 0,
+                     stream, A, sa, W, sw, (int)M, (int)N, (int)K, C, (int)pl.n_split,
+                     (int)tiles_m, (int)tiles_n, ws);
+  const int64_t threads = M * ((N - pl.n_split + 3) / 4);
+  hipLaunchKernelGGL((gemm_prefill_tail_reduce_kernel<kInt8>),
+                     dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, ws, pl.S, M,
+                     N, pl.n_split, sa, sw, C);
+  *err = hipGetLastError();
+  return true;
+}
+
+template bool launch_gemm_prefill_ws<false>(const uint8_t*, const float*, const uint8_t*,
+                                            const float*, int64_t, int64_t, int64_t, uint16_t*,
+                                            float*, int64_t, hipStream_t, hipError_t*);
+template bool launch_gemm_prefill_ws<true>(const uint8_t*, const float*, const uint8_t*,
+                                           const float*, int64_t, int64_t, int64_t, uint16_t*,
+                                           float*, int64_t, hipStream_t, hipError_t*);
 
 template bool launch_gemm_prefill<false>(const uint8_t*, const float*, const uint8_t*,
                                          const float*, int64_t, int64_t, int64_t, uint16_t*,

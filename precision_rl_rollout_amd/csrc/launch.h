@@ -129,4 +129,21 @@ bool launch_gemm_prefill(const uint8_t* A, const float* sa, const uint8_t* W, co
                          int64_t M, int64_t N, int64_t K, uint16_t* C, hipStream_t stream,
                          hipError_t* err);
 
+// With a caller workspace, more than 128 rows: the many-token kernel with
+// the last partial round's tile columns split over K (fp32 partial sums in
+// the workspace, added by a second kernel).  The plan: columns [0, n_split)
+// in whole rounds of 256-wide tiles, the rest in S slices; bytes of
+// workspace.  Returns false (launching nothing) when the shape has no such
+// round, its K is short, or the workspace is missing or too small.
+struct PrefillTailPlan {
+  int64_t n_split;
+  int S;
+  int64_t bytes;
+};
+bool prefill_tail_plan(int64_t M, int64_t N, int64_t K, PrefillTailPlan* plan);
+template <bool kInt8>
+bool launch_gemm_prefill_ws(const uint8_t* A, const float* sa, const uint8_t* W, const float* sw,
+                            int64_t M, int64_t N, int64_t K, uint16_t* C, float* ws,
+                            int64_t ws_bytes, hipStream_t stream, hipError_t* err);
+
 }  // namespace prr
