@@ -286,9 +286,11 @@ prr_status w8a8_int8_channel_gemm_ws(const int8_t* a_i8, const float* a_scale,
  * results; calls in order on one stream are safe.  A shape whose split
  * needs more than 16 MiB (S x M x N x 4 bytes, as
  * w8a8_gemm_workspace_size reports) returns PRR_ERR_UNSUPPORTED_SHAPE
- * without launching; a shape with no split runs the one-pass kernels.  Its
- * results equal those of w8a8_block_gemm_ws with a large enough workspace,
- * bit for bit.
+ * without launching; a shape with no split runs the one-pass kernels.
+ * Decode batches (M <= 64) split exactly as w8a8_block_gemm_ws does, with
+ * its results bit for bit; many-token batches (M > 128) run the one-pass
+ * kernels, w8a8_block_gemm's results (the workspace call's split of their
+ * last round needs slabs of tens of MB).
  */
 prr_status w8a8_block_gemm_scratch(const uint8_t* a_fp8, const float* a_scale,
                                    const uint8_t* w_fp8, const float* w_scale, int64_t M,
