@@ -238,7 +238,8 @@ def _workspace(workspace, M, N, K, like):
 def w8a8_block_gemm(a_fp8, a_scale, w_fp8, w_scale, out=None, workspace="auto"):
     """FP8 codes + block scales -> C [M, N] bf16.  With a workspace (by
     default one of the size the library asks for), decode-sized batches of
-    narrow or long-K layers are split over K (w8a8_block_gemm_ws)."""
+    narrow or long-K layers, and the last partial round of a many-token
+    long-K layer, are split over K (w8a8_block_gemm_ws)."""
     M, K = a_fp8.shape
     N = w_fp8.shape[0]
     _operand(a_fp8, torch.uint8, (M, K), "a_fp8")
