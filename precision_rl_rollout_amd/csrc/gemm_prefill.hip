@@ -464,12 +464,26 @@ __global__ __launch_bounds__(256) void gemm_prefill_tail_reduce_kernel(
       else f[r] += v[r];
     }
   }
+  float sm = 1.f, swv[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (kInt8) {
+    // the row's scale once, the 4 channel scales in one 16-byte load where
+    // they are aligned
+    sm = sa[m];
+    const int64_t n0 = n_base + c0;
+    if (((n0 | N) & 3) == 0 && c0 + 4 <= ncols) {
+      const float4 x = *reinterpret_cast<const float4*>(sw + n0);
+      swv[0] = x.x; swv[1] = x.y; swv[2] = x.z; swv[3] = x.w;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) swv[r] = c0 + r < ncols ? sw[n0 + r] : 0.f;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t n = n_base + c0 + r;
     if (c0 + r >= ncols) break;
     float v = f[r];
-    if constexpr (kInt8) v = (float)iacc[r] * (sa[m] * sw[n]);
+    if constexpr (kInt8) v = (float)iacc[r] * (sm * swv[r]);
     C[m * N + n] = (uint16_t)f32_to_bf16_rne(v);
   }
 }
