@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define PRR_ABI_VERSION 9
+#define PRR_ABI_VERSION 10
 
 typedef enum prr_status {
   PRR_OK = 0,
@@ -362,6 +362,37 @@ prr_status fp8_kv_scale_recalibrate(const uint16_t* x_bf16, int64_t T, int64_t C
 prr_status fp8_kv_cache_write(const uint16_t* kv_bf16, const int64_t* slot_mapping,
                               int64_t T, int64_t C, const float* scale, uint8_t* cache,
                               int64_t num_slots, hipStream_t stream);
+
+/*
+ * fp8_kv_cache_write_recalibrate -- one step of the FP8 KV cache (FP8-RL,
+ * abstract, item (ii)) in one pass over the step's new rows: they are
+ * written into the cache with the scale an earlier batch calibrated,
+ * exactly as fp8_kv_cache_write(kv_bf16, slot_mapping, T, C, scale, cache,
+ * num_slots), and the next step's scale is recalibrated from the same rows,
+ * exactly as fp8_kv_scale_recalibrate(kv_bf16, T, C, new_scale).  The two
+ * separate calls read the rows twice; this one reads them once.
+ *   kv_bf16, slot_mapping, scale, cache, T, C, num_slots: as
+ *                fp8_kv_cache_write (the write is a no-op when num_slots
+ *                is 0; kv_bf16 and slot_mapping may be NULL when T x C is
+ *                0, cache when num_slots is 0).
+ *   new_scale  out  one fp32: fl32(max |kv| / 448) over all T x C values,
+ *                every row counted whether or not its slot is in range
+ *                (+0.0 for an all-zero or empty batch).  Written by the
+ *                call's last kernel, after every read of `scale`, so it may
+ *                be the `scale` word itself (the scale updated in place).
+ *   workspace  device memory, 16-byte aligned, of workspace_bytes >=
+ *                PRR_KV_RECAL_WORKSPACE_BYTES (else PRR_ERR_INVALID_ARG):
+ *                the workgroups' partial maxima, for the call's duration
+ *                only (one call at a time per workspace; no clearing
+ *                needed).  May be NULL when T x C == 0.
+ */
+#define PRR_KV_RECAL_WORKSPACE_BYTES 8192
+prr_status fp8_kv_cache_write_recalibrate(const uint16_t* kv_bf16,
+                                          const int64_t* slot_mapping, int64_t T,
+                                          int64_t C, const float* scale, uint8_t* cache,
+                                          int64_t num_slots, float* new_scale,
+                                          void* workspace, int64_t workspace_bytes,
+                                          hipStream_t stream);
 
 /*
  * fp8_kv_decode_attention -- the read side of the FP8 KV cache (FP8-RL,

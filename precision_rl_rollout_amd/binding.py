@@ -51,6 +51,7 @@ _SIGNATURES = {
     "w8a8_block_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
     "w8a8_int8_channel_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
     "w8a8_block_gemm_scratch": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P],
+    "fp8_kv_cache_write_recalibrate": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _P],
     "fp8_weight_block_quant_multi": [_P, _I64, _P],
     "int8_weight_channel_quant_multi": [_P, _I64, _P],
 }
@@ -69,7 +70,7 @@ _lib = None
 
 # PRR_ABI_VERSION of the signatures below; a library of another version is
 # refused at load time.
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class PrrError(RuntimeError):
@@ -440,6 +441,37 @@ def attention_workspace_bytes(B: int, Hq: int, Hkv: int, D: int) -> int:
                                                              ctypes.addressof(n)))
         _ws_sizes[key] = int(n.value)
     return _ws_sizes[key]
+
+
+KV_RECAL_WORKSPACE_BYTES = 8192   # PRR_KV_RECAL_WORKSPACE_BYTES
+
+
+def fp8_kv_cache_write_recalibrate(kv: torch.Tensor, slot_mapping: torch.Tensor,
+                                   scale: torch.Tensor, cache: torch.Tensor, new_scale=None,
+                                   workspace=None):
+    """One pass over kv [T, C] bf16: fp8_kv_cache_write(kv, slot_mapping,
+    scale, cache), and the next step's scale fl32(max |kv| / 448) into
+    new_scale (fp32 [1] on the device; may be `scale` itself, updated in
+    place).  workspace: a uint8 CUDA tensor of at least
+    KV_RECAL_WORKSPACE_BYTES, or None for a new one.  Returns new_scale."""
+    kv = _bf16_bits(kv, "kv")
+    T, C = kv.shape
+    _operand(slot_mapping, torch.int64, (T,), "slot_mapping")
+    _operand(scale, torch.float32, (1,), "scale")
+    if cache.dtype != torch.uint8 or cache.dim() != 2 or cache.shape[1] != C \
+            or not cache.is_cuda or not cache.is_contiguous():
+        raise ValueError(f"cache: expected a contiguous CUDA uint8 tensor [num_slots, {C}]")
+    ns = _out(new_scale, torch.float32, (1,), kv, "new_scale")
+    if workspace is None:
+        workspace = torch.empty((KV_RECAL_WORKSPACE_BYTES,), dtype=torch.uint8, device=kv.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace: expected a contiguous CUDA uint8 tensor")
+    _check("fp8_kv_cache_write_recalibrate",
+           load().fp8_kv_cache_write_recalibrate(_ptr(kv), _ptr(slot_mapping), T, C,
+                                                 scale.data_ptr(), _ptr(cache), cache.shape[0],
+                                                 ns.data_ptr(), _ptr(workspace),
+                                                 workspace.numel(), _stream(kv)))
+    return ns
 
 
 def fp8_kv_decode_attention(q: torch.Tensor, q_scale: torch.Tensor, k_cache: torch.Tensor,

@@ -366,6 +366,26 @@ prr_status fp8_kv_cache_write(const uint16_t* kv_bf16, const int64_t* slot_mappi
       prr::launch_fp8_kv_cache_write(kv_bf16, slot_mapping, T, C, scale, cache, num_slots, stream));
 }
 
+prr_status fp8_kv_cache_write_recalibrate(const uint16_t* kv_bf16,
+                                          const int64_t* slot_mapping, int64_t T, int64_t C,
+                                          const float* scale, uint8_t* cache, int64_t num_slots,
+                                          float* new_scale, void* workspace,
+                                          int64_t workspace_bytes, hipStream_t stream) {
+  static_assert(PRR_KV_RECAL_WORKSPACE_BYTES == 4 * prr::kKvRecalParts, "partials workspace");
+  PRR_TRY(check_dims(T, C, num_slots));
+  PRR_TRY(check_ptrs({new_scale}));
+  if (workspace_bytes < 0) return PRR_ERR_INVALID_ARG;
+  if (T > 0 && C > 0) {
+    PRR_TRY(check_ptrs({kv_bf16, slot_mapping, scale, workspace}));
+    if (workspace_bytes < PRR_KV_RECAL_WORKSPACE_BYTES) return PRR_ERR_INVALID_ARG;
+    if (num_slots > 0) PRR_TRY(check_ptrs({cache}));
+  }
+  PRR_TRY(check_device());
+  return from_hip(prr::launch_fp8_kv_cache_write_recalibrate(
+      kv_bf16, slot_mapping, T, C, scale, num_slots > 0 ? cache : nullptr, num_slots, new_scale,
+      static_cast<uint32_t*>(workspace), stream));
+}
+
 prr_status tis_token_weights(const float* logp_train, const float* logp_rollout,
                              const uint8_t* mask, int64_t B, int64_t T, float cap, int mode,
                              float* weights, float* row_stats, double* totals,

@@ -20,6 +20,9 @@ __global__ void kv_amax_clear_kernel(uint32_t* acc) { *acc = 0u; }
 
 // Each thread takes kAmaxLoads 16-byte chunks per pass, all loads issued
 // before any is used (one load in flight per thread held it to ~1.9 TB/s).
+// The grid is at most one workgroup per CU, looping over the passes: the
+// atomics of more workgroups, all ending together, serialize on the one
+// word (at 131,072 x 1024 values, 1024 workgroups took 65 us, 256 took 47).
 constexpr int kAmaxLoads = 32;
 
 __global__ __launch_bounds__(256) void kv_amax_kernel(const uint16_t* __restrict__ x, int64_t n,
@@ -64,7 +67,7 @@ hipError_t launch_fp8_kv_scale_recalibrate(const uint16_t* x, int64_t n, float* 
   if (n > 0) {
     const int64_t chunks = n / 8;
     int64_t grid = (chunks + 256 * kAmaxLoads - 1) / (256 * kAmaxLoads);
-    const int64_t cap = 4 * (int64_t)compute_units();
+    const int64_t cap = compute_units();
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kv_amax_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, n, acc);
@@ -82,50 +85,109 @@ hipError_t launch_fp8_kv_scale_recalibrate(const uint16_t* x, int64_t n, float* 
 // the conversion.
 constexpr int kWriteChunks = 4;
 
-template <bool kVec>
+// kRecal (fp8_kv_cache_write_recalibrate): the same pass also reduces the
+// rows' amax -- over every row of the batch, whether or not its slot is in
+// range -- and each workgroup stores its packed maximum in part[blockIdx.x]
+// with a plain store; kv_part_scale_kernel then folds the partials into the
+// new scale.  (One atomic maximum per workgroup on the single scale word
+// serializes on that word: at 2048 workgroups it added ~9 us to a 12 us
+// write; spread over 64 words it added nothing.)  The grid is capped at kKvRecalParts workgroups, which loop
+// over the row groups, so the partials fit the caller's fixed workspace.  No
+// thread leaves before the workgroup's reduction: rows past T and rows with
+// no slot only skip their stores.
+
+template <bool kVec, bool kRecal = false>
 __global__ __launch_bounds__(256) void kv_cache_write_kernel(
     const uint16_t* __restrict__ kv, const int64_t* __restrict__ slots, int64_t T, int64_t C,
-    const float* __restrict__ scale, uint8_t* __restrict__ cache, int64_t num_slots, int rpw) {
+    const float* __restrict__ scale, uint8_t* __restrict__ cache, int64_t num_slots, int rpw,
+    uint32_t* __restrict__ part) {
   const int lpr = 256 / rpw;                      // threads per row
-  const int64_t t = (int64_t)blockIdx.x * rpw + threadIdx.x / lpr;
-  if (t >= T) return;
-  const uint16_t* src = kv + t * C;
   const int64_t lane8 = (int64_t)(threadIdx.x % lpr) * 8;
   const int64_t step = (int64_t)lpr * 8;
-  for (int64_t col0 = lane8; col0 < C; col0 += step * kWriteChunks) {
-    uint4 v[kWriteChunks];
+  const int64_t groups = (T + rpw - 1) / rpw;
+  uint32_t am = 0;                                // packed |x| maxima (kRecal)
+  // One row group per workgroup for the plain write; a grid-stride loop
+  // over them for kRecal.
+  for (int64_t g = blockIdx.x; g < groups; g += kRecal ? (int64_t)gridDim.x : groups) {
+    const int64_t t = g * rpw + threadIdx.x / lpr;
+    const bool row_live = t < T;
+    if (!kRecal && !row_live) return;
+    const uint16_t* src = kv + (row_live ? t : 0) * C;
+    for (int64_t col0 = lane8; col0 < C; col0 += step * kWriteChunks) {
+      uint4 v[kWriteChunks];
 #pragma unroll
-    for (int i = 0; i < kWriteChunks; ++i) {
-      const int64_t col = col0 + i * step;
-      if constexpr (kVec) {         // C % 8 == 0: whole 16-byte chunks, aligned
-        v[i] = col < C ? load_once16(src + col) : make_uint4(0, 0, 0, 0);
-      } else {
-        uint32_t h[8];
+      for (int i = 0; i < kWriteChunks; ++i) {
+        const int64_t col = col0 + i * step;
+        const bool in = row_live && col < C;
+        if constexpr (kVec) {       // C % 8 == 0: whole 16-byte chunks, aligned
+          v[i] = in ? load_once16(src + col) : make_uint4(0, 0, 0, 0);
+        } else {
+          uint32_t h[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (col + e < C) ? (uint32_t)src[col + e] : 0u;
-        v[i] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                          h[6] | (h[7] << 16));
+          for (int e = 0; e < 8; ++e)
+            h[e] = (row_live && col + e < C) ? (uint32_t)src[col + e] : 0u;
+          v[i] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                            h[6] | (h[7] << 16));
+        }
+      }
+      if constexpr (kRecal) {
+#pragma unroll
+        for (int i = 0; i < kWriteChunks; ++i) {
+          am = absmax_bf16x2(am, v[i].x);
+          am = absmax_bf16x2(am, v[i].y);
+          am = absmax_bf16x2(am, v[i].z);
+          am = absmax_bf16x2(am, v[i].w);
+        }
+      }
+      const int64_t slot = row_live ? slots[t] : -1;
+      if (slot < 0 || slot >= num_slots) {
+        if constexpr (kRecal) continue;
+        else return;
+      }
+      const float s = *scale;
+      const BlockDiv d = block_div(s);
+      uint8_t* dst = cache + slot * C;
+#pragma unroll
+      for (int i = 0; i < kWriteChunks; ++i) {
+        const int64_t col = col0 + i * step;
+        if (col >= C) break;
+        const uint2 c = e4m3_chunk_any<true>(v[i], s, d);
+        if constexpr (kVec) {
+          *reinterpret_cast<uint2*>(dst + col) = c;
+        } else {
+          const uint32_t cw[2] = {c.x, c.y};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e < C) dst[col + e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
+        }
       }
     }
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) return;
-    const float s = *scale;
-    const BlockDiv d = block_div(s);
-    uint8_t* dst = cache + slot * C;
-#pragma unroll
-    for (int i = 0; i < kWriteChunks; ++i) {
-      const int64_t col = col0 + i * step;
-      if (col >= C) break;
-      const uint2 c = e4m3_chunk_any<true>(v[i], s, d);
-      if constexpr (kVec) {
-        *reinterpret_cast<uint2*>(dst + col) = c;
-      } else {
-        const uint32_t cw[2] = {c.x, c.y};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (col + e < C) dst[col + e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
-      }
-    }
+  }
+  if constexpr (kRecal) {
+    __shared__ uint32_t red[4];
+    uint32_t m = wave_max_u32(absmax_fold(am));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) part[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+  }
+}
+
+// The new scale from the n partial maxima: fl32(amax / 448), +0.0 when
+// every partial is 0 (an all-zero or empty batch).  One workgroup.  Its
+// trace duration, ~4 us, is the kernel boundary (the same as the one-thread
+// clear kernel's after a large write): two 16-byte loads per thread instead
+// of this loop measured the same.
+__global__ __launch_bounds__(256) void kv_part_scale_kernel(const uint32_t* __restrict__ part,
+                                                            int n, float* __restrict__ scale) {
+  __shared__ uint32_t red[4];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += 256) m = max(m, part[i]);
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    *scale = m ? div_rn(__uint_as_float(m << 16), kFp8Max) : 0.0f;
   }
 }
 
@@ -140,10 +202,34 @@ hipError_t launch_fp8_kv_cache_write(const uint16_t* kv, const int64_t* slots, i
   const unsigned grid = (unsigned)((T + rpw - 1) / rpw);
   if (C % 8 == 0)
     hipLaunchKernelGGL(kv_cache_write_kernel<true>, dim3(grid), dim3(256), 0, stream, kv, slots,
-                       T, C, scale, cache, num_slots, rpw);
+                       T, C, scale, cache, num_slots, rpw, nullptr);
   else
     hipLaunchKernelGGL(kv_cache_write_kernel<false>, dim3(grid), dim3(256), 0, stream, kv,
-                       slots, T, C, scale, cache, num_slots, rpw);
+                       slots, T, C, scale, cache, num_slots, rpw, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_kv_cache_write_recalibrate(const uint16_t* kv, const int64_t* slots,
+                                                 int64_t T, int64_t C, const float* scale,
+                                                 uint8_t* cache, int64_t num_slots,
+                                                 float* new_scale, uint32_t* part,
+                                                 hipStream_t stream) {
+  int grid = 0;
+  if (T > 0 && C > 0) {
+    const int64_t chunks = (C + 7) / 8;
+    const int64_t per = (chunks + kWriteChunks - 1) / kWriteChunks;
+    int rpw = 1;
+    while (rpw < 256 && 256 / (rpw * 2) >= per) rpw *= 2;
+    const int64_t groups = (T + rpw - 1) / rpw;
+    grid = (int)(groups < kKvRecalParts ? groups : kKvRecalParts);
+    if (C % 8 == 0)
+      hipLaunchKernelGGL((kv_cache_write_kernel<true, true>), dim3(grid), dim3(256), 0, stream, kv,
+                         slots, T, C, scale, cache, num_slots, rpw, part);
+    else
+      hipLaunchKernelGGL((kv_cache_write_kernel<false, true>), dim3(grid), dim3(256), 0, stream,
+                         kv, slots, T, C, scale, cache, num_slots, rpw, part);
+  }
+  hipLaunchKernelGGL(kv_part_scale_kernel, dim3(1), dim3(256), 0, stream, part, grid, new_scale);
   return hipGetLastError();
 }
 

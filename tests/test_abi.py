@@ -51,7 +51,8 @@ def test_header_declares_the_boundary():
                      "int8_weight_channel_quant", "int8_act_token_quant",
                      "w8a8_int8_channel_gemm", "w8a8_block_gemm_grouped",
                      "fp8_kv_scale_recalibrate",
-                     "fp8_kv_cache_write", "tis_token_weights", "w8a8_gemm_workspace_size",
+                     "fp8_kv_cache_write", "fp8_kv_cache_write_recalibrate",
+                     "tis_token_weights", "w8a8_gemm_workspace_size",
                      "fp8_kv_decode_attention", "fp8_kv_decode_attention_workspace_size",
                      "fp8_kv_decode_attention_ws", "w8a8_block_gemm_ws",
                      "w8a8_int8_channel_gemm_ws", "w8a8_block_gemm_scratch",
@@ -184,10 +185,43 @@ def test_kv_cache_write_argument_checks():
     assert c(None, None, 4, 8, None, None, 0, None) == OK
 
 
+def test_kv_write_recalibrate_argument_checks():
+    c = lambda *a: binding.call("fp8_kv_cache_write_recalibrate", *a)
+    NEW = FAKE + 256                             # another aligned word
+    WS = FAKE + 4096
+    WSB = binding.KV_RECAL_WORKSPACE_BYTES
+    assert WSB == 8192
+    assert c(FAKE, FAKE, -1, 8, FAKE, FAKE, 4, NEW, WS, WSB, None) == INVALID
+    assert c(FAKE, FAKE, 4, 8, FAKE, FAKE, -4, NEW, WS, WSB, None) == INVALID
+    assert c(FAKE, FAKE, 4, 8, FAKE, FAKE, 16, NEW, WS, -1, None) == INVALID
+    for i in (0, 1, 4, 5, 7, 8):
+        args = [FAKE, FAKE, 4, 8, FAKE, FAKE, 16, NEW, WS, WSB, None]
+        args[i] = None
+        assert c(*args) == INVALID, i
+        args[i] = ODD
+        assert c(*args) == MISALIGNED, i
+    # the partial maxima need the whole workspace
+    assert c(FAKE, FAKE, 4, 8, FAKE, FAKE, 16, NEW, WS, WSB - 4, None) == INVALID
+    # an empty batch still writes its new scale (0): that pointer is needed
+    assert c(None, None, 0, 8, None, None, 16, None, None, 0, None) == INVALID
+
+
 @pytest.mark.skipif(_gpu_visible(), reason="needs a process without a GPU")
 def test_kv_no_device_is_reported():
     assert binding.call("fp8_kv_scale_recalibrate", FAKE, 4, 8, FAKE, None) == NO_DEVICE
     assert binding.call("fp8_kv_cache_write", FAKE, FAKE, 4, 8, FAKE, FAKE, 16, None) == NO_DEVICE
+    WSB = binding.KV_RECAL_WORKSPACE_BYTES
+    assert binding.call("fp8_kv_cache_write_recalibrate", FAKE, FAKE, 4, 8, FAKE, FAKE, 16,
+                        FAKE + 256, FAKE + 4096, WSB, None) == NO_DEVICE
+    # the new scale may be the scale word (updated in place)
+    assert binding.call("fp8_kv_cache_write_recalibrate", FAKE, FAKE, 4, 8, FAKE, FAKE, 16,
+                        FAKE, FAKE + 4096, WSB, None) == NO_DEVICE
+    # an empty batch or no slots: nothing is read (no workspace either), the
+    # new scale is still set
+    assert binding.call("fp8_kv_cache_write_recalibrate", None, None, 0, 8, None, None, 16,
+                        FAKE, None, 0, None) == NO_DEVICE
+    assert binding.call("fp8_kv_cache_write_recalibrate", FAKE, FAKE, 4, 8, FAKE, None, 0,
+                        FAKE + 256, FAKE + 4096, WSB, None) == NO_DEVICE
 
 
 def test_tis_argument_checks():

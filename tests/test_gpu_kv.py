@@ -68,12 +68,13 @@ def test_recalibrate_zero_and_empty():
 
 
 def test_recalibrate_past_one_pass_of_the_grid():
-    # 66,000 x 1024 values: more 16-byte chunks than one pass of the largest
-    # grid covers, so threads loop; the second check puts the maximum where
-    # only the second pass reads it
+    # 66,000 x 1024 values: more 16-byte chunks than one pass of the grid
+    # covers (one workgroup per CU, 32 chunks per thread: 2,097,152 chunks on
+    # 256 CUs), so threads loop; the second check puts the maximum in the
+    # last 11,000 chunks, which only the last pass reads
     T, C = 66000, 1024
     xb = workloads.kv_rows(T, C, 5, "K")
-    announce(f"fp8_kv_scale_recalibrate T{T} C{C} (two passes)")
+    announce(f"fp8_kv_scale_recalibrate T{T} C{C} (several passes)")
     xd = bits_to_dev(xb)
     assert _f32_bits(host(binding.fp8_kv_scale_recalibrate(xd))[0]) == _f32_bits(kv.kv_scale(xb))
     pos = T * C - 84_000
@@ -154,3 +155,130 @@ def test_full_32b_prefill_write():
     cache = torch.from_numpy(cache0).cuda()
     binding.fp8_kv_cache_write(xd, torch.from_numpy(slots).cuda(), sd, cache)
     assert np.array_equal(host(cache), want)
+
+
+# ------------------------------------------------- write + recalibrate, one pass
+def _fused_case(T, C, num_slots, seed, pad_every=0, xb=None, stale_seed=None, inplace=False,
+                workspace=None):
+    """The step's rows written with the scale an earlier batch calibrated,
+    and the next scale recalibrated from the same rows, in one call; the
+    oracle's write and scale as the two steps.  inplace: the new scale
+    replaces the old one in the same word."""
+    if xb is None:
+        xb = workloads.kv_rows(T, C, seed, "V")
+    earlier = workloads.kv_rows(max(T, 1), max(C, 1), seed + 1000 if stale_seed is None
+                                else stale_seed, "V")
+    s_old = kv.kv_scale(earlier)
+    slots = workloads.kv_slot_mapping(T, num_slots, 16, seed, pad_every) if T else \
+        np.zeros(0, dtype=np.int64)
+    cache0 = np.full((num_slots, C), CANARY, dtype=np.uint8)
+    want_cache = kv.kv_cache_write(cache0, xb, slots, s_old) if T else cache0
+    want_scale = kv.kv_scale(xb)
+    cache = torch.from_numpy(cache0).cuda()
+    sd = torch.tensor([s_old], dtype=torch.float32, device="cuda:0")
+    new = sd if inplace else torch.full((1,), 7.0, dtype=torch.float32, device="cuda:0")
+    binding.fp8_kv_cache_write_recalibrate(bits_to_dev(xb), torch.from_numpy(slots).cuda(), sd,
+                                           cache, new_scale=new, workspace=workspace)
+    return host(cache), host(new)[0], want_cache, want_scale, xb, slots, s_old
+
+
+@pytest.mark.parametrize("T,C,num_slots,pad", [(1, 8, 16, 0), (7, 40, 64, 3), (128, 1024, 512, 0),
+                                               (333, 1001, 1024, 5), (100, 3, 2048, 0),
+                                               (1000, 256, 4096, 9)])
+def test_write_recalibrate_matches_oracle(T, C, num_slots, pad):
+    announce(f"fp8_kv_cache_write_recalibrate T{T} C{C} slots{num_slots} pad{pad}")
+    got, got_s, want, want_s, *_ = _fused_case(T, C, num_slots, seed=T + C, pad_every=pad)
+    assert np.array_equal(got, want)
+    assert _f32_bits(got_s) == _f32_bits(want_s)
+
+
+def test_write_recalibrate_in_place():
+    # new_scale is the scale word: the rows are written with the old value,
+    # then the word holds the new one.
+    announce("fp8_kv_cache_write_recalibrate in place T300 C136")
+    got, got_s, want, want_s, *_ = _fused_case(300, 136, 1024, seed=3, pad_every=4, inplace=True)
+    assert np.array_equal(got, want)
+    assert _f32_bits(got_s) == _f32_bits(want_s)
+
+
+@pytest.mark.parametrize("T,C", [(20000, 1024), (600000, 8)])
+def test_write_recalibrate_groups_past_the_grid(T, C):
+    # More row groups than workgroups (2048): the workgroups loop; the
+    # batch maximum sits in the last row, which a second pass reaches.
+    xb = workloads.kv_rows(T, C, 41, "K")
+    xb[T - 1, C - 1] = 0xC700                    # -32768.0
+    announce(f"fp8_kv_cache_write_recalibrate T{T} C{C} (grid-stride)")
+    got, got_s, want, want_s, *_ = _fused_case(T, C, T + 4096, seed=41, pad_every=13, xb=xb)
+    assert np.array_equal(got, want)
+    assert _f32_bits(got_s) == _f32_bits(want_s) == _f32_bits(np.float32(32768.0) / np.float32(448))
+
+
+def test_write_recalibrate_reuses_a_workspace():
+    # The partials of a large call are left in the workspace; a smaller
+    # call on it reads only its own.
+    ws = torch.empty(binding.KV_RECAL_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
+    big = workloads.kv_rows(16384, 256, 51, "K")
+    big[100, 3] = 0x4780                         # 65536.0: a stale partial if read
+    for T, C, xb in ((16384, 256, big), (9, 40, None), (1, 8, None)):
+        announce(f"fp8_kv_cache_write_recalibrate T{T} C{C} on a used workspace")
+        got, got_s, want, want_s, *_ = _fused_case(T, C, T + 64, seed=52, xb=xb, workspace=ws)
+        assert np.array_equal(got, want)
+        assert _f32_bits(got_s) == _f32_bits(want_s)
+
+
+def test_write_recalibrate_counts_rows_without_a_slot():
+    # The batch maximum sits in a padding row (negative slot): the write
+    # skips the row, the scale counts it.
+    T, C = 64, 128
+    xb = workloads.kv_rows(T, C, 21, "K")
+    slots_pad = workloads.kv_slot_mapping(T, 256, 16, 21, 7)
+    pad_row = int(np.flatnonzero(slots_pad < 0)[0])
+    xb[pad_row, 5] = 0x4700                      # 32768.0, far above the rest
+    announce("fp8_kv_cache_write_recalibrate: maximum in a padding row")
+    got, got_s, want, want_s, *_ = _fused_case(T, C, 256, seed=21, pad_every=7, xb=xb)
+    assert np.array_equal(got, want)
+    assert _f32_bits(got_s) == _f32_bits(want_s) == _f32_bits(np.float32(32768.0) / np.float32(448))
+
+
+def test_write_recalibrate_equals_the_two_calls():
+    T, C, S = 2000, 1024, 8192
+    xb = workloads.kv_rows(T, C, 31, "K")
+    slots = torch.from_numpy(workloads.kv_slot_mapping(T, S, 16, 31, 11)).cuda()
+    xd = bits_to_dev(xb)
+    s_old = binding.fp8_kv_scale_recalibrate(bits_to_dev(workloads.kv_rows(T, C, 32, "K")))
+    announce("fp8_kv_cache_write_recalibrate against fp8_kv_cache_write + recalibrate")
+    c1 = torch.full((S, C), CANARY, dtype=torch.uint8, device="cuda:0")
+    c2 = c1.clone()
+    binding.fp8_kv_cache_write(xd, slots, s_old, c1)
+    s1 = binding.fp8_kv_scale_recalibrate(xd)
+    s2 = binding.fp8_kv_cache_write_recalibrate(xd, slots, s_old, c2)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+def test_write_recalibrate_empty_and_no_slots():
+    announce("fp8_kv_cache_write_recalibrate: empty batch, empty cache")
+    sd = torch.tensor([0.5], dtype=torch.float32, device="cuda:0")
+    cache = torch.full((16, 8), CANARY, dtype=torch.uint8, device="cuda:0")
+    empty = torch.empty((0, 8), dtype=torch.int16, device="cuda:0")
+    new = binding.fp8_kv_cache_write_recalibrate(empty, torch.empty(0, dtype=torch.int64,
+                                                                    device="cuda:0"), sd, cache)
+    torch.cuda.synchronize()
+    assert _f32_bits(host(new)[0]) == 0
+    assert torch.all(cache == CANARY)
+    # no cache rows at all: nothing written, the scale still recalibrated
+    xb = workloads.kv_rows(9, 40, 5, "K")
+    none = torch.empty((0, 40), dtype=torch.uint8, device="cuda:0")
+    new = binding.fp8_kv_cache_write_recalibrate(
+        bits_to_dev(xb), torch.arange(9, dtype=torch.int64, device="cuda:0"), sd, none)
+    assert _f32_bits(host(new)[0]) == _f32_bits(kv.kv_scale(xb))
+
+
+def test_full_32b_prefill_write_recalibrate():
+    cfg = workloads.KV_32B
+    T, C, S = cfg["T"], cfg["C"], cfg["num_slots"]
+    announce(f"fp8_kv_cache_write_recalibrate full T{T} C{C} slots{S}")
+    got, got_s, want, want_s, *_ = _fused_case(T, C, S, seed=0)
+    assert np.array_equal(got, want)
+    assert _f32_bits(got_s) == _f32_bits(want_s)
