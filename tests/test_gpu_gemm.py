@@ -97,9 +97,9 @@ GEMM_SHAPES = [(16, 256, 256), (5, 200, 384), (1, 16, 128), (17, 129, 256), (33,
                # 65-128 rows: two row ranges on pairs of decode workgroups
                # (uneven halves, ragged N, a grid below 32 workers, a single
                # strip that falls back to the many-token kernel, K beyond the
-               # register budget that does too)
+               # register budget that does too, 4375 strips: ~17 per pair)
                (65, 1000, 640), (72, 20000, 1024), (100, 3000, 6144), (96, 130, 256),
-               (80, 16, 128), (128, 777, 8192), (113, 5120, 5120),
+               (80, 16, 128), (128, 777, 8192), (113, 5120, 5120), (72, 70000, 256),
                # many-token kernel (256 x 256 tiles): odd K-block count over a
                # 3 x 4 tile grid, a single K block over 9 x 2 tiles, 4 x 4 tiles
                (513, 777, 1152), (2304, 512, 128), (1024, 1024, 256)]

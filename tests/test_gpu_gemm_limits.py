@@ -7,12 +7,14 @@ the C ABI, against the CPU oracle.
   reaches 127^2 x 133,120 = 2,147,082,880, 400,767 below 2^31, on each path
   that takes such a K -- the skinny kernel (no workspace), split-K with int32
   partial sums added exactly by the second kernel (workspace), the
-  many-token kernel (more than 128 rows).  All-positive codes make every
+  many-token kernel (more than 128 rows, and 100 rows, whose K is beyond the
+  registers of the 65-128-row decode kernel).  All-positive codes make every
   product add up to the bound; a seeded sign pattern checks that the
   cancellations are exact too.
 * FP8 at the longest K of the skinny kernel's LDS-staged activation scales
   (81,920 at 64 rows), and beyond it, where 64 rows run on the many-token
-  kernel's mostly empty 256-row tiles, or split-K with a workspace.
+  kernel's mostly empty 256-row tiles, or split-K with a workspace; and 100
+  rows at the same K, on the many-token kernel.
 """
 
 import numpy as np
@@ -46,7 +48,7 @@ def _int8_codes(rows, K, signs, rng):
     return np.where(rng.integers(0, 2, size=(rows, K)) == 1, -127, 127).astype(np.int8)
 
 
-@pytest.mark.parametrize("M,N", [(1, 200), (40, 300), (200, 260)])
+@pytest.mark.parametrize("M,N", [(1, 200), (40, 300), (100, 260), (200, 260)])
 @pytest.mark.parametrize("signs", ["positive", "mixed"])
 def test_int8_gemm_at_the_accumulator_bound(M, N, signs):
     rng = np.random.default_rng([M, N, 0 if signs == "positive" else 1])
@@ -72,7 +74,8 @@ def test_int8_gemm_at_the_accumulator_bound(M, N, signs):
         _check(out, c64, label)
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 300, 81920), (64, 130, 90112), (7, 129, 90112)])
+@pytest.mark.parametrize("M,N,K", [(64, 300, 81920), (64, 130, 90112), (7, 129, 90112),
+                                   (100, 300, 90112)])
 def test_fp8_gemm_long_k(M, N, K):
     p = workloads.gemm_problem(M, N, K, outliers=True, seed=5)
     aq, sa = quant.fp8_act_token_quant(p["A"])
