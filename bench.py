@@ -35,7 +35,11 @@ workspace, which splits the batch's tokens over the CUs; ``batch_sizes``
 adds the first 1, 2, 8 and 64 sequences with and without the split),
 ``sync32b_requant`` (quantize-on-receive: the 32B up/gate weight arriving
 in 8 shards from pinned host memory, each quantized into place in the full
-FP8 weight while the next is in transfer).
+FP8 weight while the next is in transfer).  Steps of these workloads run
+behind a short hold of the launch stream, so that the host has queued
+them before the GPU starts (several of their kernels are shorter than a
+Python call into the binding); their time is the GPU time of the queued
+steps, and ``timing`` notes the host's own time per step beside it.
 """
 
 from __future__ import annotations
@@ -148,31 +152,79 @@ class Timer:
                 for k, v in self.pairs.items()}
 
 
+# One note per timed_steps pass ({step, host_us_per_step, queued}); main()
+# attaches them to the line as "timing".
+TIMINGS = []
+
+
+def hold_stream(torch, us, mark=None):
+    """Keep the launch stream busy for about `us` microseconds with torch's
+    one-thread spin kernel (bounded: it counts down a fixed number of
+    clock cycles), so that the host queues the calls that follow ahead of
+    the GPU.  Kernels of 10-20 us are shorter than a Python call into the
+    binding: unheld, the GPU waits on the host between them and event pairs
+    time the host's launch path, not the kernels.  The spin's cycles per
+    microsecond follow the clock, so a short spin is timed first, at the
+    clock of the moment.  `mark`, an event, is recorded just before the
+    hold itself."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    torch.cuda._sleep(200_000)
+    e1.record()
+    torch.cuda.synchronize()
+    per_us = 200_000 / max(1.0, e0.elapsed_time(e1) * 1e3)
+    if mark is not None:
+        mark.record()
+    torch.cuda._sleep(int(us * per_us))
+
+
 def timed_steps(torch, step, args):
     """Warm-up steps; a short instrumented pass (untimed) that gives every
-    kernel's duration and names the dominant one; then the timed steps,
+    kernel's duration and names the dominant one; then the K timed steps,
     with HIP events around the dominant kernel's calls only.  (An event
     pair around every call leaves the GPU idle ~3.5 us per marker: the
     6-kernel decode step measured 258 us instrumented, 213 us without,
-    and 213 us as a HIP graph replay.)  step(i, timer) runs step i.
+    and 213 us as a HIP graph replay.)  Both passes start behind a hold of
+    the launch stream (hold_stream) four times as long as the host took to
+    issue that many warm-up steps (the instrumented steps' event markers
+    slow the host down), so the steps run back to back on the GPU; the step
+    time is the GPU time of the K queued steps, between a HIP event after
+    the hold and one after the last step (the host's own time per step is
+    noted in TIMINGS, with whether the hold outlasted the host's issue of
+    the K steps).  step(i, timer) runs step i.
     Returns (seconds per step, {kernel: us}, dominant kernel)."""
+    t0 = time.perf_counter()
     for i in range(args.warmup):
         step(i, None)
+    host_us = (time.perf_counter() - t0) * 1e6 / max(1, args.warmup)
     torch.cuda.synchronize()
+    n_pre = max(1, min(args.steps, 10))
+    hold_stream(torch, 4 * host_us * n_pre + 500)
     pre = Timer(torch)
-    for i in range(max(1, min(args.steps, 10))):
+    for i in range(n_pre):
         step(i, pre)
     torch.cuda.synchronize()
     us = pre.avg_us()
     dom = max(us, key=us.get)
     timer = Timer(torch, only=dom)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     torch.cuda.synchronize()
+    hold_stream(torch, 4 * host_us * args.steps + 500, mark=ev[0])
+    ev[1].record()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, timer)
+    enqueue_us = (time.perf_counter() - t0) * 1e6
+    ev[2].record()
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
+    dt = ev[1].elapsed_time(ev[2]) * 1e-3 / args.steps
     us[dom] = timer.avg_us()[dom]
+    hold_us = ev[0].elapsed_time(ev[1]) * 1e3
+    TIMINGS.append({"step": getattr(step, "__name__", "step"), "steps": args.steps,
+                    "gpu_us_per_step": round(dt * 1e6, 2),
+                    "host_us_per_step": round(enqueue_us / args.steps, 1),
+                    "queued": bool(hold_us >= enqueue_us)})
     return dt, us, dom
 
 
@@ -1071,6 +1123,8 @@ def main(argv=None):
            "tis_batch": run_tis, "stack32b_gemm": run_stack_gemm,
            "att32b_decode": run_att, "sync32b_requant": run_sync32b}[args.workload]
     line = run(args, torch, B, W)
+    if TIMINGS:
+        line["timing"] = TIMINGS
     print(json.dumps(line), flush=True)
     return 0
 
