@@ -27,18 +27,6 @@ __device__ __forceinline__ v4i mfma_i8x2(const v8i& w, const v8i& a, v4i acc) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(wh, ah, acc, 0, 0, 0);
 }
 
-__device__ __forceinline__ v8i load32(const uint8_t* p) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-  v8i r = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  return r;
-}
-
-__device__ __forceinline__ v8i zero8() {
-  v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
-  return r;
-}
-
 // Four fp32 results for C[m, n..n+3] -> bf16, bounds-checked store.
 __device__ __forceinline__ void store4(uint16_t* C, int64_t M, int64_t N, int64_t m, int64_t n,
                                        const float v[4]) {
@@ -87,10 +75,6 @@ __device__ __forceinline__ v8i buffer_load32(__amdgpu_buffer_rsrc_t r, int voff,
 // LDS the skinny kernel may use for its staged FP8 activation scales
 // (64 rows x K/128 floats: K up to 81,920 at 64 rows).
 constexpr int kSkinnyLdsBytes = 160 * 1024;
-
-__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int voff) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
-}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
