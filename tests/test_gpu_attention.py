@@ -10,14 +10,17 @@ batch, and element by element within two bf16 roundings plus 1e-3 of the
 output's rms.  Cases: group sizes 1 to 8, lengths 0, 1, a partial page and
 several thousand tokens, page sizes 16 and 5, tokens skipped through
 invalid block-table entries, lengths beyond the table (clamped), and the
-32B-class layout (40 query heads over 8 KV heads) on sampled sequences of
-the full 64-sequence batch; for the split: one long sequence cut over every
+32B-class layout (40 query heads over 8 KV heads) on all of the full
+64-sequence batch; for the split: one long sequence cut over every
 CU, hundreds of short sequences sharing workgroups, the most sequences it
 takes (2048), one-token pages with a workgroup range of more than 1024
 pages (its page table staged in several chunks), shapes it does not take
 (more than 8 KV heads, more than 2048 sequences, a workspace too small),
 and bitwise-repeatable results.
 """
+
+import functools
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -26,7 +29,7 @@ import torch
 from oracle import attention, kv
 from oracle.gemm import bf16_bits_to_f64, rel_frobenius
 from precision_rl_rollout_amd import binding, workloads
-from tests.gpu_util import announce, bits_to_dev, host
+from tests.gpu_util import announce, bits_to_dev, host, oracle_workers
 
 pytestmark = pytest.mark.gpu
 
@@ -61,10 +64,11 @@ def _gpu(p, ws="auto"):
     return host(out)
 
 
-def _check(got, p, label, rows=None):
-    ref = attention.decode_attention(p["q"], p["sq"], p["kc"], p["vc"], p["sk"], p["sv"],
-                                     p["table"], p["lens"], p["Hkv"], p["page"],
-                                     batch_rows=rows)
+def _check(got, p, label, rows=None, ref=None):
+    if ref is None:
+        ref = attention.decode_attention(p["q"], p["sq"], p["kc"], p["vc"], p["sk"], p["sv"],
+                                         p["table"], p["lens"], p["Hkv"], p["page"],
+                                         batch_rows=rows)
     g = got if rows is None else got[rows]
     err = rel_frobenius(g, ref)
     assert err <= TOL, f"{label}: relative Frobenius error {err:.3e}"
@@ -161,22 +165,36 @@ def test_skipped_tokens_and_clamped_lengths(ws):
     _check(got, dict(p, lens=np.array([40, 40, 40], np.int32)), "clamped lengths")
 
 
-@pytest.mark.parametrize("ws", WS)
-def test_full_32b_batch_sampled(ws):
+@functools.lru_cache(maxsize=1)
+def _full_32b_case():
+    """The 64-sequence 32B-class batch and the oracle's output for all of
+    it, computed once for both launch forms: sequences in pairs on worker
+    threads (each pair's output depends on that pair alone)."""
     cfg = workloads.ATT_32B
     B, Hq, Hkv, D, page = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["page"]
     lens = workloads.att_lengths(B, cfg["min_len"], cfg["max_len"], 0)
     table, num_slots = workloads.att_block_table(lens, page, 0)
-    announce(f"fp8_kv_decode_attention full 32B batch B{B} slots{num_slots} workspace {ws}")
     q = workloads.att_query(B, Hq, D, 0)
     kc = workloads.att_random_codes(num_slots, Hkv * D, 0)
     vc = workloads.att_random_codes(num_slots, Hkv * D, 1)
     # scales that keep the scores of random codes in a softmax-relevant range
     p = dict(q=q, sq=kv.kv_scale(q), kc=kc, vc=vc, sk=np.float32(2.0 ** -12),
              sv=np.float32(2.0 ** -8), table=table, lens=lens, Hkv=Hkv, page=page)
+    pairs = [list(range(b, min(B, b + 2))) for b in range(0, B, 2)]
+    with ThreadPoolExecutor(oracle_workers()) as ex:
+        parts = list(ex.map(lambda rows: attention.decode_attention(
+            q, p["sq"], kc, vc, p["sk"], p["sv"], table, lens, Hkv, page, batch_rows=rows),
+            pairs))
+    return p, np.concatenate(parts, axis=0), num_slots
+
+
+@pytest.mark.parametrize("ws", WS)
+def test_full_32b_batch(ws):
+    p, ref, num_slots = _full_32b_case()
+    B = p["q"].shape[0]
+    announce(f"fp8_kv_decode_attention full 32B batch B{B} slots{num_slots} workspace {ws}")
     got = _gpu(p, ws)
-    rows = [0, 17, 40, 63]
-    _check(got, p, "32B batch", rows=rows)
+    _check(got, p, "32B batch", ref=ref)
 
 
 def test_split_at_most_sequences():
