@@ -9,7 +9,7 @@ relative Frobenius error of at most 1e-3 against the fp64 result rounded
 once to bf16.  Cases: the 16 x 256 x 256 layer, ragged and edge shapes on
 both the decode (M <= 128) and the tiled (M > 128) paths, the 7B decode
 up/gate layer in full, the 32B decode sweep M = 1 .. 128, and the 32B
-prefill up/gate and down GEMMs (oracle on 1024 of the 8192 rows).
+prefill up/gate and down GEMMs (all 8192 rows).
 """
 
 import numpy as np
@@ -260,24 +260,18 @@ def test_full_32b_decode_sweep():
 @pytest.mark.parametrize("kind", ["fp8", "int8"])
 def test_full_32b_prefill(which, kind):
     """The 32B prefill GEMMs at full size (M 8192), compared with the oracle
-    element by element on 1024 of the 8192 output rows: the first and the
-    last 256-row tile in full and 512 rows drawn from the rest; every output
-    is finite."""
+    element by element on all 8192 x N outputs (the oracle's fp64 GEMM of
+    2.3 TFLOP takes tens of seconds on the host)."""
     down = which == "down"
     N, K = (5120, 27648) if down else (27648, 5120)
     p = workloads.gemm_problem(8192, N, K, True, seed=0, down=down)
-    rng = np.random.default_rng(K + (kind == "int8"))
-    rows = np.concatenate([np.arange(256), rng.choice(np.arange(256, 7936), 512, replace=False),
-                           np.arange(7936, 8192)])
-    rows.sort()
     announce(f"{kind} GEMM full 32B prefill {which} M8192 N{N} K{K}")
     if kind == "fp8":
         c = _gpu_fp8(p["A"], p["Wt"])
-        ref = _ref_fp8(p["A"], None, rows=rows,
+        ref = _ref_fp8(p["A"], None,
                        wq_sw=oracle_by_rows(quant.fp8_weight_block_quant, p["Wt"], 1024))
     else:
         c = _gpu_int8(p["A"], p["Wt"])
-        ref = _ref_int8(p["A"], None, rows=rows,
+        ref = _ref_int8(p["A"], None,
                         wq_sw=oracle_by_rows(quant.int8_weight_channel_quant, p["Wt"], 1024))
-    assert np.all(np.isfinite(gemm.bf16_bits_to_f64(c)))
-    _check(c[rows], ref, f"32B prefill {which} {kind} (1024 rows)")
+    _check(c, ref, f"32B prefill {which} {kind} (all rows)")
