@@ -131,7 +131,7 @@ def test_split_not_taken_falls_back():
     lens = np.full(2100, 3, dtype=np.int32)
     q = _build(2100, 8, 2, lens, 4, seed=2)
     announce("fp8_kv_decode_attention_ws 2100 sequences")
-    _check(_gpu(q, "auto"), q, "2100 sequences", rows=[0, 1000, 2099])
+    _check(_gpu(q, "auto"), q, "2100 sequences")
 
 
 def test_split_is_bitwise_repeatable():
@@ -203,7 +203,7 @@ def test_split_at_most_sequences():
     p = _build(2048, 8, 2, lens, 4, seed=2)
     assert binding.attention_workspace_bytes(2048, 8, 2, 128) > 0
     announce("fp8_kv_decode_attention_ws 2048 sequences")
-    _check(_gpu(p, "auto"), p, "2048 sequences", rows=[0, 1, 5, 1023, 2046, 2047])
+    _check(_gpu(p, "auto"), p, "2048 sequences")
 
 
 def test_split_long_ranges_of_one_token_pages():

@@ -136,17 +136,13 @@ def test_prefill_tail_split_over_k(M, N, K):
     last round runs that round's tile columns split over K (fp32 partial
     sums in the workspace, then a reduction): 8 row tiles x 33 column tiles
     on 256 compute units leave one column of 8 tiles, split 4 ways.  Against
-    the oracle on 512 rows (the first and last row tiles and 256 drawn
-    rows), with and without the workspace; INT8 must agree bit for bit
+    the oracle on every output, with and without the workspace; INT8 must
+    agree bit for bit
     between the two (exact int32 partial sums, the same final scaling).
     The second shape is ragged: 2000 rows, 254 columns in the split part
     (not a multiple of 4)."""
     assert binding.gemm_workspace_bytes(M, N, K) > 0, "no tail split planned for this shape"
     p = workloads.gemm_problem(M, N, K, True, seed=7)
-    rng = np.random.default_rng(M + N)
-    last = (M - 1) // 256 * 256
-    rows = np.unique(np.concatenate([np.arange(256), np.arange(last, M),
-                                     rng.choice(np.arange(256, last), 256, replace=False)]))
     announce(f"prefill tail split over K: M{M} N{N} K{K}")
     a8 = binding.fp8_act_token_quant(bits_to_dev(p["A"]))
     w8 = binding.fp8_weight_block_quant(bits_to_dev(p["Wt"]))
@@ -161,11 +157,11 @@ def test_prefill_tail_split_over_k(M, N, K):
             out[kind, ws] = host(c.t)
             assert c.intact(), "write outside C"
     assert np.array_equal(out["int8", None], out["int8", "auto"]), "int8 split != one pass"
-    ref8 = _ref_fp8(p["A"], p["Wt"], rows=rows)
-    refi = _ref_int8(p["A"], p["Wt"], rows=rows)
+    ref8 = _ref_fp8(p["A"], p["Wt"])
+    refi = _ref_int8(p["A"], p["Wt"])
     for ws in (None, "auto"):
-        _check(out["fp8", ws][rows], ref8, f"fp8 M{M} N{N} K{K} workspace={ws}")
-        _check(out["int8", ws][rows], refi, f"int8 M{M} N{N} K{K} workspace={ws}")
+        _check(out["fp8", ws], ref8, f"fp8 M{M} N{N} K{K} workspace={ws}")
+        _check(out["int8", ws], refi, f"int8 M{M} N{N} K{K} workspace={ws}")
 
 
 def test_gemm_k_zero_writes_zeros_and_empty_is_noop():
