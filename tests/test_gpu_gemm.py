@@ -52,15 +52,15 @@ def _gpu_int8(A, Wt, w_dev=None):
     return out
 
 
-def _ref_fp8(A, Wt, rows=None, wq_sw=None):
-    aq, sa = quant.fp8_act_token_quant(A if rows is None else A[rows])
+def _ref_fp8(A, Wt, wq_sw=None):
+    aq, sa = quant.fp8_act_token_quant(A)
     wq, sw = wq_sw if wq_sw is not None else quant.fp8_weight_block_quant(Wt)
     c64 = gemm.w8a8_block_gemm(aq, sa, wq, sw)
     return c64, gemm.round_bf16(c64)
 
 
-def _ref_int8(A, Wt, rows=None, wq_sw=None):
-    aq, sa = quant.int8_act_token_quant(A if rows is None else A[rows])
+def _ref_int8(A, Wt, wq_sw=None):
+    aq, sa = quant.int8_act_token_quant(A)
     wq, sw = wq_sw if wq_sw is not None else quant.int8_weight_channel_quant(Wt)
     c64 = gemm.int8_channel_gemm(aq, sa, wq, sw)
     return c64, gemm.round_bf16(c64)
