@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define PRR_ABI_VERSION 10
+#define PRR_ABI_VERSION 11
 
 typedef enum prr_status {
   PRR_OK = 0,
@@ -393,6 +393,35 @@ prr_status fp8_kv_cache_write_recalibrate(const uint16_t* kv_bf16,
                                           int64_t num_slots, float* new_scale,
                                           void* workspace, int64_t workspace_bytes,
                                           hipStream_t stream);
+
+/*
+ * fp8_kv_cache_write_recalibrate_multi -- fp8_kv_cache_write_recalibrate
+ * for up to PRR_MAX_KV_JOBS tensors of one step that share the slot mapping
+ * (K and V: FP8-RL, abstract, item (ii)), in one launch over all of their
+ * rows and one over their partial maxima; each job's results are those of
+ * the single call.
+ *   jobs   host array of `count` prr_kv_job: kv_bf16 [T, C], the scale it is
+ *          written with, its cache [num_slots, C], its new_scale (which may
+ *          be its own scale word).  The new_scale words must be distinct
+ *          (PRR_ERR_INVALID_ARG otherwise); caches and the other jobs'
+ *          scales must not overlap what another job writes.
+ *   count  0 .. PRR_MAX_KV_JOBS (0: nothing is done).
+ *   slot_mapping, T, C, num_slots: shared, as fp8_kv_cache_write.
+ *   workspace  count x PRR_KV_RECAL_WORKSPACE_BYTES bytes at least, 16-byte
+ *          aligned (job j's partials at byte j x PRR_KV_RECAL_WORKSPACE_BYTES),
+ *          for the call's duration only; may be NULL when T x C == 0.
+ */
+#define PRR_MAX_KV_JOBS 16
+typedef struct prr_kv_job {
+  const uint16_t* kv_bf16;
+  const float* scale;
+  uint8_t* cache;
+  float* new_scale;
+} prr_kv_job;
+prr_status fp8_kv_cache_write_recalibrate_multi(const prr_kv_job* jobs, int64_t count,
+                                                const int64_t* slot_mapping, int64_t T,
+                                                int64_t C, int64_t num_slots, void* workspace,
+                                                int64_t workspace_bytes, hipStream_t stream);
 
 /*
  * fp8_kv_decode_attention -- the read side of the FP8 KV cache (FP8-RL,

@@ -52,16 +52,22 @@ _SIGNATURES = {
     "w8a8_int8_channel_gemm_ws": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64, _P],
     "w8a8_block_gemm_scratch": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P],
     "fp8_kv_cache_write_recalibrate": [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _P],
+    "fp8_kv_cache_write_recalibrate_multi": [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P],
     "fp8_weight_block_quant_multi": [_P, _I64, _P],
     "int8_weight_channel_quant_multi": [_P, _I64, _P],
 }
 
 MAX_WEIGHT_JOBS = 16
+MAX_KV_JOBS = 16
 
 
 class WeightJob(ctypes.Structure):
     """prr_weight_job: one whole weight and its outputs."""
     _fields_ = [("w_bf16", _P), ("N", _I64), ("K", _I64), ("q", _P), ("scale", _P)]
+
+class KvJob(ctypes.Structure):
+    """prr_kv_job: one tensor of a step's KV cache write + recalibration."""
+    _fields_ = [("kv_bf16", _P), ("scale", _P), ("cache", _P), ("new_scale", _P)]
 
 IS_TRUNCATE = 0     # TIS: min(ratio, cap)
 IS_MASK = 1         # MIS: ratio, or 0 above the cap
@@ -70,7 +76,7 @@ _lib = None
 
 # PRR_ABI_VERSION of the signatures below; a library of another version is
 # refused at load time.
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 
 class PrrError(RuntimeError):
@@ -471,6 +477,48 @@ def fp8_kv_cache_write_recalibrate(kv: torch.Tensor, slot_mapping: torch.Tensor,
                                                  scale.data_ptr(), _ptr(cache), cache.shape[0],
                                                  ns.data_ptr(), _ptr(workspace),
                                                  workspace.numel(), _stream(kv)))
+    return ns
+
+
+def fp8_kv_cache_write_recalibrate_multi(kvs, slot_mapping: torch.Tensor, scales, caches,
+                                         new_scales=None, workspace=None):
+    """fp8_kv_cache_write_recalibrate for several tensors sharing the slot
+    mapping (K and V of a step), in one launch over their rows: kvs, scales,
+    caches and new_scales are sequences of the single call's arguments
+    (new_scales[i] may be scales[i]; None: new tensors).  workspace: a uint8
+    CUDA tensor of at least len(kvs) x KV_RECAL_WORKSPACE_BYTES, or None for
+    a new one.  Returns the new scales."""
+    n = len(kvs)
+    if not (len(scales) == len(caches) == n) or n > MAX_KV_JOBS:
+        raise ValueError(f"kvs, scales, caches: {n} each, at most {MAX_KV_JOBS}")
+    if n == 0:
+        return []
+    kvs = [_bf16_bits(k, "kv") for k in kvs]
+    T, C = kvs[0].shape
+    if any(k.shape != (T, C) for k in kvs):
+        raise ValueError("kvs: every tensor [T, C] alike")
+    _operand(slot_mapping, torch.int64, (T,), "slot_mapping")
+    num_slots = caches[0].shape[0] if caches[0].dim() == 2 else -1
+    for sc, ca in zip(scales, caches):
+        _operand(sc, torch.float32, (1,), "scale")
+        if ca.dtype != torch.uint8 or ca.dim() != 2 or tuple(ca.shape) != (num_slots, C) \
+                or not ca.is_cuda or not ca.is_contiguous():
+            raise ValueError(f"caches: contiguous CUDA uint8 tensors [num_slots, {C}], all alike")
+    if new_scales is None:
+        new_scales = [None] * n
+    ns = [_out(x, torch.float32, (1,), kvs[0], "new_scale") for x in new_scales]
+    need = n * KV_RECAL_WORKSPACE_BYTES
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=kvs[0].device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace: expected a contiguous CUDA uint8 tensor")
+    jobs = (KvJob * n)(*[KvJob(_ptr(k), sc.data_ptr(), _ptr(ca), x.data_ptr())
+                         for k, sc, ca, x in zip(kvs, scales, caches, ns)])
+    _check("fp8_kv_cache_write_recalibrate_multi",
+           load().fp8_kv_cache_write_recalibrate_multi(ctypes.addressof(jobs), n,
+                                                       _ptr(slot_mapping), T, C, num_slots,
+                                                       _ptr(workspace), workspace.numel(),
+                                                       _stream(kvs[0])))
     return ns
 
 

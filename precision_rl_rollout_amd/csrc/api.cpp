@@ -366,24 +366,65 @@ prr_status fp8_kv_cache_write(const uint16_t* kv_bf16, const int64_t* slot_mappi
       prr::launch_fp8_kv_cache_write(kv_bf16, slot_mapping, T, C, scale, cache, num_slots, stream));
 }
 
+// Checks of the write + recalibration calls; fills *kj.  Per job: new_scale
+// always (an empty batch still writes 0); the rows, scale and workspace
+// when T x C > 0, the cache when num_slots > 0; new_scale words distinct.
+static prr_status kv_recal_jobs(const prr_kv_job* jobs, int64_t count,
+                                const int64_t* slot_mapping, int64_t T, int64_t C,
+                                int64_t num_slots, const void* workspace, int64_t workspace_bytes,
+                                prr::KvJobs* kj) {
+  static_assert(PRR_KV_RECAL_WORKSPACE_BYTES == 4 * prr::kKvRecalParts, "partials workspace");
+  static_assert(PRR_MAX_KV_JOBS == prr::kMaxKvJobs, "job limit");
+  PRR_TRY(check_dims(T, C, num_slots));
+  if (count < 0 || count > PRR_MAX_KV_JOBS || workspace_bytes < 0) return PRR_ERR_INVALID_ARG;
+  if (count > 0 && jobs == nullptr) return PRR_ERR_INVALID_ARG;
+  const bool rows = T > 0 && C > 0;
+  if (rows && count > 0) {
+    PRR_TRY(check_ptrs({slot_mapping, workspace}));
+    if (workspace_bytes < count * (int64_t)PRR_KV_RECAL_WORKSPACE_BYTES) return PRR_ERR_INVALID_ARG;
+  }
+  kj->count = (int)count;
+  for (int64_t j = 0; j < count; ++j) {
+    const prr_kv_job& jb = jobs[j];
+    PRR_TRY(check_ptrs({jb.new_scale}));
+    if (rows) {
+      PRR_TRY(check_ptrs({jb.kv_bf16, jb.scale}));
+      if (num_slots > 0) PRR_TRY(check_ptrs({jb.cache}));
+    }
+    for (int64_t i = 0; i < j; ++i)
+      if (jobs[i].new_scale == jb.new_scale) return PRR_ERR_INVALID_ARG;
+    kj->kv[j] = jb.kv_bf16;
+    kj->scale[j] = jb.scale;
+    kj->cache[j] = num_slots > 0 ? jb.cache : nullptr;
+    kj->new_scale[j] = jb.new_scale;
+  }
+  return PRR_OK;
+}
+
 prr_status fp8_kv_cache_write_recalibrate(const uint16_t* kv_bf16,
                                           const int64_t* slot_mapping, int64_t T, int64_t C,
                                           const float* scale, uint8_t* cache, int64_t num_slots,
                                           float* new_scale, void* workspace,
                                           int64_t workspace_bytes, hipStream_t stream) {
-  static_assert(PRR_KV_RECAL_WORKSPACE_BYTES == 4 * prr::kKvRecalParts, "partials workspace");
-  PRR_TRY(check_dims(T, C, num_slots));
-  PRR_TRY(check_ptrs({new_scale}));
-  if (workspace_bytes < 0) return PRR_ERR_INVALID_ARG;
-  if (T > 0 && C > 0) {
-    PRR_TRY(check_ptrs({kv_bf16, slot_mapping, scale, workspace}));
-    if (workspace_bytes < PRR_KV_RECAL_WORKSPACE_BYTES) return PRR_ERR_INVALID_ARG;
-    if (num_slots > 0) PRR_TRY(check_ptrs({cache}));
-  }
+  const prr_kv_job job{kv_bf16, scale, cache, new_scale};
+  prr::KvJobs kj;
+  PRR_TRY(kv_recal_jobs(&job, 1, slot_mapping, T, C, num_slots, workspace, workspace_bytes, &kj));
   PRR_TRY(check_device());
   return from_hip(prr::launch_fp8_kv_cache_write_recalibrate(
-      kv_bf16, slot_mapping, T, C, scale, num_slots > 0 ? cache : nullptr, num_slots, new_scale,
-      static_cast<uint32_t*>(workspace), stream));
+      kj, slot_mapping, T, C, num_slots, static_cast<uint32_t*>(workspace), stream));
+}
+
+prr_status fp8_kv_cache_write_recalibrate_multi(const prr_kv_job* jobs, int64_t count,
+                                                const int64_t* slot_mapping, int64_t T,
+                                                int64_t C, int64_t num_slots, void* workspace,
+                                                int64_t workspace_bytes, hipStream_t stream) {
+  prr::KvJobs kj;
+  PRR_TRY(kv_recal_jobs(jobs, count, slot_mapping, T, C, num_slots, workspace, workspace_bytes,
+                        &kj));
+  if (count == 0) return PRR_OK;
+  PRR_TRY(check_device());
+  return from_hip(prr::launch_fp8_kv_cache_write_recalibrate(
+      kj, slot_mapping, T, C, num_slots, static_cast<uint32_t*>(workspace), stream));
 }
 
 prr_status tis_token_weights(const float* logp_train, const float* logp_rollout,

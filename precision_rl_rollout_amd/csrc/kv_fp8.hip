@@ -91,13 +91,13 @@ constexpr int kWriteChunks = 4;
 // with a plain store; kv_part_scale_kernel then folds the partials into the
 // new scale.  (One atomic maximum per workgroup on the single scale word
 // serializes on that word: at 2048 workgroups it added ~9 us to a 12 us
-// write; spread over 64 words it added nothing.)  The grid is capped at kKvRecalParts workgroups, which loop
-// over the row groups, so the partials fit the caller's fixed workspace.  No
-// thread leaves before the workgroup's reduction: rows past T and rows with
-// no slot only skip their stores.
-
-template <bool kVec, bool kRecal = false>
-__global__ __launch_bounds__(256) void kv_cache_write_kernel(
+// write; spread over 64 words it added nothing.)  The grid is capped at
+// kKvRecalParts workgroups, which loop over the row groups, so the partials
+// fit the caller's fixed workspace.  No thread leaves before the
+// workgroup's reduction: rows past T and rows with no slot only skip their
+// stores.
+template <bool kVec, bool kRecal>
+__device__ __forceinline__ void kv_write_rows(
     const uint16_t* __restrict__ kv, const int64_t* __restrict__ slots, int64_t T, int64_t C,
     const float* __restrict__ scale, uint8_t* __restrict__ cache, int64_t num_slots, int rpw,
     uint32_t* __restrict__ part) {
@@ -172,64 +172,88 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
   }
 }
 
-// The new scale from the n partial maxima: fl32(amax / 448), +0.0 when
-// every partial is 0 (an all-zero or empty batch).  One workgroup.  Its
-// trace duration, ~4 us, is the kernel boundary (the same as the one-thread
-// clear kernel's after a large write): two 16-byte loads per thread instead
-// of this loop measured the same.
-__global__ __launch_bounds__(256) void kv_part_scale_kernel(const uint32_t* __restrict__ part,
-                                                            int n, float* __restrict__ scale) {
+template <bool kVec>
+__global__ __launch_bounds__(256) void kv_cache_write_kernel(
+    const uint16_t* __restrict__ kv, const int64_t* __restrict__ slots, int64_t T, int64_t C,
+    const float* __restrict__ scale, uint8_t* __restrict__ cache, int64_t num_slots, int rpw) {
+  kv_write_rows<kVec, false>(kv, slots, T, C, scale, cache, num_slots, rpw, nullptr);
+}
+
+// The write with recalibration for several tensors sharing the slot mapping
+// (K and V of a step): workgroup (x, j) works on job j, its partials at
+// part + j kKvRecalParts.
+template <bool kVec>
+__global__ __launch_bounds__(256) void kv_cache_write_recal_kernel(
+    KvJobs jobs, const int64_t* __restrict__ slots, int64_t T, int64_t C, int64_t num_slots,
+    int rpw, uint32_t* __restrict__ part) {
+  const int j = blockIdx.y;
+  kv_write_rows<kVec, true>(jobs.kv[j], slots, T, C, jobs.scale[j], jobs.cache[j], num_slots,
+                            rpw, part + (int64_t)j * kKvRecalParts);
+}
+
+// The new scale of job blockIdx.x from its n partial maxima: fl32(amax /
+// 448), +0.0 when every partial is 0 (an all-zero or empty batch).  One
+// workgroup per job.  Its trace duration, ~4 us, is the kernel boundary
+// (the same as the one-thread clear kernel's after a large write): two
+// 16-byte loads per thread instead of this loop measured the same.
+__global__ __launch_bounds__(256) void kv_part_scale_kernel(KvJobs jobs,
+                                                            const uint32_t* __restrict__ part,
+                                                            int n) {
   __shared__ uint32_t red[4];
+  const uint32_t* pj = part + (int64_t)blockIdx.x * kKvRecalParts;
   uint32_t m = 0;
-  for (int i = threadIdx.x; i < n; i += 256) m = max(m, part[i]);
+  for (int i = threadIdx.x; i < n; i += 256) m = max(m, pj[i]);
   m = wave_max_u32(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     m = max(max(red[0], red[1]), max(red[2], red[3]));
-    *scale = m ? div_rn(__uint_as_float(m << 16), kFp8Max) : 0.0f;
+    *jobs.new_scale[blockIdx.x] = m ? div_rn(__uint_as_float(m << 16), kFp8Max) : 0.0f;
   }
 }
 
-hipError_t launch_fp8_kv_cache_write(const uint16_t* kv, const int64_t* slots, int64_t T,
-                                     int64_t C, const float* scale, uint8_t* cache,
-                                     int64_t num_slots, hipStream_t stream) {
+static int kv_rows_per_wg(int64_t C) {
   // Threads per row: enough for kWriteChunks chunks each (at most 256).
   const int64_t chunks = (C + 7) / 8;
   const int64_t per = (chunks + kWriteChunks - 1) / kWriteChunks;
   int rpw = 1;                                    // rows per workgroup
   while (rpw < 256 && 256 / (rpw * 2) >= per) rpw *= 2;
+  return rpw;
+}
+
+hipError_t launch_fp8_kv_cache_write(const uint16_t* kv, const int64_t* slots, int64_t T,
+                                     int64_t C, const float* scale, uint8_t* cache,
+                                     int64_t num_slots, hipStream_t stream) {
+  const int rpw = kv_rows_per_wg(C);
   const unsigned grid = (unsigned)((T + rpw - 1) / rpw);
   if (C % 8 == 0)
     hipLaunchKernelGGL(kv_cache_write_kernel<true>, dim3(grid), dim3(256), 0, stream, kv, slots,
-                       T, C, scale, cache, num_slots, rpw, nullptr);
+                       T, C, scale, cache, num_slots, rpw);
   else
     hipLaunchKernelGGL(kv_cache_write_kernel<false>, dim3(grid), dim3(256), 0, stream, kv,
-                       slots, T, C, scale, cache, num_slots, rpw, nullptr);
+                       slots, T, C, scale, cache, num_slots, rpw);
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_kv_cache_write_recalibrate(const uint16_t* kv, const int64_t* slots,
-                                                 int64_t T, int64_t C, const float* scale,
-                                                 uint8_t* cache, int64_t num_slots,
-                                                 float* new_scale, uint32_t* part,
-                                                 hipStream_t stream) {
+hipError_t launch_fp8_kv_cache_write_recalibrate(const KvJobs& jobs, const int64_t* slots,
+                                                 int64_t T, int64_t C, int64_t num_slots,
+                                                 uint32_t* part, hipStream_t stream) {
+  if (jobs.count < 1) return hipSuccess;
   int grid = 0;
   if (T > 0 && C > 0) {
-    const int64_t chunks = (C + 7) / 8;
-    const int64_t per = (chunks + kWriteChunks - 1) / kWriteChunks;
-    int rpw = 1;
-    while (rpw < 256 && 256 / (rpw * 2) >= per) rpw *= 2;
+    const int rpw = kv_rows_per_wg(C);
     const int64_t groups = (T + rpw - 1) / rpw;
     grid = (int)(groups < kKvRecalParts ? groups : kKvRecalParts);
+    const dim3 g((unsigned)grid, (unsigned)jobs.count);
     if (C % 8 == 0)
-      hipLaunchKernelGGL((kv_cache_write_kernel<true, true>), dim3(grid), dim3(256), 0, stream, kv,
-                         slots, T, C, scale, cache, num_slots, rpw, part);
+      hipLaunchKernelGGL(kv_cache_write_recal_kernel<true>, g, dim3(256), 0, stream, jobs, slots,
+                         T, C, num_slots, rpw, part);
     else
-      hipLaunchKernelGGL((kv_cache_write_kernel<false, true>), dim3(grid), dim3(256), 0, stream,
-                         kv, slots, T, C, scale, cache, num_slots, rpw, part);
+      hipLaunchKernelGGL(kv_cache_write_recal_kernel<false>, g, dim3(256), 0, stream, jobs,
+                         slots, T, C, num_slots, rpw, part);
   }
-  hipLaunchKernelGGL(kv_part_scale_kernel, dim3(1), dim3(256), 0, stream, part, grid, new_scale);
+  hipLaunchKernelGGL(kv_part_scale_kernel, dim3((unsigned)jobs.count), dim3(256), 0, stream, jobs,
+                     part, grid);
   return hipGetLastError();
 }
 

@@ -52,15 +52,23 @@ hipError_t launch_fp8_kv_scale_recalibrate(const uint16_t* x, int64_t n, float* 
 hipError_t launch_fp8_kv_cache_write(const uint16_t* kv, const int64_t* slots, int64_t T,
                                      int64_t C, const float* scale, uint8_t* cache,
                                      int64_t num_slots, hipStream_t stream);
-// Both in one pass over kv: the write with `scale`, and new_scale
-// recalibrated from kv through per-workgroup maxima in `part` (at most
-// kKvRecalParts words, written before they are read).
+// Both in one pass over the rows, for up to kMaxKvJobs tensors sharing the
+// slot mapping (K and V of a step): job j's rows written into cache[j] with
+// scale[j], and new_scale[j] recalibrated from them through per-workgroup
+// maxima in part + j kKvRecalParts (at most kKvRecalParts words each,
+// written before they are read).
 constexpr int kKvRecalParts = 2048;
-hipError_t launch_fp8_kv_cache_write_recalibrate(const uint16_t* kv, const int64_t* slots,
-                                                 int64_t T, int64_t C, const float* scale,
-                                                 uint8_t* cache, int64_t num_slots,
-                                                 float* new_scale, uint32_t* part,
-                                                 hipStream_t stream);
+constexpr int kMaxKvJobs = 16;
+struct KvJobs {
+  const uint16_t* kv[kMaxKvJobs];
+  const float* scale[kMaxKvJobs];
+  uint8_t* cache[kMaxKvJobs];
+  float* new_scale[kMaxKvJobs];
+  int count;
+};
+hipError_t launch_fp8_kv_cache_write_recalibrate(const KvJobs& jobs, const int64_t* slots,
+                                                 int64_t T, int64_t C, int64_t num_slots,
+                                                 uint32_t* part, hipStream_t stream);
 
 hipError_t launch_tis_token_weights(const float* lp_train, const float* lp_rollout,
                                     const uint8_t* mask, int64_t B, int64_t T, float cap,

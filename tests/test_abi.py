@@ -57,6 +57,7 @@ def test_header_declares_the_boundary():
                      "fp8_kv_decode_attention_ws", "w8a8_block_gemm_ws",
                      "w8a8_int8_channel_gemm_ws", "w8a8_block_gemm_scratch",
                      "fp8_weight_block_quant_multi", "int8_weight_channel_quant_multi",
+                     "fp8_kv_cache_write_recalibrate_multi",
                      "prr_status_string", "prr_abi_version"}
 
 
@@ -388,3 +389,39 @@ def test_multi_weight_argument_checks(fn):
     assert c(empty, 2) == OK                              # empty jobs: no device work
     if not _gpu_visible():
         assert c(one, 1) == NO_DEVICE
+
+
+def test_kv_write_recalibrate_multi_argument_checks():
+    J = binding.KvJob
+    WSB = binding.KV_RECAL_WORKSPACE_BYTES
+    c = lambda jobs, n, T=4, C=8, S=16, ws=FAKE + 8192, wsb=2 * WSB: binding.call(
+        "fp8_kv_cache_write_recalibrate_multi", None if jobs is None else ctypes.addressof(jobs),
+        n, FAKE, T, C, S, ws, wsb, None)
+    good = lambda k: J(FAKE + 16 * k, FAKE + 256 + 16 * k, FAKE + 512 + 16 * k, FAKE + 1024 + 16 * k)
+    two = (J * 2)(good(0), good(1))
+    assert binding.MAX_KV_JOBS == 16
+    assert c(None, 0) == OK                                # nothing to do
+    assert c(None, 1) == INVALID                           # jobs missing
+    assert c(two, -1) == INVALID
+    assert c(two, binding.MAX_KV_JOBS + 1) == INVALID
+    assert c(two, 2, T=-1) == INVALID
+    assert c(two, 2, wsb=2 * WSB - 4) == INVALID           # a workspace slot per job
+    assert c(two, 2, ws=None) == INVALID
+    assert c(two, 2, ws=ODD) == MISALIGNED
+    for field in ("kv_bf16", "scale", "cache", "new_scale"):
+        for v, want in ((None, INVALID), (ODD, MISALIGNED)):
+            bad = good(1)
+            setattr(bad, field, v)
+            assert c((J * 2)(good(0), bad), 2) == want, (field, v)
+    dup = good(1)
+    dup.new_scale = good(0).new_scale                      # the new scales must be distinct
+    assert c((J * 2)(good(0), dup), 2) == INVALID
+    if not _gpu_visible():
+        assert c(two, 2) == NO_DEVICE
+        # a new scale may be its own job's scale word (updated in place)
+        inplace = good(0)
+        inplace.new_scale = inplace.scale
+        assert c((J * 1)(inplace), 1, wsb=WSB) == NO_DEVICE
+        # an empty batch: rows, caches and workspace unused; the new scales are set
+        empty = (J * 2)(J(None, None, None, FAKE), J(None, None, None, FAKE + 16))
+        assert c(empty, 2, T=0, ws=None, wsb=0) == NO_DEVICE

@@ -282,3 +282,77 @@ def test_full_32b_prefill_write_recalibrate():
     got, got_s, want, want_s, *_ = _fused_case(T, C, S, seed=0)
     assert np.array_equal(got, want)
     assert _f32_bits(got_s) == _f32_bits(want_s)
+
+
+# ----------------------------------------- write + recalibrate, several tensors
+def _multi_case(T, C, num_slots, seeds, pad_every=0, inplace=False):
+    """Several tensors of one step (K, V, ...) sharing the slot mapping, in
+    one fp8_kv_cache_write_recalibrate_multi call; each against the oracle's
+    write with its earlier scale and its new scale."""
+    slots = workloads.kv_slot_mapping(T, num_slots, 16, seeds[0], pad_every) if T else \
+        np.zeros(0, dtype=np.int64)
+    xs, olds, cache0s = [], [], []
+    for i, sd in enumerate(seeds):
+        xs.append(workloads.kv_rows(T, C, sd, "KV"[i % 2]))
+        olds.append(kv.kv_scale(workloads.kv_rows(max(T, 1), max(C, 1), sd + 500, "KV"[i % 2])))
+        cache0s.append(np.full((num_slots, C), CANARY, dtype=np.uint8))
+    scales = [torch.tensor([s], dtype=torch.float32, device="cuda:0") for s in olds]
+    caches = [torch.from_numpy(c).cuda() for c in cache0s]
+    news = scales if inplace else None
+    got_s = binding.fp8_kv_cache_write_recalibrate_multi(
+        [bits_to_dev(x) for x in xs], torch.from_numpy(slots).cuda(), scales, caches,
+        new_scales=news)
+    for i in range(len(seeds)):
+        want = kv.kv_cache_write(cache0s[i], xs[i], slots, olds[i]) if T else cache0s[i]
+        assert np.array_equal(host(caches[i]), want), f"job {i}"
+        assert _f32_bits(host(got_s[i])[0]) == _f32_bits(kv.kv_scale(xs[i])), f"job {i}"
+
+
+@pytest.mark.parametrize("T,C,num_slots,pad", [(1, 8, 16, 0), (128, 1024, 512, 0),
+                                               (333, 1001, 1024, 5), (1000, 256, 4096, 9)])
+def test_write_recalibrate_multi_k_and_v(T, C, num_slots, pad):
+    announce(f"fp8_kv_cache_write_recalibrate_multi K+V T{T} C{C} slots{num_slots} pad{pad}")
+    _multi_case(T, C, num_slots, seeds=[T + 1, T + 2], pad_every=pad)
+
+
+def test_write_recalibrate_multi_three_in_place():
+    announce("fp8_kv_cache_write_recalibrate_multi 3 jobs in place T300 C136")
+    _multi_case(300, 136, 1024, seeds=[7, 8, 9], pad_every=4, inplace=True)
+
+
+def test_write_recalibrate_multi_equals_single_calls():
+    T, C, S = 2000, 1024, 8192
+    slots = torch.from_numpy(workloads.kv_slot_mapping(T, S, 16, 61, 11)).cuda()
+    xk = bits_to_dev(workloads.kv_rows(T, C, 61, "K"))
+    xv = bits_to_dev(workloads.kv_rows(T, C, 62, "V"))
+    sk = binding.fp8_kv_scale_recalibrate(bits_to_dev(workloads.kv_rows(T, C, 63, "K")))
+    sv = binding.fp8_kv_scale_recalibrate(bits_to_dev(workloads.kv_rows(T, C, 64, "V")))
+    announce("fp8_kv_cache_write_recalibrate_multi against two single calls")
+    ck1 = torch.full((S, C), CANARY, dtype=torch.uint8, device="cuda:0")
+    cv1, ck2, cv2 = ck1.clone(), ck1.clone(), ck1.clone()
+    nk1 = binding.fp8_kv_cache_write_recalibrate(xk, slots, sk, ck1)
+    nv1 = binding.fp8_kv_cache_write_recalibrate(xv, slots, sv, cv1)
+    nk2, nv2 = binding.fp8_kv_cache_write_recalibrate_multi([xk, xv], slots, [sk, sv], [ck2, cv2])
+    torch.cuda.synchronize()
+    assert torch.equal(ck1, ck2) and torch.equal(cv1, cv2)
+    assert torch.equal(nk1.view(torch.int32), nk2.view(torch.int32))
+    assert torch.equal(nv1.view(torch.int32), nv2.view(torch.int32))
+
+
+def test_write_recalibrate_multi_empty_batch():
+    announce("fp8_kv_cache_write_recalibrate_multi: empty batch")
+    s = [torch.tensor([0.5], dtype=torch.float32, device="cuda:0") for _ in range(2)]
+    caches = [torch.full((16, 8), CANARY, dtype=torch.uint8, device="cuda:0") for _ in range(2)]
+    empty = torch.empty((0, 8), dtype=torch.int16, device="cuda:0")
+    news = binding.fp8_kv_cache_write_recalibrate_multi(
+        [empty, empty], torch.empty(0, dtype=torch.int64, device="cuda:0"), s, caches)
+    torch.cuda.synchronize()
+    assert all(_f32_bits(host(n)[0]) == 0 for n in news)
+    assert all(bool(torch.all(c == CANARY)) for c in caches)
+
+
+def test_full_32b_prefill_write_recalibrate_multi():
+    cfg = workloads.KV_32B
+    T, C, S = cfg["T"], cfg["C"], cfg["num_slots"]
+    announce(f"fp8_kv_cache_write_recalibrate_multi full K+V T{T} C{C} slots{S}")
+    _multi_case(T, C, S, seeds=[0, 1])
