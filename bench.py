@@ -23,8 +23,9 @@ the CPU oracle on the same GEMM (a row sample of the prefill one).
 Other workloads (``--workload``): ``decode32b_sweep`` (GEMMs at M = 1..128,
 N 27648, K 5120, cold weights), ``prefill32b`` (M 8192 up/gate and down
 GEMMs, TFLOP/s), ``stack32b_requant`` (FP8 and INT8 re-quantization of a
-32B-class layer's seven weights), ``kv32b_prefill`` (FP8 KV-cache scale
-recalibration and quantize-on-write of a 16,384-token prefill),
+32B-class layer's seven weights), ``kv32b_prefill`` (FP8 KV-cache
+quantize-on-write and scale recalibration of a 16,384-token prefill's K
+and V in one call, beside the per-tensor and the separate calls),
 ``moe_decode`` (a 128-expert top-8 decode layer: weight re-quantization of
 every expert, activation quantization, the grouped GEMM), ``tis_batch``
 (TIS and MIS token weights of 1024 responses padded to 8192 tokens),
@@ -697,8 +698,16 @@ def run_stack_gemm(args, torch, B, W):
 
 def run_kv32b(args, torch, B, W):
     """FP8 KV cache of a 32B-class layer for a 16,384-token prefill: per
-    step, recalibrate the K and V scales on the new rows and write both into
-    a 65,536-slot cache (16-slot pages in random order)."""
+    step, the K and V rows written into a 65,536-slot cache (16-slot pages
+    in random order) with the scales the previous step calibrated, and the
+    next step's scales recalibrated from them.
+
+    value / roofline: the step as one call for K and V
+    (fp8_kv_cache_write_recalibrate_multi), algorithmic bytes (both
+    tensors' rows read once, their codes written, the slot mapping, the
+    scales) per second.  `forms` times the same step as one one-pass call
+    per tensor, and as the separate recalibration and write calls (which
+    read the rows twice), against the same algorithmic bytes."""
     cfg = W.KV_32B
     T, C, S = cfg["T"], cfg["C"], cfg["num_slots"]
     kb, vb = W.kv_rows(T, C, 0, "K"), W.kv_rows(T, C, 0, "V")
@@ -710,41 +719,17 @@ def run_kv32b(args, torch, B, W):
     vc = torch.zeros_like(kc)
     ks = torch.empty(1, dtype=torch.float32, device="cuda:0")
     vs = torch.empty_like(ks)
-
-    def step(_i, timer=None):
-        calls = [("fp8_kv_scale_recalibrate", lambda: B.fp8_kv_scale_recalibrate(k, out=ks)),
-                 ("fp8_kv_scale_recalibrate", lambda: B.fp8_kv_scale_recalibrate(v, out=vs)),
-                 ("fp8_kv_cache_write", lambda: B.fp8_kv_cache_write(k, slots, ks, kc)),
-                 ("fp8_kv_cache_write", lambda: B.fp8_kv_cache_write(v, slots, vs, vc))]
-        for name, fn in calls:
-            timer.run(name, fn) if timer else fn()
-    dt, us, _ = timed_steps(torch, step, args)
-    b_recal = 2 * T * C + 4
-    b_write = 3 * T * C + 8 * T + 4
-    step_bytes = 2 * b_recal + 2 * b_write
-    line = {"metric": METRIC, "value": round(step_bytes / dt / 1e9, 1), "unit": "GB/s",
-            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "vs_baseline": None,
-            "dtype": "fp8e4m3", "data": "synthetic",
-            "config": {"workload": "kv32b_prefill", "tokens": T, "row": C, "slots": S},
-            "roofline": {"bound": "hbm", "kernel": "fp8_kv_cache_write",
-                         "achieved": round(b_write / us["fp8_kv_cache_write"] / 1e3, 1),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(b_write / us["fp8_kv_cache_write"] / 1e3 / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic("fp8_kv_cache_write", "kv32b_prefill")},
-            "kernels": {"fp8_kv_scale_recalibrate": {"us": round(us["fp8_kv_scale_recalibrate"], 2),
-                                                     "algorithmic_bytes": b_recal,
-                                                     "GB/s": round(b_recal / us["fp8_kv_scale_recalibrate"] / 1e3, 1)},
-                        "fp8_kv_cache_write": {"us": round(us["fp8_kv_cache_write"], 2),
-                                               "algorithmic_bytes": b_write,
-                                               "GB/s": round(b_write / us["fp8_kv_cache_write"] / 1e3, 1)}}}
-    # The same step in one pass per tensor: each call writes its rows with
-    # the scale the previous step calibrated and replaces that scale, in
-    # place, with the one recalibrated from the same rows; then K and V in
-    # one call (fp8_kv_cache_write_recalibrate_multi).
+    B.fp8_kv_scale_recalibrate(k, out=ks)
+    B.fp8_kv_scale_recalibrate(v, out=vs)
     kws = torch.empty(2 * B.KV_RECAL_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
+    step_bytes = 2 * (3 * T * C + 8) + 8 * T          # rows read, codes written, scales; slots once
 
-    def fused_step(_i, timer=None):
+    def multi_step(_i, timer=None):
+        fn = lambda: B.fp8_kv_cache_write_recalibrate_multi([k, v], slots, [ks, vs], [kc, vc],
+                                                            new_scales=[ks, vs], workspace=kws)
+        timer.run("fp8_kv_cache_write_recalibrate_multi", fn) if timer else fn()
+
+    def per_tensor_step(_i, timer=None):
         calls = [("fp8_kv_cache_write_recalibrate",
                   lambda: B.fp8_kv_cache_write_recalibrate(k, slots, ks, kc, new_scale=ks,
                                                            workspace=kws)),
@@ -754,38 +739,69 @@ def run_kv32b(args, torch, B, W):
         for name, fn in calls:
             timer.run(name, fn) if timer else fn()
 
-    def multi_step(_i, timer=None):
-        fn = lambda: B.fp8_kv_cache_write_recalibrate_multi([k, v], slots, [ks, vs], [kc, vc],
-                                                            new_scales=[ks, vs], workspace=kws)
-        timer.run("fp8_kv_cache_write_recalibrate_multi", fn) if timer else fn()
+    def separate_step(_i, timer=None):
+        calls = [("fp8_kv_scale_recalibrate", lambda: B.fp8_kv_scale_recalibrate(k, out=ks)),
+                 ("fp8_kv_scale_recalibrate", lambda: B.fp8_kv_scale_recalibrate(v, out=vs)),
+                 ("fp8_kv_cache_write", lambda: B.fp8_kv_cache_write(k, slots, ks, kc)),
+                 ("fp8_kv_cache_write", lambda: B.fp8_kv_cache_write(v, slots, vs, vc))]
+        for name, fn in calls:
+            timer.run(name, fn) if timer else fn()
 
-    fdt, fus, _ = timed_steps(torch, fused_step, args)
-    mdt, mus, _ = timed_steps(torch, multi_step, args)
-    b_fused = 3 * T * C + 8 * T + 8
-    line["fused_step"] = {
-        "step": "fp8_kv_cache_write_recalibrate_multi for K and V in one call (write with the "
-                "previous step's scale, recalibrate the next from the same rows: one read of the "
-                "rows)",
-        "ms_per_step": round(mdt * 1e3, 3), "step_algorithmic_bytes": 2 * b_fused - 8 * T,
-        "GB/s": round((2 * b_fused - 8 * T) / mdt / 1e9, 1),
-        "speedup_vs_separate_calls": round(dt / mdt, 3),
-        "kernels": {"fp8_kv_cache_write_recalibrate_multi": {
-            "us": round(mus["fp8_kv_cache_write_recalibrate_multi"], 2),
-            "algorithmic_bytes": 2 * b_fused - 8 * T,
-            "traffic": measured_traffic("fp8_kv_cache_write_recalibrate_multi", "kv32b_prefill")}},
-        "per_tensor_calls": {
-            "ms_per_step": round(fdt * 1e3, 3),
-            "us_per_call": round(fus["fp8_kv_cache_write_recalibrate"], 2),
-            "traffic": measured_traffic("fp8_kv_cache_write_recalibrate", "kv32b_prefill")}}
+    dt, us, _ = timed_steps(torch, multi_step, args)
+    pdt, pus, _ = timed_steps(torch, per_tensor_step, args)
+    sdt, sus, _ = timed_steps(torch, separate_step, args)
+    m_us = us["fp8_kv_cache_write_recalibrate_multi"]
+    b_recal = 2 * T * C + 4
+    b_write = 3 * T * C + 8 * T + 4
+    b_one = 3 * T * C + 8 * T + 8
+    line = {"metric": METRIC, "value": round(step_bytes / dt / 1e9, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "vs_baseline": None,
+            "dtype": "fp8e4m3", "data": "synthetic",
+            "config": {"workload": "kv32b_prefill", "tokens": T, "row": C, "slots": S,
+                       "step": "fp8_kv_cache_write_recalibrate_multi for K and V (write with "
+                               "the previous step's scales, recalibrate the next from the same "
+                               "rows)", "step_algorithmic_bytes": step_bytes},
+            "roofline": {"bound": "hbm", "kernel": "fp8_kv_cache_write_recalibrate_multi",
+                         "achieved": round(step_bytes / m_us / 1e3, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(step_bytes / m_us / 1e3 / HBM_PEAK_GBS, 4),
+                         "us_per_launch": round(m_us, 2),
+                         "traffic": measured_traffic("fp8_kv_cache_write_recalibrate_multi",
+                                                     "kv32b_prefill")},
+            "forms": {
+                "per_tensor_calls": {
+                    "ms_per_step": round(pdt * 1e3, 4),
+                    "GB/s": round(step_bytes / pdt / 1e9, 1),
+                    "fp8_kv_cache_write_recalibrate": {
+                        "us": round(pus["fp8_kv_cache_write_recalibrate"], 2),
+                        "algorithmic_bytes": b_one,
+                        "traffic": measured_traffic("fp8_kv_cache_write_recalibrate",
+                                                    "kv32b_prefill")}},
+                "separate_calls": {
+                    "ms_per_step": round(sdt * 1e3, 4),
+                    "GB/s": round(step_bytes / sdt / 1e9, 1),
+                    "fp8_kv_scale_recalibrate": {
+                        "us": round(sus["fp8_kv_scale_recalibrate"], 2), "algorithmic_bytes": b_recal,
+                        "GB/s": round(b_recal / sus["fp8_kv_scale_recalibrate"] / 1e3, 1)},
+                    "fp8_kv_cache_write": {
+                        "us": round(sus["fp8_kv_cache_write"], 2), "algorithmic_bytes": b_write,
+                        "GB/s": round(b_write / sus["fp8_kv_cache_write"] / 1e3, 1),
+                        "traffic": measured_traffic("fp8_kv_cache_write", "kv32b_prefill")}},
+                "speedup_vs_separate_calls": round(sdt / dt, 3)}}
     if not args.no_cpu_baseline:
         from oracle import kv as okv
+        cache0 = np.zeros((S, C), np.uint8)
+        s_old = {id(kb): okv.kv_scale(kb), id(vb): okv.kv_scale(vb)}
         t0 = time.perf_counter()
         for xb in (kb, vb):
-            okv.kv_cache_write(np.zeros((S, C), np.uint8), xb, slots_np, okv.kv_scale(xb))
+            okv.kv_cache_write(cache0, xb, slots_np, s_old[id(xb)])
+            okv.kv_scale(xb)
         ct = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(step_bytes / ct / 1e9, 3), "unit": "GB/s",
                                 "cores": cpu_threads(), "os_cpu_count": os.cpu_count(), "kind": "oracle",
-                                "sample": "one whole step (K and V: recalibration and cache write)"}
+                                "sample": "one whole step (K and V: cache write with the earlier "
+                                          "scale and the new scale)"}
     return line
 
 
