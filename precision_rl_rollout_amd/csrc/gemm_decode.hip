@@ -1,4 +1,5 @@
-// W8A8 GEMM for decode-sized batches (M <= 64): activation-resident,
+// W8A8 GEMM for decode-sized batches (M <= 64 per workgroup; 65-128 rows
+// as two row ranges on pairs of workgroups): activation-resident,
 // weight-streaming, persistent.
 //
 // Long-tail decode runs the linear layers at small effective batch, where
