@@ -32,8 +32,11 @@
 //    strips, one barrier per strip); MT waves add them, apply the epilogue
 //    and store bf16 while the next strip's first task is in flight.  The
 //    barrier orders LDS only, so it does not drain the loads in flight.
-//  * Start-up: the ring's first loads, the resident activations and their
-//    scales are all issued before the first wait (one memory latency).
+//  * Start-up: the ring's first loads, then the activation scales, then
+//    the resident activations.  INT8 issues them all before its first
+//    wait; FP8 stages its scales in LDS first, which waits for them (and
+//    the ring loads ahead of them) before the activations go out (issuing
+//    the activations ahead of the staging measured no faster).
 //  * Output: a strip writes 32 bytes of each of its M rows.  Strips are
 //    mapped to workgroups so that the 4 strips sharing 128-byte output
 //    lines run on one XCD, whose L2 merges their writes.  Measured on a
@@ -204,8 +207,8 @@ __device__ __forceinline__ void decode_segment(
   // h gives lane s chunk 4 h + (s & 3) of token s / 4 -- and one
   // ds_bpermute per register then moves lane 4 n + g to lane 16 g + n: the
   // fragment layout (measured 5-8% faster over the whole GEMM at 32-64
-  // rows).  They are issued after the activation scales have been staged in
-  // LDS (so that staging waits for the scales alone), block by block.
+  // rows).  They are issued, block by block, once the FP8 activation scales
+  // have been staged in LDS.
   const __amdgpu_buffer_rsrc_t ares = buffer_rsrc(A, (int64_t)M * ld);
   constexpr bool kSectorLoads = MT >= 2;
   v8i afr[MT][P];
