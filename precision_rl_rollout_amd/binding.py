@@ -123,6 +123,12 @@ def call(name: str, *args) -> int:
 
 
 def _stream(t: torch.Tensor) -> int:
+    # The library runs on the current HIP device (its checks, launches and
+    # per-device scratch all follow it): the tensors must live there.
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensor on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}; call under "
+                         f"torch.cuda.device({t.device.index})")
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
