@@ -346,6 +346,27 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
   // wave is done with the stages before they hold the output tile.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   const int r16 = lane & 15, g = lane >> 4;
+  // INT8 epilogue scales: the lane's 4 row scales and 32 channel scales,
+  // loaded once, branch-free (clamped indices, zero past M or N), so the
+  // epilogue waits for one round trip.  (Loaded per element under bounds
+  // branches, they cost one wait per fragment: ~5 us per tile.)
+  float sml[4], swl[NJ][4];
+  if constexpr (kInt8 && !kPartial) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = (int64_t)m0 + wm * 64 + i * 16 + r16;
+      const float x = sa[min(m, (int64_t)M - 1)];
+      sml[i] = m < M ? x : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t n = (int64_t)n0 + wn * kWaveN + j * 16 + 4 * g + r;
+        const float x = sw[min(n, (int64_t)N - 1)];
+        swl[j][r] = n < N ? x : 0.f;
+      }
+  }
   if constexpr (kPartial) {
     // The partial sums, 16 bytes (4 columns of one row) a lane and
     // fragment, to slab `slice` [M][ncols] of the workspace.
@@ -386,8 +407,6 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rr = (wm & 1) * 64 + i * 16 + r16;   // row within the half
-    const int64_t m = m0 + wm * 64 + i * 16 + r16;
-    const float sm = kInt8 ? ((m < M) ? sa[m] : 0.f) : 1.f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int nl = wn * kWaveN + j * 16 + 4 * g;   // column within the tile
@@ -395,8 +414,7 @@ __global__ __launch_bounds__(512) void gemm_prefill_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (kInt8) {
-          const int64_t n = n0 + nl + r;
-          v[r] = (float)acc.v[j][i][r] * (sm * ((n < N) ? sw[n] : 0.f));
+          v[r] = (float)acc.v[j][i][r] * (sml[i] * swl[j][r]);
         } else {
           v[r] = acc.v[j][i][r];
         }
