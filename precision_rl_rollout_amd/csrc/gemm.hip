@@ -203,6 +203,26 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
               accf[s][mt][r] += red[wave + j][s][mt][r][lane];
           }
   }
+  // INT8: the row and channel scales this lane applies, loaded together
+  // and branch-free (clamped indices, zero past M or N), so the stores
+  // below wait for one round trip rather than one per fragment.
+  float smv[MT], snv[S][4];
+  if constexpr (kInt8) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int64_t m = mt * 16 + r16;
+      const float x = sa[min(m, (int64_t)M - 1)];
+      smv[mt] = m < M ? x : 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t n = (int64_t)n0 + s * 16 + 4 * g + r;
+        const float x = sw[min(n, (int64_t)N - 1)];
+        snv[s][r] = n < N ? x : 0.f;
+      }
+  }
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -213,9 +233,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (kInt8) {
-          const float sm = (m < M) ? sa[m] : 0.f;
-          const float sn = (n + r < N) ? sw[n + r] : 0.f;
-          v[r] = (float)acci[s][mt][r] * (sm * sn);
+          v[r] = (float)acci[s][mt][r] * (smv[mt] * snv[s][r]);
         } else {
           v[r] = accf[s][mt][r];
         }
